@@ -1,0 +1,147 @@
+"""MXFP4 page geometry and exact dequantisation (CPU oracle, test infrastructure).
+
+Source: page *vllm.models.minimax_m3.amd.ops.mxfp4_pages*, module docstring
+and the function ``mxfp4_page_views``.  One 128-token page of one head holds
+the 128 rows of 128-wide e2m1 data, two elements per byte with the even
+element in the low nibble (64 B per row), and then one e8m0 scale byte per
+32 elements (4 B per row).  The page is 128 x 64 + 128 x 4 = 8704 B and has
+no global scale.  K, V and the single index-key head all use this page.
+
+The numeric meaning of the two element formats is the OCP Microscaling one,
+which the page names but does not spell out:
+
+* e2m1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa, so the
+  magnitudes of codes 0..7 are 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Code 8 is -0.0.
+* e8m0: the byte e means 2**(e - 127); 0xFF is NaN.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s
+``cpu_baseline`` leg may use this module.
+"""
+
+import numpy as np
+
+PAGE_TOKENS = 128  # rows (tokens) per page
+ROW_ELEMS = 128  # elements per row (head_dim)
+SCALE_BLOCK = 32  # elements sharing one e8m0 scale
+DATA_BYTES = ROW_ELEMS // 2  # 64: two e2m1 elements per byte
+SCALE_BYTES = ROW_ELEMS // SCALE_BLOCK  # 4
+DATA_REGION = PAGE_TOKENS * DATA_BYTES  # 8192: the scale region starts here
+PAGE_BYTES = DATA_REGION + PAGE_TOKENS * SCALE_BYTES  # 8704
+
+# e2m1 magnitudes of codes 0..7 (OCP MX FP4); codes 8..15 are their negatives.
+E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def page_views(pages):
+    """(data, scale) zero-copy views of uint8 pages ``[..., 8704]``.
+
+    Follows ``mxfp4_page_views`` on the mxfp4_pages page: the data view is
+    ``[..., 128, 64]`` at byte offset 0 with row stride 64, the scale view is
+    ``[..., 128, 4]`` at byte offset 128*64 with row stride 4, and both keep
+    the leading dims and their strides.  A wrong dtype, a last dim other than
+    8704 or a non-unit byte stride raises ValueError, as there.
+    """
+    pages = np.asarray(pages)
+    if pages.dtype != np.uint8 or pages.ndim < 1 or pages.shape[-1] != PAGE_BYTES:
+        raise ValueError(
+            f"MXFP4 pages must be uint8 [..., {PAGE_BYTES}], got {pages.dtype} {pages.shape}"
+        )
+    if pages.strides[-1] != 1:
+        raise ValueError("MXFP4 pages need a contiguous byte axis")
+    lead = pages.shape[:-1]
+    lead_strides = pages.strides[:-1]
+    data = np.lib.stride_tricks.as_strided(
+        pages, shape=(*lead, PAGE_TOKENS, DATA_BYTES), strides=(*lead_strides, DATA_BYTES, 1)
+    )
+    # The scale view starts DATA_REGION bytes into each page.
+    tail = pages[..., DATA_REGION:]
+    scale = np.lib.stride_tricks.as_strided(
+        tail, shape=(*lead, PAGE_TOKENS, SCALE_BYTES), strides=(*lead_strides, SCALE_BYTES, 1)
+    )
+    return data, scale
+
+
+def pack(codes, scales):
+    """Pages ``[..., 8704]`` from one e2m1 code per byte and the e8m0 scales.
+
+    ``codes``: uint8 ``[..., 128, 128]`` (only the low 4 bits are used);
+    ``scales``: uint8 ``[..., 128, 4]``.  Element 2c of a row goes to the low
+    nibble of data byte c and element 2c+1 to its high nibble (mxfp4_pages
+    page, module docstring: "the low nibble the even one").
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    scales = np.asarray(scales, dtype=np.uint8)
+    lead = codes.shape[:-2]
+    assert codes.shape[-2:] == (PAGE_TOKENS, ROW_ELEMS)
+    assert scales.shape == (*lead, PAGE_TOKENS, SCALE_BYTES)
+    even = codes[..., 0::2] & 0x0F
+    odd = codes[..., 1::2] & 0x0F
+    data = (even | (odd << 4)).astype(np.uint8)  # [..., 128, 64]
+    pages = np.empty((*lead, PAGE_BYTES), dtype=np.uint8)
+    pages[..., :DATA_REGION] = data.reshape(*lead, DATA_REGION)
+    pages[..., DATA_REGION:] = scales.reshape(*lead, PAGE_TOKENS * SCALE_BYTES)
+    return pages
+
+
+def unpack(pages):
+    """Inverse of ``pack``: (codes ``[..., 128, 128]``, scales ``[..., 128, 4]``)."""
+    data, scale = page_views(pages)
+    lead = data.shape[:-2]
+    codes = np.empty((*lead, PAGE_TOKENS, ROW_ELEMS), dtype=np.uint8)
+    codes[..., 0::2] = data & 0x0F
+    codes[..., 1::2] = data >> 4
+    return codes, np.array(scale, dtype=np.uint8)
+
+
+def e2m1_value(code):
+    """float64 value of e2m1 code(s) 0..15; code 8 gives -0.0."""
+    code = np.asarray(code, dtype=np.int64)
+    mag = np.asarray(E2M1_MAGNITUDES, dtype=np.float64)[code & 7]
+    return np.where((code & 8) != 0, -mag, mag)
+
+
+def e8m0_value(e):
+    """float64 value 2**(e - 127) of e8m0 byte(s); 255 gives NaN."""
+    e = np.asarray(e, dtype=np.int64)
+    return np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+
+
+def dequant(pages):
+    """Exact float64 values ``[..., 128, 128]`` of MXFP4 pages ``[..., 8704]``.
+
+    Element i of row r is e2m1(code[r, i]) * 2**(e[r, i // 32] - 127): the
+    32-element blocks of a row are contiguous and each has its own scale
+    byte (mxfp4_pages page, module docstring: one e8m0 scale per 32
+    elements).  Every product is exact in float64.
+    """
+    codes, scales = unpack(pages)
+    block_scale = e8m0_value(scales)  # [..., 128, 4]
+    per_elem = np.repeat(block_scale, SCALE_BLOCK, axis=-1)  # [..., 128, 128]
+    return e2m1_value(codes) * per_elem
+
+
+def round_to_f32(x):
+    """float64 -> float32 with round-to-nearest-even (numpy's cast)."""
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float64).astype(np.float32)
+
+
+def round_to_bf16_bits(x):
+    """float64 -> bfloat16 bit patterns (uint16), round-to-nearest-even.
+
+    Goes float64 -> float32 (RNE) -> bfloat16 (RNE on the top 16 bits).  For
+    values with at most 8 significant bits, such as every finite MXFP4 value,
+    both roundings are exact, so the result is the value itself.
+    """
+    f = round_to_f32(x)
+    u = f.view(np.uint32).astype(np.uint64)
+    nan = np.isnan(f)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = np.where(nan, (u >> 16) | 0x40, rounded)
+    return out.astype(np.uint16)
+
+
+def bf16_bits_to_f64(bits):
+    """bfloat16 bit patterns (uint16) -> float64 (exact)."""
+    bits = np.asarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
