@@ -1,0 +1,221 @@
+"""Decode-step benchmark of the sparse paged MXFP4 decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+A step is one pass of the whole path over one batch: mono_index_score_topk
+(index scores + top-k) then mono_pa_decode_mxfp4 (attention over the selected
+tokens); dense workloads run the attention call alone.  The default workload
+is batch 64, context 32768 (256 pages per request), top-2048.
+
+Inputs are resident in HBM before timing starts.  The K, V and index-key
+pools are replicated ``--copies`` times and the steps rotate through the
+copies, so each step reads pages that are not in the 256 MB Infinity Cache.
+
+Printed (one JSON line): achieved HBM GB/s over the KV+index bytes the method
+must read (the index pages of every valid token once per request, the K and V
+rows of every selected token once per request), the step time, the roofline
+entry of the index call (its share of the step is the largest), and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
+ROW_BYTES = 68  # 64 B e2m1 data + 4 B e8m0 scales per token row
+METRIC = "decode-step µs + achieved HBM GB/s (% of peak), B=64 ctx=32k top-2048"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
+    p.add_argument("--cpu-sample", type=int, default=6, help="query tokens timed on the CPU oracle (0 = skip)")
+    return p.parse_args()
+
+
+def algorithmic_bytes(w, sel):
+    """(index bytes, K+V bytes) the step must read: 68 B per index row of every
+    valid token once per request, 2 x 68 B per selected (or, dense, valid)
+    token once per request (union over the request's query tokens)."""
+    idx_bytes = int(np.sum(w.seq_lens.astype(np.int64))) * ROW_BYTES if w.sparse else 0
+    kv_tokens = 0
+    for b in range(w.B):
+        if sel is None:
+            kv_tokens += int(w.seq_lens[b])
+        else:
+            rows = sel[b * w.T : (b + 1) * w.T]
+            kv_tokens += int(np.unique(rows[rows >= 0]).size)
+    return idx_bytes, 2 * ROW_BYTES * kv_tokens
+
+
+def cpu_baseline(w, n_sample):
+    """The oracle (numpy float64) on the first n_sample query tokens, scaled to GB/s."""
+    from oracle import decode
+
+    threads = len(os.sched_getaffinity(0))
+    pos = decode.query_positions(w.seq_lens, w.T)
+    n = min(n_sample, w.N)
+    t0 = time.perf_counter()
+    done_bytes = 0
+    for i in range(n):
+        b = i // w.T
+        bt = w.block_table[b]
+        sel = None
+        if w.sparse:
+            s = decode.index_scores(w.index_q[i], w.index_pool, bt, pos[i])
+            sel = decode.topk(s, w.k)
+            done_bytes += (pos[i] + 1) * ROW_BYTES
+        decode.decode_one(w.q[i], w.k_pool, w.v_pool, bt, pos[i], w.scale, sel)
+        done_bytes += 2 * ROW_BYTES * (len(sel) if sel is not None else pos[i] + 1)
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(done_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{n} of {w.N} query tokens of {w.name} (scores + top-k + attention per query token), "
+        f"{dt:.1f} s; numpy float64, BLAS threads <= {threads}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_paged_decode_amd as spd
+    from workloads import workload
+
+    spd.load_library()
+    dev = torch.device("cuda:0")
+    w = workload(args.workload)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q = bf16(w.q)
+    bt = torch.from_numpy(w.block_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    iq = bf16(w.index_q) if w.sparse else None
+    copies = max(1, args.copies)
+    kp = [torch.from_numpy(w.k_pool).to(dev)]
+    vp = [torch.from_numpy(w.v_pool).to(dev)]
+    ip = [torch.from_numpy(w.index_pool).to(dev)] if w.sparse else [None]
+    for _ in range(copies - 1):
+        kp.append(kp[0].clone())
+        vp.append(vp[0].clone())
+        ip.append(ip[0].clone() if w.sparse else None)
+    sel = torch.empty((w.N, w.k), dtype=torch.int32, device=dev) if w.sparse else None
+    out = torch.empty_like(q)
+    ws_topk = spd.Workspace(dev)
+    ws_pa = spd.Workspace(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(c, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        if w.sparse:
+            spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
+        if ev is not None:
+            ev[1].record(stream)
+        spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, sel, w.scale, T=w.T, out=out, workspace=ws_pa)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for s in range(args.warmup):
+        step(s % copies)
+    torch.cuda.synchronize(dev)
+    sel_np = sel.cpu().numpy() if w.sparse else None
+    idx_bytes, kv_bytes = algorithmic_bytes(w, sel_np)
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for s in range(K):
+        step(s % copies, evs[s])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
+    topk_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pa_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    total_ms = evs[0][0].elapsed_time(evs[-1][2])
+    ms_per_step = total_ms / K
+    bytes_step = idx_bytes + kv_bytes
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    if w.sparse:
+        dom_name, dom_ms, dom_bytes = "mono_index_score_topk", float(np.mean(topk_ms)), idx_bytes
+    else:
+        dom_name, dom_ms, dom_bytes = "mono_pa_decode_mxfp4", float(np.mean(pa_ms)), kv_bytes
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(w, args.cpu_sample)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": w.B,
+            "T": w.T,
+            "context": int(w.seq_lens.max()) if w.T == 1 else [int(w.seq_lens.min()), int(w.seq_lens.max())],
+            "k": w.k,
+            "pool_copies_rotated": copies,
+        },
+        "step_us": round(ms_per_step * 1e3, 2),
+        "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": {"index": idx_bytes, "kv": kv_bytes},
+        "calls_us_mean": {
+            "mono_index_score_topk": round(float(np.mean(topk_ms)) * 1e3, 2) if w.sparse else 0.0,
+            "mono_pa_decode_mxfp4": round(float(np.mean(pa_ms)) * 1e3, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom_name,
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": cpu,
+        "wall_s": round(wall, 3),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * mono_decode.h -- C ABI of the MI355X (gfx950) sparse paged MXFP4 decode library
+ * (libmono_decode.so).
+ *
+ * What the library computes
+ * -------------------------
+ * One decode step of sparse attention over MXFP4-quantised paged caches:
+ *   1. mono_index_score_topk: for every query token, the fp32 dot product of
+ *      its bf16 index-q row with every valid dequantised index-K row, then
+ *      the k highest-scoring tokens;
+ *   2. mono_pa_decode_mxfp4: 16-query-head : 1-KV-head attention (head_dim
+ *      128) over the selected tokens, or over every valid token when no
+ *      selection is given.
+ *
+ * Sources.  Page "vllm.models.minimax_m3.amd.ops.mxfp4_pages" (module
+ * docstring and mxfp4_page_views) fixes the page: 128 tokens x 64 B of e2m1
+ * data (two elements a byte, the even one in the low nibble), then
+ * 128 x 4 B of e8m0 scales (one per 32 elements), 8704 B in all, no global
+ * scale; K, V and the single index-key head share it, and pa_decode reads
+ * [pages, heads, 8704] pools while the index scorers read [pages, 8704].
+ * Page "vllm.models.minimax_m3.amd.mono.dispatch" (_step_refusal,
+ * _slots_shared) fixes the step tables: one int32 block table, rows
+ * bt_stride apart, shared by K, V and the index key; int32 seq_lens; a step
+ * decodes T tokens of each of B requests, flattened request-major.  Page
+ * "vllm.models.minimax_m3.amd.mono.weights" (_build_cp_qkv) gives the
+ * per-rank head shape: 16 query heads of 128 per KV head, one index-q head
+ * and one index-key head, each 128 wide.
+ *
+ * Readings where the pages are silent:
+ *   - e2m1 / e8m0 are the OCP Microscaling formats: codes 0..7 are
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6 and 8..15 their negatives; byte e scales
+ *     by 2^(e-127), 0xFF is NaN.  Element i of a row uses scale byte i/32.
+ *   - Token j of request b is row j%128 of page block_table[b*bt_stride + j/128].
+ *   - seq_lens counts every token, the T being decoded included, so query
+ *     token t of request b (flat index i = b*T + t) sits at position
+ *     pos_i = seq_lens[b] - T + t and sees tokens 0..pos_i.
+ *   - The index score is the plain fp32 dot product (no ReLU, weight or
+ *     bias); top-k keeps the k highest scores among the valid tokens, ties
+ *     to the lower token index, NaN below every number.
+ *   - Attention: logits scale * q.k, softmax over the candidates, no sink,
+ *     soft-cap or window; an empty candidate set gives a zero output.
+ *
+ * Conventions of every call
+ * -------------------------
+ *   - Pointers named *_dev are device pointers (HIP global memory); all
+ *     other pointers are host pointers.  bf16 values are passed as uint16_t
+ *     bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns: no host synchronisation and no device
+ *     allocation, so a sequence of calls can be captured in a HIP graph.
+ *     mono_check_device_errors is the one exception (it synchronises).
+ *   - The caller owns every buffer, the workspace included.  The library
+ *     keeps no state between calls except a thread-local error string.
+ *   - Workspaces: ask the *_workspace function for the size; the buffer
+ *     must be zero-filled before its first use.  Every call that returns
+ *     MONO_OK leaves the workspace's counters and histograms zero again (the
+ *     rest holds scratch data that the next call overwrites), so one buffer
+ *     serves any sequence of calls of any shape that fits it.  Calls that
+ *     share one workspace must not overlap in time.
+ *   - Return value: MONO_OK (0) or a negative MONO_E* code; on error nothing
+ *     was enqueued and mono_last_error() says why.  Nothing aborts.
+ *   - Device-side checks: a block-table entry outside [0, num_pages) for a
+ *     page that a valid token needs, or seq_lens[b] < T or
+ *     seq_lens[b] > bt_stride*128, is not dereferenced; the kernels set a
+ *     bit in the workspace's error word instead and the affected outputs
+ *     are unspecified.
+ */
+#ifndef MONO_DECODE_H
+#define MONO_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MONO_ABI_VERSION 1
+
+#define MONO_OK 0
+#define MONO_EINVAL (-1)  /* bad pointer, size, stride, k, T or B */
+#define MONO_ENOTSUP (-2) /* a shape this build does not handle */
+#define MONO_ENOSPC (-3)  /* workspace smaller than the *_workspace size */
+#define MONO_EHIP (-4)    /* the HIP runtime refused a launch */
+
+/* Device error bits (mono_check_device_errors). */
+#define MONO_DEVERR_PAGE_ID 1u     /* block-table entry outside [0, num_pages) */
+#define MONO_DEVERR_SEQ_LEN 2u     /* seq_lens[b] < T or > bt_stride*128 */
+#define MONO_DEVERR_SELECTION 4u   /* internal selection counts disagreed (a bug; output refused) */
+
+/* Geometry of one MXFP4 page (mxfp4_pages page, module docstring). */
+#define MONO_PAGE_TOKENS 128
+#define MONO_HEAD_DIM 128
+#define MONO_PAGE_DATA_BYTES 8192  /* 128 rows x 64 B of packed e2m1 */
+#define MONO_PAGE_BYTES 8704       /* + 128 rows x 4 B of e8m0 scales */
+#define MONO_Q_HEADS_PER_KV 16
+
+/* ABI version (MONO_ABI_VERSION of the build). */
+int mono_abi_version(void);
+
+/* Reason for the last non-zero return on the calling thread ("" if none).
+ * The string stays valid until the next call on this thread. */
+const char* mono_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Page packing (mxfp4_pages page, module docstring).
+ *
+ * mxfp4_pages_pack: codes_dev uint8 [n_pages, 128, 128], one e2m1 code per
+ * byte (the high 4 bits are ignored); scales_dev uint8 [n_pages, 128, 4]
+ * e8m0; pages_dev uint8 [n_pages, 8704] receives
+ *   pages[p][64r + c]        = codes[p][r][2c] | codes[p][r][2c+1] << 4
+ *   pages[p][8192 + 4r + g]  = scales[p][r][g].
+ * mxfp4_pages_unpack is the exact inverse (codes come out in 0..15).
+ * All buffers are contiguous.  n_pages == 0 is a no-op; n_pages < 0 or a
+ * NULL pointer with n_pages > 0 gives MONO_EINVAL.
+ * ------------------------------------------------------------------------- */
+int mxfp4_pages_pack(const uint8_t* codes_dev, const uint8_t* scales_dev, uint8_t* pages_dev,
+                     int64_t n_pages, void* stream);
+int mxfp4_pages_unpack(const uint8_t* pages_dev, uint8_t* codes_dev, uint8_t* scales_dev,
+                       int64_t n_pages, void* stream);
+
+/* Dequantisation of whole pages: out_dev [n_pages, 128, 128].
+ * mxfp4_pages_dequant writes fp32: the exact value e2m1(code) * 2^(e-127)
+ * rounded to fp32 (round-to-nearest-even; subnormals kept, overflow to inf,
+ * e = 0xFF gives NaN, code 8 gives -0.0).
+ * mxfp4_pages_dequant_bf16 writes bf16 bit patterns through the very
+ * conversion the attention and scoring kernels use, so that conversion can
+ * be checked bit for bit against the exact value rounded to bf16. */
+int mxfp4_pages_dequant(const uint8_t* pages_dev, float* out_dev, int64_t n_pages, void* stream);
+int mxfp4_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages,
+                             void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Index scoring and top-k (the index scorers the mxfp4_pages page names;
+ * the rule is the reading above).
+ *
+ * index_q_dev        bf16 [B*T, 128], query token i = b*T + t.
+ * index_pages_dev    uint8 [num_pages, 8704], the single index-key head.
+ * block_table_dev    int32 [B, bt_stride], row-contiguous; entries past a
+ *                    request's last page are never read.
+ * seq_lens_dev       int32 [B]; T <= seq_lens[b] <= bt_stride*128.
+ * k                  >= 1.
+ * selected_idx_dev   int32 [B*T, k] out: the min(k, pos_i+1) selected token
+ *                    positions of query i in any order, then -1 padding.
+ * selected_scores_dev  NULL or fp32 [B*T, k] out: the fp32 score of each
+ *                    selected token (NaN for padding).
+ * ws_dev, ws_bytes   workspace of at least mono_index_score_topk_workspace().
+ * ------------------------------------------------------------------------- */
+size_t mono_index_score_topk_workspace(int B, int T, int bt_stride, int k);
+int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                          int64_t num_pages, const int32_t* block_table_dev, int bt_stride,
+                          const int32_t* seq_lens_dev, int B, int T, int k,
+                          int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
+                          size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Paged GQA decode attention over MXFP4 K/V pages (the pa_decode the
+ * mxfp4_pages page names: [pages, heads, 128, 64] / [pages, heads, 128, 4]
+ * views of [pages, heads, 8704] pools).
+ *
+ * q_dev            bf16 [B*T, kv_heads*16, 128]; query heads 16h..16h+15 read
+ *                  KV head h.
+ * k_pages_dev, v_pages_dev  uint8 [num_pages, kv_heads, 8704].
+ * block_table_dev, bt_stride, seq_lens_dev, B, T: as for the index call.
+ * selected_idx_dev NULL: dense, every token 0..pos_i.  Otherwise int32
+ *                  [B*T, k]: attention over the listed tokens; entries < 0 or
+ *                  > pos_i are skipped; valid entries must be distinct.
+ * k                list length (ignored when selected_idx_dev is NULL).
+ * scale            logit scale (e.g. 1/sqrt(128)).
+ * out_dev          bf16 [B*T, kv_heads*16, 128] out (round-to-nearest-even).
+ * ws_dev, ws_bytes workspace of at least mono_pa_decode_workspace() for the
+ *                  same (B, T, kv_heads, bt_stride, k, sparse) arguments.
+ * ------------------------------------------------------------------------- */
+size_t mono_pa_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k, int sparse);
+int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                         const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                         const int32_t* block_table_dev, int bt_stride,
+                         const int32_t* seq_lens_dev, int B, int T,
+                         const int32_t* selected_idx_dev, int k, float scale, uint16_t* out_dev,
+                         void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Debug/test only.  Waits for `stream`, then returns the device error bits
+ * (MONO_DEVERR_*) accumulated in the workspace and clears them, or a
+ * negative MONO_E* code.  ws_dev is a workspace of either call above. */
+int mono_check_device_errors(void* ws_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONO_DECODE_H */

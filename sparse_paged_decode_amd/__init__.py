@@ -1,0 +1,37 @@
+"""MI355X (gfx950) sparse paged MXFP4 decode attention.
+
+The compute lives in ``libmono_decode.so`` (hand-written HIP kernels behind
+a C ABI, declared in ``include/mono_decode.h``); this package is its thin
+Python binding.  PyTorch supplies device memory and streams only.
+
+Step of the method (page *vllm.models.minimax_m3.amd.ops.mxfp4_pages*:
+MXFP4 K, V and index-key pages; page *vllm.models.minimax_m3.amd.mono.dispatch*:
+pure-decode steps over one shared block table):
+
+    sel = mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, T=T)
+    out = mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, sel, scale, T=T)
+"""
+
+from ._binding import (  # noqa: F401
+    DEVERR_PAGE_ID,
+    DEVERR_SEQ_LEN,
+    EXPORTED_SYMBOLS,
+    HEAD_DIM,
+    PAGE_BYTES,
+    PAGE_TOKENS,
+    Q_HEADS_PER_KV,
+    MonoError,
+    Workspace,
+    check_device_errors,
+    index_score_topk_workspace_bytes,
+    load_library,
+    mono_index_score_topk,
+    mono_pa_decode_mxfp4,
+    mxfp4_page_views,
+    mxfp4_pages_dequant,
+    mxfp4_pages_dequant_bf16,
+    mxfp4_pages_pack,
+    mxfp4_pages_unpack,
+    pa_decode_workspace_bytes,
+)
+from .build import LIB_PATH  # noqa: F401

@@ -1,0 +1,361 @@
+"""ctypes binding of libmono_decode.so (argument marshalling only).
+
+Every computation happens in the library's HIP kernels; this module checks
+tensor arguments, takes device pointers and the current HIP stream from
+PyTorch, and raises on a non-zero return code.  If the library is missing or
+cannot be loaded, every call raises: there is no fallback path.
+
+Argument checks follow the pages: ``mxfp4_page_views`` on the page
+*vllm.models.minimax_m3.amd.ops.mxfp4_pages* (uint8, last dim 8704, unit
+byte stride) and ``_step_refusal`` on the page
+*vllm.models.minimax_m3.amd.mono.dispatch* (int32 tables, a row-contiguous
+block table, tables at least as long as the batch, a token count divisible
+by the tokens per request).
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .build import LIB_PATH
+
+PAGE_TOKENS = 128
+HEAD_DIM = 128
+DATA_BYTES = 64
+SCALE_BYTES = 4
+PAGE_BYTES = PAGE_TOKENS * (DATA_BYTES + SCALE_BYTES)  # 8704
+Q_HEADS_PER_KV = 16
+
+MONO_OK = 0
+MONO_EINVAL = -1
+MONO_ENOTSUP = -2
+MONO_ENOSPC = -3
+MONO_EHIP = -4
+
+DEVERR_PAGE_ID = 1
+DEVERR_SEQ_LEN = 2
+
+EXPORTED_SYMBOLS = (
+    "mono_abi_version",
+    "mono_last_error",
+    "mxfp4_pages_pack",
+    "mxfp4_pages_unpack",
+    "mxfp4_pages_dequant",
+    "mxfp4_pages_dequant_bf16",
+    "mono_index_score_topk_workspace",
+    "mono_index_score_topk",
+    "mono_pa_decode_workspace",
+    "mono_pa_decode_mxfp4",
+    "mono_check_device_errors",
+)
+
+
+class MonoError(RuntimeError):
+    """A non-zero return code of libmono_decode.so."""
+
+    def __init__(self, code, message):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libmono_decode.so and declare its signatures (cached)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run sparse_paged_decode_amd.build.build() "
+            "(or __graft_entry__.build()) first"
+        )
+    lib = ctypes.CDLL(path)
+    P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "mono_abi_version": (I, []),
+        "mono_last_error": (ctypes.c_char_p, []),
+        "mxfp4_pages_pack": (I, [P, P, P, I64, P]),
+        "mxfp4_pages_unpack": (I, [P, P, P, I64, P]),
+        "mxfp4_pages_dequant": (I, [P, P, I64, P]),
+        "mxfp4_pages_dequant_bf16": (I, [P, P, I64, P]),
+        "mono_index_score_topk_workspace": (SZ, [I, I, I, I]),
+        "mono_index_score_topk": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
+        "mono_pa_decode_workspace": (SZ, [I, I, I, I, I, I]),
+        "mono_pa_decode_mxfp4": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, P, P, SZ, P]),
+        "mono_check_device_errors": (I, [P, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(rc):
+    if rc != MONO_OK:
+        msg = _lib.mono_last_error().decode(errors="replace")
+        raise MonoError(rc, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        _need(t.is_cuda and t.device == dev, "all tensors must be on the same GPU")
+    return dev
+
+
+# --- page views (zero-copy) -------------------------------------------------------
+
+
+def mxfp4_page_views(pages):
+    """(data, scale) views of uint8 pages ``[..., 8704]``.
+
+    As ``mxfp4_page_views`` on the mxfp4_pages page: the data view is
+    ``[..., 128, 64]`` from byte 0 of each page, the scale view ``[..., 128, 4]``
+    from byte 8192, both keeping the leading dims and strides.  Raises
+    ValueError for a dtype other than uint8, a last dim other than 8704 or a
+    non-unit stride on the byte axis.
+    """
+    if pages.dtype != torch.uint8 or pages.dim() < 1 or pages.shape[-1] != PAGE_BYTES:
+        raise ValueError(f"MXFP4 pages are uint8 [..., {PAGE_BYTES}]; got {pages.dtype} {tuple(pages.shape)}")
+    if pages.stride(-1) != 1:
+        raise ValueError("MXFP4 pages need a contiguous byte axis")
+    lead = list(pages.shape[:-1])
+    lead_strides = list(pages.stride()[:-1])
+    base = pages.storage_offset()
+    data = pages.as_strided(lead + [PAGE_TOKENS, DATA_BYTES], lead_strides + [DATA_BYTES, 1], base)
+    scale = pages.as_strided(
+        lead + [PAGE_TOKENS, SCALE_BYTES], lead_strides + [SCALE_BYTES, 1], base + PAGE_TOKENS * DATA_BYTES
+    )
+    return data, scale
+
+
+def _check_pages(pages, name, ndim):
+    _need(pages.dtype == torch.uint8, f"{name} must be uint8, got {pages.dtype}")
+    _need(pages.dim() == ndim and pages.shape[-1] == PAGE_BYTES, f"{name} must be [{'..., ' * (ndim - 1)}{PAGE_BYTES}]")
+    _need(pages.is_contiguous(), f"{name} must be contiguous")
+
+
+# --- packing and dequantisation ----------------------------------------------------
+
+
+def mxfp4_pages_pack(codes, scales, out=None):
+    """uint8 codes ``[n, 128, 128]`` + e8m0 scales ``[n, 128, 4]`` -> pages ``[n, 8704]``."""
+    load_library()
+    _need(codes.dtype == torch.uint8 and codes.dim() == 3 and tuple(codes.shape[1:]) == (128, 128), "codes: uint8 [n,128,128]")
+    n = codes.shape[0]
+    _need(scales.dtype == torch.uint8 and tuple(scales.shape) == (n, 128, 4), "scales: uint8 [n,128,4]")
+    _need(codes.is_contiguous() and scales.is_contiguous(), "codes and scales must be contiguous")
+    dev = _on_gpu(codes, scales)
+    if out is None:
+        out = torch.empty((n, PAGE_BYTES), dtype=torch.uint8, device=dev)
+    _check_pages(out, "out", 2)
+    _need(out.shape[0] == n, "out must have n pages")
+    _check(_lib.mxfp4_pages_pack(_ptr(codes), _ptr(scales), _ptr(out), n, _stream(dev)))
+    return out
+
+
+def mxfp4_pages_unpack(pages):
+    """pages ``[n, 8704]`` -> (codes ``[n, 128, 128]``, scales ``[n, 128, 4]``)."""
+    load_library()
+    _check_pages(pages, "pages", 2)
+    dev = _on_gpu(pages)
+    n = pages.shape[0]
+    codes = torch.empty((n, 128, 128), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, 128, 4), dtype=torch.uint8, device=dev)
+    _check(_lib.mxfp4_pages_unpack(_ptr(pages), _ptr(codes), _ptr(scales), n, _stream(dev)))
+    return codes, scales
+
+
+def mxfp4_pages_dequant(pages):
+    """pages ``[n, 8704]`` -> exact fp32 values ``[n, 128, 128]``."""
+    load_library()
+    _check_pages(pages, "pages", 2)
+    dev = _on_gpu(pages)
+    out = torch.empty((pages.shape[0], 128, 128), dtype=torch.float32, device=dev)
+    _check(_lib.mxfp4_pages_dequant(_ptr(pages), _ptr(out), pages.shape[0], _stream(dev)))
+    return out
+
+
+def mxfp4_pages_dequant_bf16(pages):
+    """pages ``[n, 8704]`` -> bf16 values ``[n, 128, 128]`` via the kernels' conversion."""
+    load_library()
+    _check_pages(pages, "pages", 2)
+    dev = _on_gpu(pages)
+    out = torch.empty((pages.shape[0], 128, 128), dtype=torch.bfloat16, device=dev)
+    _check(_lib.mxfp4_pages_dequant_bf16(_ptr(pages), _ptr(out), pages.shape[0], _stream(dev)))
+    return out
+
+
+# --- workspaces --------------------------------------------------------------------
+
+
+class Workspace:
+    """A zero-filled device buffer that the step calls reuse.
+
+    It starts zero-filled; every successful call leaves its counters and
+    histograms zero again, so one buffer serves any number of calls made one
+    after another.  Calls that share a workspace must not run concurrently.
+    """
+
+    def __init__(self, device, nbytes=0):
+        self.device = torch.device(device)
+        self.buf = None
+        self.ensure(nbytes)
+
+    def ensure(self, nbytes):
+        nbytes = max(int(nbytes), 256)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=self.device)
+            assert self.buf.data_ptr() % 256 == 0
+        return self.buf
+
+    @property
+    def nbytes(self):
+        return self.buf.numel()
+
+
+_default_ws = {}
+
+
+def _workspace(ws, device, nbytes, key):
+    if ws is None:
+        ws = _default_ws.get((device, key))
+        if ws is None:
+            ws = _default_ws[(device, key)] = Workspace(device, nbytes)
+    ws.ensure(nbytes)
+    return ws
+
+
+def check_device_errors(ws):
+    """Synchronise and return (then clear) the device error bits of a workspace."""
+    load_library()
+    rc = _lib.mono_check_device_errors(_ptr(ws.buf), _stream(ws.device))
+    if rc < 0:
+        _check(rc)
+    return rc
+
+
+def default_workspaces(device=None):
+    """The per-device workspaces used when a call is not given one."""
+    dev = torch.device(device) if device is not None else None
+    return [w for (d, _), w in _default_ws.items() if dev is None or d == dev]
+
+
+# --- step tables -------------------------------------------------------------------
+
+
+def _check_tables(block_table, seq_lens, n_tokens, T):
+    _need(T >= 1, f"T must be >= 1, got {T}")
+    _need(n_tokens >= 1 and n_tokens % T == 0, f"{n_tokens} tokens for {T} per request")
+    B = n_tokens // T
+    _need(block_table.dtype == torch.int32 and seq_lens.dtype == torch.int32, "tables not int32")
+    _need(block_table.dim() == 2 and seq_lens.dim() == 1, "block_table must be 2-D and seq_lens 1-D")
+    _need(block_table.shape[0] >= B and seq_lens.shape[0] >= B, "tables shorter than the batch")
+    _need(block_table.stride(1) == 1 and block_table.stride(0) == block_table.shape[1], "block table not row-contiguous")
+    _need(seq_lens.stride(0) == 1, "seq_lens must be contiguous")
+    return B
+
+
+def index_score_topk_workspace_bytes(B, T, bt_stride, k):
+    return int(load_library().mono_index_score_topk_workspace(B, T, bt_stride, k))
+
+
+def pa_decode_workspace_bytes(B, T, kv_heads, bt_stride, k, sparse):
+    return int(load_library().mono_pa_decode_workspace(B, T, kv_heads, bt_stride, k, int(bool(sparse))))
+
+
+def mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, *, T=1, out=None,
+                          out_scores=None, return_scores=False, workspace=None):
+    """Top-k token positions per query token by fp32 index score.
+
+    index_q: bf16 ``[B*T, 128]``; index_pages: uint8 ``[P, 8704]``;
+    block_table: int32 ``[>=B, W]`` row-contiguous; seq_lens: int32 ``[>=B]``.
+    Returns int32 ``[B*T, k]`` (any order within a row, -1 padding), and the
+    fp32 scores of the selected tokens too if ``return_scores``.
+    """
+    lib = load_library()
+    _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM,
+          "index_q must be bf16 [B*T, 128]")
+    _need(index_q.is_contiguous(), "index_q must be contiguous")
+    _check_pages(index_pages, "index_pages", 2)
+    N = index_q.shape[0]
+    B = _check_tables(block_table, seq_lens, N, T)
+    dev = _on_gpu(index_q, index_pages, block_table, seq_lens)
+    k = int(k)
+    _need(k >= 1, "k must be >= 1")
+    bt_stride = block_table.shape[1]
+    if out is None:
+        out = torch.empty((N, k), dtype=torch.int32, device=dev)
+    _need(out.dtype == torch.int32 and tuple(out.shape) == (N, k) and out.is_contiguous(), "out must be int32 [B*T, k]")
+    if return_scores and out_scores is None:
+        out_scores = torch.empty((N, k), dtype=torch.float32, device=dev)
+    if out_scores is not None:
+        _need(out_scores.dtype == torch.float32 and tuple(out_scores.shape) == (N, k) and out_scores.is_contiguous(),
+              "out_scores must be fp32 [B*T, k]")
+    nbytes = lib.mono_index_score_topk_workspace(B, T, bt_stride, k)
+    _need(nbytes > 0, "invalid shape for mono_index_score_topk")
+    ws = _workspace(workspace, dev, nbytes, "topk")
+    _check(lib.mono_index_score_topk(
+        _ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table), bt_stride,
+        _ptr(seq_lens), B, T, k, _ptr(out), _ptr(out_scores), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    return (out, out_scores) if return_scores else out
+
+
+def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_idx=None,
+                         scale=1.0 / math.sqrt(HEAD_DIM), *, T=1, out=None, workspace=None):
+    """Paged GQA decode attention over MXFP4 K/V pages.
+
+    q: bf16 ``[B*T, 16*H, 128]``; k_pages/v_pages: uint8 ``[P, H, 8704]``;
+    selected_idx: None (dense: every token up to each query's position) or
+    int32 ``[B*T, k]`` (entries < 0 or past the position are skipped).
+    Returns bf16 ``[B*T, 16*H, 128]``.
+    """
+    lib = load_library()
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be bf16 [B*T, 16*H, 128]")
+    _need(q.is_contiguous(), "q must be contiguous")
+    _check_pages(k_pages, "k_pages", 3)
+    _check_pages(v_pages, "v_pages", 3)
+    _need(k_pages.shape == v_pages.shape, "k_pages and v_pages must have the same shape")
+    H = k_pages.shape[1]
+    _need(q.shape[1] == Q_HEADS_PER_KV * H, f"q has {q.shape[1]} heads; the pools have {H} KV heads x 16")
+    N = q.shape[0]
+    B = _check_tables(block_table, seq_lens, N, T)
+    dev = _on_gpu(q, k_pages, v_pages, block_table, seq_lens)
+    bt_stride = block_table.shape[1]
+    k = 0
+    if selected_idx is not None:
+        _on_gpu(q, selected_idx)
+        _need(selected_idx.dtype == torch.int32 and selected_idx.dim() == 2 and selected_idx.shape[0] == N
+              and selected_idx.is_contiguous(), "selected_idx must be int32 [B*T, k], contiguous")
+        k = selected_idx.shape[1]
+        _need(k >= 1, "selected_idx must have k >= 1 columns")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.dtype == torch.bfloat16 and out.shape == q.shape and out.is_contiguous(), "out must match q")
+    nbytes = lib.mono_pa_decode_workspace(B, T, H, bt_stride, k, int(selected_idx is not None))
+    _need(nbytes > 0, "invalid shape for mono_pa_decode_mxfp4")
+    ws = _workspace(workspace, dev, nbytes, "pa")
+    _check(lib.mono_pa_decode_mxfp4(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H, _ptr(block_table), bt_stride,
+        _ptr(seq_lens), B, T, _ptr(selected_idx), k, ctypes.c_float(float(scale)), _ptr(out),
+        _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    return out

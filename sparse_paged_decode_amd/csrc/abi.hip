@@ -1,0 +1,182 @@
+// C ABI of libmono_decode.so: argument validation, error reporting and the
+// calls into the kernel launchers.  The contract of every entry point is in
+// include/mono_decode.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/mono_decode.h"
+#include "launch.h"
+
+namespace mono {
+
+namespace {
+thread_local char g_error[512] = "";
+
+inline void clear_error() { g_error[0] = '\0'; }
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxBtStride = 1 << 20;  // 2^27 tokens per request
+constexpr int kMaxHeads = 64;
+}  // namespace
+
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(MONO_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return MONO_OK;
+}
+
+namespace {
+
+int check_step_shape(int B, int T, int bt_stride, int k, bool need_k) {
+  if (B < 1) return set_error(MONO_EINVAL, "B must be >= 1 (got %d)", B);
+  if (T < 1) return set_error(MONO_EINVAL, "T must be >= 1 (got %d)", T);
+  if ((long long)B * T > (1LL << 30)) return set_error(MONO_EINVAL, "B*T too large (%d x %d)", B, T);
+  if (bt_stride < 1 || bt_stride > kMaxBtStride)
+    return set_error(MONO_EINVAL, "bt_stride must be in [1, %d] (got %d)", kMaxBtStride, bt_stride);
+  if (need_k && k < 1) return set_error(MONO_EINVAL, "k must be >= 1 (got %d)", k);
+  if (need_k && k > bt_stride * MONO_PAGE_TOKENS)
+    return set_error(MONO_EINVAL, "k (%d) exceeds the block table's capacity (%d tokens)", k,
+                     bt_stride * MONO_PAGE_TOKENS);
+  return MONO_OK;
+}
+
+int check_pages_args(const void* a, const void* b, const void* c, int64_t n_pages, const char* what) {
+  if (n_pages < 0) return set_error(MONO_EINVAL, "%s: n_pages < 0", what);
+  if (n_pages > (int64_t)1 << 34) return set_error(MONO_EINVAL, "%s: n_pages too large", what);
+  if (n_pages > 0 && (!a || !b || !c))
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  return MONO_OK;
+}
+
+}  // namespace
+}  // namespace mono
+
+using namespace mono;
+
+extern "C" {
+
+int mono_abi_version(void) { return MONO_ABI_VERSION; }
+
+const char* mono_last_error(void) { return g_error; }
+
+int mxfp4_pages_pack(const uint8_t* codes_dev, const uint8_t* scales_dev, uint8_t* pages_dev,
+                     int64_t n_pages, void* stream) {
+  clear_error();
+  if (int rc = check_pages_args(codes_dev, scales_dev, pages_dev, n_pages, "mxfp4_pages_pack")) return rc;
+  if (n_pages == 0) return MONO_OK;
+  if (!aligned(codes_dev, 16) || !aligned(pages_dev, 16) || !aligned(scales_dev, 4))
+    return set_error(MONO_EINVAL, "mxfp4_pages_pack: codes/pages need 16-byte and scales 4-byte alignment");
+  return launch_pack(codes_dev, scales_dev, pages_dev, n_pages, (hipStream_t)stream);
+}
+
+int mxfp4_pages_unpack(const uint8_t* pages_dev, uint8_t* codes_dev, uint8_t* scales_dev,
+                       int64_t n_pages, void* stream) {
+  clear_error();
+  if (int rc = check_pages_args(pages_dev, codes_dev, scales_dev, n_pages, "mxfp4_pages_unpack")) return rc;
+  if (n_pages == 0) return MONO_OK;
+  if (!aligned(codes_dev, 16) || !aligned(pages_dev, 16) || !aligned(scales_dev, 4))
+    return set_error(MONO_EINVAL, "mxfp4_pages_unpack: codes/pages need 16-byte and scales 4-byte alignment");
+  return launch_unpack(pages_dev, codes_dev, scales_dev, n_pages, (hipStream_t)stream);
+}
+
+int mxfp4_pages_dequant(const uint8_t* pages_dev, float* out_dev, int64_t n_pages, void* stream) {
+  clear_error();
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "mxfp4_pages_dequant")) return rc;
+  if (n_pages == 0) return MONO_OK;
+  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
+    return set_error(MONO_EINVAL, "mxfp4_pages_dequant: pages and out need 16-byte alignment");
+  return launch_dequant_f32(pages_dev, out_dev, n_pages, (hipStream_t)stream);
+}
+
+int mxfp4_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages, void* stream) {
+  clear_error();
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "mxfp4_pages_dequant_bf16")) return rc;
+  if (n_pages == 0) return MONO_OK;
+  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
+    return set_error(MONO_EINVAL, "mxfp4_pages_dequant_bf16: pages and out need 16-byte alignment");
+  return launch_dequant_bf16(pages_dev, out_dev, n_pages, (hipStream_t)stream);
+}
+
+size_t mono_index_score_topk_workspace(int B, int T, int bt_stride, int k) {
+  if (check_step_shape(B, T, bt_stride, k, true) != MONO_OK) return 0;
+  return topk_layout(B, T, bt_stride, k).total;
+}
+
+int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                          const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
+                          int B, int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev,
+                          void* ws_dev, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (!index_q_dev || !index_pages_dev || !block_table_dev || !seq_lens_dev || !selected_idx_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "mono_index_score_topk: NULL buffer");
+  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_index_score_topk: num_pages must be >= 1");
+  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(ws_dev, 256) ||
+      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4) ||
+      !aligned(selected_scores_dev, 4))
+    return set_error(MONO_EINVAL,
+                     "mono_index_score_topk: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment");
+  const TopkLayout lay = topk_layout(B, T, bt_stride, k);
+  if (ws_bytes < lay.total)
+    return set_error(MONO_ENOSPC, "mono_index_score_topk: workspace %zu B < %zu B", ws_bytes, lay.total);
+  TopkArgs a{index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride, seq_lens_dev,
+             B, T, k, selected_idx_dev, selected_scores_dev, static_cast<uint8_t*>(ws_dev)};
+  return launch_index_topk(a, lay, (hipStream_t)stream);
+}
+
+size_t mono_pa_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k, int sparse) {
+  if (check_step_shape(B, T, bt_stride, k, sparse != 0) != MONO_OK) return 0;
+  if (kv_heads < 1 || kv_heads > kMaxHeads) return 0;
+  return pa_layout(B, T, kv_heads, bt_stride, k, sparse != 0).total;
+}
+
+int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev, const uint8_t* v_pages_dev,
+                         int64_t num_pages, int kv_heads, const int32_t* block_table_dev, int bt_stride,
+                         const int32_t* seq_lens_dev, int B, int T, const int32_t* selected_idx_dev, int k,
+                         float scale, uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  clear_error();
+  const bool sparse = selected_idx_dev != nullptr;
+  if (int rc = check_step_shape(B, T, bt_stride, k, sparse)) return rc;
+  if (kv_heads < 1 || kv_heads > kMaxHeads)
+    return set_error(MONO_ENOTSUP, "mono_pa_decode_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads,
+                     kv_heads);
+  if (!q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev || !seq_lens_dev || !out_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: NULL buffer");
+  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: num_pages must be >= 1");
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: scale must be finite");
+  if (!aligned(q_dev, 16) || !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256) || !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) ||
+      !aligned(selected_idx_dev, 4))
+    return set_error(MONO_EINVAL,
+                     "mono_pa_decode_mxfp4: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment");
+  const PaLayout lay = pa_layout(B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
+  if (ws_bytes < lay.total)
+    return set_error(MONO_ENOSPC, "mono_pa_decode_mxfp4: workspace %zu B < %zu B", ws_bytes, lay.total);
+  PaArgs a{q_dev, k_pages_dev, v_pages_dev, num_pages, kv_heads, block_table_dev, bt_stride, seq_lens_dev,
+           B, T, selected_idx_dev, sparse ? k : 0, scale, out_dev, static_cast<uint8_t*>(ws_dev)};
+  return launch_pa_decode(a, lay, (hipStream_t)stream);
+}
+
+int mono_check_device_errors(void* ws_dev, void* stream) {
+  clear_error();
+  if (!ws_dev) return set_error(MONO_EINVAL, "mono_check_device_errors: NULL workspace");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  uint32_t bits = 0;
+  if (e == hipSuccess) e = hipMemcpy(&bits, ws_dev, sizeof(bits), hipMemcpyDeviceToHost);
+  if (e == hipSuccess) e = hipMemset(ws_dev, 0, sizeof(bits));
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return set_error(MONO_EHIP, "mono_check_device_errors: %s", hipGetErrorString(e));
+  return (int)(bits & 0x7fffffffu);
+}
+
+}  // extern "C"

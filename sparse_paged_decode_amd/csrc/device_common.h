@@ -1,0 +1,96 @@
+// Device helpers shared by the gfx950 kernels of libmono_decode.so.
+//
+// Page layout (page "vllm.models.minimax_m3.amd.ops.mxfp4_pages", module
+// docstring): a page is 128 rows of 64 B packed e2m1 data (element 2c in the
+// low nibble of byte c, element 2c+1 in the high nibble) followed by 128 rows
+// of 4 e8m0 scale bytes, one per 32 elements; 8704 B, no global scale.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mono {
+
+constexpr int kPageTokens = 128;
+constexpr int kHeadDim = 128;
+constexpr int kRowBytes = 64;        // packed e2m1 bytes per row
+constexpr int kScaleOffset = 8192;   // 128 rows x 64 B
+constexpr int kPageBytes = 8704;     // + 128 rows x 4 B
+constexpr int kQHeads = 16;          // query heads per KV head
+
+// Workspace error word bits (mirrors MONO_DEVERR_* of the public header).
+constexpr uint32_t kErrPageId = 1u;
+constexpr uint32_t kErrSeqLen = 2u;
+constexpr uint32_t kErrSelection = 4u;  // selection counts inconsistent (never expected)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// e8m0 byte -> the fp32 scale operand of the gfx950 scaled fp4 conversions.
+// Bytes 1..254 give the normal float 2^(e-127) (exponent field e, zero
+// mantissa).  Byte 0 gives the subnormal 2^-127 and byte 255 a quiet NaN, so
+// the operand carries the exact e8m0 value whether the instruction reads the
+// operand's value or only its exponent field.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) {
+  uint32_t bits = e << 23;
+  bits = (e == 0u) ? 0x00400000u : bits;
+  bits = (e == 255u) ? 0x7fc00000u : bits;
+  return __uint_as_float(bits);
+}
+
+// Eight e2m1 codes (one dword of packed row data: elements 8w..8w+7 when the
+// dword is the w-th of the row) -> eight bf16 values times the block scale,
+// in element order.  v_cvt_scalef32_pk_bf16_fp4 converts the two nibbles of
+// one selected byte; bf16 has fp32's exponent range, so every finite
+// product of an e2m1 value and an e8m0 scale is exact.
+__device__ __forceinline__ bf16x8_t dequant8_bf16(uint32_t packed, float scale) {
+  bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 0);
+  bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 1);
+  bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 2);
+  bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 3);
+  bf16x8_t r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+// Exact fp32 value of one e2m1 code times 2^(e-127), built from integer
+// fields: code magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are m * 2^-1 with
+// m = 0, 1, 2, 3, 4, 6, 8, 12; ldexp then applies the scale with IEEE
+// rounding (subnormal results stay exact, overflow gives inf).
+__device__ __forceinline__ float e2m1_times_e8m0_exact(uint32_t code, uint32_t e) {
+  const uint32_t mag_half = (0xC8643210u >> (4u * (code & 7u))) & 0xFu;  // m above
+  float v = (float)mag_half;
+  v = (code & 8u) ? -v : v;
+  if (e == 255u) return __uint_as_float(0x7fc00000u);
+  // 2^(e-127) * m / 2 in two steps so no intermediate leaves the range early.
+  return __builtin_amdgcn_ldexpf(v, (int)e - 128);
+}
+
+// Monotone fp32 -> uint32 key: a > b as floats <=> key(a) > key(b); NaN maps
+// to 0, below every number.
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (s != s) ? 0u : k;
+}
+
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+  bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Set device error bits in the workspace error word.
+__device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {
+  atomicOr(err, bits);
+}
+
+// Coherent (L2) load of a value other workgroups update with atomics.
+__device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace mono

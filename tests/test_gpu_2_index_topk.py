@@ -1,0 +1,133 @@
+"""GPU parity of index scoring + top-k against the oracle.
+
+Small cases compare every query token; the full-size workloads (the ones the
+benchmark times, in the same launch configuration) compare sampled query
+tokens one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import check_topk_row, to_device
+from oracle import decode, mxfp4
+from workloads import make_workload, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_amd as spd
+
+    spd.load_library()
+    assert torch.cuda.is_available()
+    return spd
+
+
+def _run(spd, w, k, **kw):
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    sel, scores = spd.mono_index_score_topk(
+        d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], k, T=w.T, return_scores=True,
+        workspace=ws, **kw)
+    torch.cuda.synchronize()
+    assert spd.check_device_errors(ws) == 0
+    # the same workspace serves the next call: counters and histograms were reset
+    again = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], k, T=w.T,
+                                      workspace=ws, **kw)
+    np.testing.assert_array_equal(np.sort(again.cpu().numpy(), axis=1), np.sort(sel.cpu().numpy(), axis=1))
+    return sel.cpu().numpy(), scores.cpu().numpy()
+
+
+SMALL = [
+    # name, B, T, seq_lens, bt_width, k
+    ("one_page_k_lt_n", 1, 1, [100], 1, 10),
+    ("k_ge_valid", 2, 1, [50, 129], 2, 200),
+    ("k_one", 3, 1, [1, 128, 700], 6, 1),
+    ("ragged_multi_token", 4, 4, [4, 300, 1000, 2049], 17, 37),
+    ("several_chunks", 2, 1, [5000, 4097], 40, 700),
+    ("t3_group", 2, 3, [640, 3001], 24, 250),
+    ("t6_two_groups", 2, 6, [900, 2300], 18, 128),
+]
+
+
+@pytest.mark.parametrize("name,B,T,lens,W,k", SMALL, ids=[c[0] for c in SMALL])
+def test_topk_small(spd, name, B, T, lens, W, k):
+    w = make_workload(name, B=B, T=T, seq_lens=lens, bt_width=W, k=k, seed=sum(map(ord, name)))
+    sel, scores = _run(spd, w, k)
+    for i in range(w.N):
+        check_topk_row(sel[i], w, i, k)
+        # the reported scores are the fp32 scores of the reported tokens
+        b = i // T
+        pos = int(w.seq_lens[b]) - T + i % T
+        n = min(k, pos + 1)
+        s = decode.index_scores(w.index_q[i], w.index_pool, w.block_table[b], pos)
+        # fp32 accumulation of 128 exact products: |err| <= 128 * 2^-24 * sum |products|
+        rows = decode.sequence_rows(w.index_pool, w.block_table[b], pos + 1)
+        mag = np.abs(rows) @ np.abs(mxfp4.bf16_bits_to_f64(w.index_q[i]))
+        j = sel[i, :n]
+        assert np.all(np.abs(scores[i, :n] - s[j]) <= 128 * 2.0**-24 * mag[j])
+        assert np.all(np.isnan(scores[i, n:]))
+
+
+def test_topk_scale_stress(spd):
+    """Wide e8m0 range (as the long-context workload uses)."""
+    w = make_workload("wide", B=2, T=1, seq_lens=[3000, 2222], bt_width=24, k=300, seed=77, exp_range=(110, 140))
+    sel, _ = _run(spd, w, 300)
+    for i in range(w.N):
+        check_topk_row(sel[i], w, i, 300)
+
+
+def test_topk_all_equal_scores_overflow_path(spd):
+    """Every score equal: the candidate list overflows and ties go to the lowest indices."""
+    w = make_workload("eq", B=1, T=1, seq_lens=[9000], bt_width=71, k=1000, seed=5)
+    codes = np.full((w.num_pages, 128, 128), 2, dtype=np.uint8)
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+    sel, _ = _run(spd, w, 1000)
+    assert sorted(sel[0].tolist()) == list(range(1000))
+
+
+def test_topk_many_ties_in_candidate_list(spd):
+    """A few distinct score values: exact ties at the threshold, candidates fit the list."""
+    w = make_workload("ties", B=1, T=1, seq_lens=[3000], bt_width=24, k=777, seed=6)
+    rng = np.random.default_rng(0)
+    codes = np.zeros((w.num_pages, 128, 128), dtype=np.uint8)
+    codes[:, :, 0] = rng.integers(0, 8, size=(w.num_pages, 128))  # score = iq[0] * value
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+    w.index_q[:, 0] = mxfp4.round_to_bf16_bits(np.array([1.0]))[0]
+    sel, _ = _run(spd, w, 777)
+    check_topk_row(sel[0], w, 0, 777)
+    ref = decode.topk(decode.index_scores(w.index_q[0], w.index_pool, w.block_table[0], 2999), 777)
+    assert sorted(sel[0].tolist()) == sorted(ref.tolist())  # lowest-index tie-break, exactly
+
+
+def test_topk_repeat_calls_deterministic(spd):
+    w = make_workload("rep", B=3, T=2, seq_lens=[3000, 5000, 4100], bt_width=40, k=512, seed=8)
+    a, _ = _run(spd, w, 512)
+    b, _ = _run(spd, w, 512)
+    np.testing.assert_array_equal(np.sort(a, axis=1), np.sort(b, axis=1))
+
+
+def test_topk_bad_page_id_is_flagged_not_dereferenced(spd):
+    w = make_workload("bad", B=2, T=1, seq_lens=[300, 300], bt_width=3, k=16, seed=9)
+    d = to_device(w)
+    d["block_table"][1, 1] = 10**6
+    ws = spd.Workspace("cuda")
+    spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], 16, workspace=ws)
+    assert spd.check_device_errors(ws) & spd.DEVERR_PAGE_ID
+
+
+@pytest.mark.parametrize("number,samples", [(3, [0, 17, 63]), (4, [0, 1, 2, 3, 258, 511]), (5, [0, 5])])
+def test_topk_full_size_sampled(spd, number, samples):
+    w = workload(number)
+    sel, _ = _run(spd, w, w.k)
+    for i in samples:
+        check_topk_row(sel[i], w, i, w.k)
+    # every row: right count, valid distinct entries, -1 padding
+    pos = decode.query_positions(w.seq_lens, w.T)
+    for i in range(w.N):
+        n = min(w.k, pos[i] + 1)
+        row = sel[i]
+        assert np.all(row[n:] == -1) and np.all((row[:n] >= 0) & (row[:n] <= pos[i]))
+        assert np.unique(row[:n]).size == n
