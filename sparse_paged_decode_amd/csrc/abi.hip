@@ -4,7 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include "../../include/mono_decode.h"
+#include "mono_decode.h"
 #include "launch.h"
 
 namespace mono {

@@ -88,9 +88,35 @@ __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {
   atomicOr(err, bits);
 }
 
-// Coherent (L2) load of a value other workgroups update with atomics.
+// Cross-workgroup hand-off within one kernel.  On gfx950 an agent-scope
+// fence writes back and invalidates the whole L2 of the XCD, which costs far
+// more than the data it protects.  Instead, every value one workgroup hands
+// to another is written and read with agent-scope atomic stores/loads (these
+// are coherent across XCDs by themselves), and the producer waits for its
+// memory operations to complete (vmcnt 0) before a barrier and the counter
+// increment that publishes them.
 __device__ __forceinline__ uint32_t load_coherent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void store_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until this thread's outstanding vector memory operations (loads,
+// stores, atomics) have completed; also a compiler memory barrier.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 }  // namespace mono

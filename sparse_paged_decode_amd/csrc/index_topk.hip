@@ -11,14 +11,13 @@
 // Two kernels:
 //   index_scan  -- streams each request's index pages once for all of its
 //                  query tokens, computes the scores with bf16 MFMA
-//                  (16 token rows x up to 4 query columns, fp32 accumulate;
+//                  (up to 4 query rows x 16 token columns, fp32 accumulate;
 //                  every product of a bf16 and an MXFP4 value is exact), stores
 //                  them in the workspace and builds a per-query histogram of
-//                  the top 11 bits of the order-preserving score key.  The
-//                  last workgroup of a request locates the bin that holds the
-//                  k-th largest score.
+//                  the top 11 bits of the order-preserving score key.
 //   topk_filter -- one workgroup per (query token, slice of 4096 scores):
-//                  tokens in bins above that bin are selected outright,
+//                  each finds the histogram bin that holds the k-th largest
+//                  score; tokens in bins above it are selected outright,
 //                  tokens in the bin become candidates.  The last workgroup of
 //                  a query token finishes the selection inside the bin with
 //                  two more radix passes (11 + 10 key bits); exact ties at the
@@ -29,10 +28,12 @@
 namespace mono {
 
 constexpr int kScanChunkPages = 16;  // index pages per scan workgroup
+constexpr int kBatch = 4;            // pages per prefetch batch
 constexpr int kHistBins = 2048;      // top 11 bits of the score key
 constexpr int kHistShift = 21;
 constexpr int kSlice = 4096;         // scores per filter workgroup
 constexpr int kCandCap = 8192;       // candidates kept per query token
+constexpr int kLdsCand = 4096;       // candidates the resolving workgroup stages in LDS
 
 TopkLayout topk_layout(int B, int T, int bt_stride, int k) {
   (void)k;
@@ -47,11 +48,9 @@ TopkLayout topk_layout(int B, int T, int bt_stride, int k) {
   l.q_groups = (T + 3) / 4;
   l.lcap = bt_stride * kPageTokens;
   l.err = take(256);
-  l.seq_cnt = take((size_t)B * l.q_groups * 4);
   l.flt_cnt = take(N * 4);
   l.out_cnt = take(N * 4);
   l.cand_cnt = take(N * 4);
-  l.meta = take(N * 16);
   l.hist = take(N * kHistBins * 4);
   l.scores = take(N * (size_t)l.lcap * 4);
   l.cand = take(N * (size_t)kCandCap * 8);
@@ -64,15 +63,14 @@ namespace {
 // grid (chunks of kScanChunkPages pages, B, query groups of 4); 256 threads.
 // Wave w scores rows 32w..32w+31 of every page of the chunk as two 16-row
 // MFMA tiles; lane (g = lane/16, m = lane%16) loads the 16-byte chunk g
-// (elements 32g..32g+31, one e8m0 block) of row m of a tile.
+// (elements 32g..32g+31, one e8m0 block) of row m of a tile, which is the
+// B-operand slot of that row's elements for the four k-steps.
 template <int TQ>
-__global__ __launch_bounds__(256) void index_scan_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void index_scan_kernel(
     const uint16_t* __restrict__ index_q, const uint8_t* __restrict__ pages, int64_t num_pages,
     const int32_t* __restrict__ block_table, int bt_stride, const int32_t* __restrict__ seq_lens,
-    int T, int k, uint8_t* __restrict__ ws, TopkLayout lay) {
+    int T, uint8_t* __restrict__ ws, TopkLayout lay) {
   __shared__ uint32_t hist[TQ * kHistBins];
-  __shared__ uint32_t scratch[8];
-  __shared__ uint32_t s_last;
 
   const int chunk = blockIdx.x, b = blockIdx.y, qg = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -94,84 +92,105 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   const int p_begin = chunk * kScanChunkPages;
   const int p_end = min(p_begin + kScanChunkPages, n_pages);
 
-  // B operand: column n = m is query token t0 + m (zero when m >= tq);
-  // its k-slot (g, e) of k-step s holds index-q element 32g + 8s + e.
+  // A operand: row m is query token t0 + m (zero when m >= tq); its k-slot
+  // (g, e) of k-step s holds index-q element 32g + 8s + e.
   const bool has_q = m < tq;
-  const int qi_lane = b * T + t0 + (has_q ? m : 0);
-  bf16x8_t bq[4];
+  bf16x8_t aq[4];
   {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(index_q + (size_t)qi_lane * kHeadDim + 32 * g);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
+        index_q + (size_t)(b * T + t0 + (has_q ? m : 0)) * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t v = src[s];
       if (!has_q) v = u32x4_t{0u, 0u, 0u, 0u};
-      bq[s] = __builtin_bit_cast(bf16x8_t, v);
+      aq[s] = __builtin_bit_cast(bf16x8_t, v);
     }
   }
-  const int my_pos = has_q ? (L - T + t0 + m) : -1;
-  float* my_scores = reinterpret_cast<float*>(ws + lay.scores) + (size_t)qi_lane * lcap;
+  // Scores and positions of the group's query tokens (used by lanes g == 0).
+  float* q_scores = reinterpret_cast<float*>(ws + lay.scores) + (size_t)(b * T + t0) * lcap;
+  const int pos0 = L - T + t0;  // position of query token t0; token t0 + i is at pos0 + i
 
   for (int x = tid; x < TQ * kHistBins; x += kBlock) hist[x] = 0;
   __syncthreads();
 
   const int32_t* bt_row = block_table + (size_t)b * bt_stride;
   const int row0 = 32 * wave + m;  // tile 0 row; tile 1 is row0 + 16
+  // 32-bit lane offsets inside a page, so each load is (page base in SGPRs) +
+  // (fixed lane offset) with no per-load address arithmetic.
+  const uint32_t off_d0 = (uint32_t)(row0 * kRowBytes + 16 * g);
+  const uint32_t off_d1 = off_d0 + 16u * kRowBytes;
+  const uint32_t off_e0 = (uint32_t)(kScaleOffset + row0 * 4 + g);
+  const uint32_t off_e1 = off_e0 + 16u * 4u;
 
-  auto page_base = [&](int p) -> const uint8_t* {
-    int pid = bt_row[p];
-    if (pid < 0 || pid >= num_pages) {
-      raise_error(err, kErrPageId);
-      pid = 0;
-    }
-    return pages + (size_t)pid * kPageBytes;
+  // The chunk's physical page ids, one per lane (lanes past the chunk repeat
+  // its last page); each page's id is then taken with readlane, so no load
+  // waits on a block-table lookup.
+  const int n_cp = p_end - p_begin;
+  int lane_pid = bt_row[p_begin + min(lane, n_cp - 1)];
+  if (lane_pid < 0 || lane_pid >= num_pages) {
+    raise_error(err, kErrPageId);
+    lane_pid = 0;
+  }
+
+  // Pages are fetched in batches of kBatch, one batch ahead of the one being
+  // scored.  Loads are unconditional (past the chunk end they repeat its last
+  // page, whose rows are then all masked), so the compiler can count the
+  // outstanding loads exactly and wait only for the batch being scored.
+  struct Rows {
+    u32x4_t d[2];
+    uint32_t e[2];
   };
-
-  const uint8_t* pg = page_base(p_begin);
-  u32x4_t d0 = *reinterpret_cast<const u32x4_t*>(pg + row0 * kRowBytes + 16 * g);
-  u32x4_t d1 = *reinterpret_cast<const u32x4_t*>(pg + (row0 + 16) * kRowBytes + 16 * g);
-  uint32_t e0 = pg[kScaleOffset + row0 * 4 + g];
-  uint32_t e1 = pg[kScaleOffset + (row0 + 16) * 4 + g];
-
-  for (int p = p_begin; p < p_end; ++p) {
-    u32x4_t nd0 = d0, nd1 = d1;
-    uint32_t ne0 = e0, ne1 = e1;
-    if (p + 1 < p_end) {  // prefetch the next page while this one is scored
-      const uint8_t* np = page_base(p + 1);
-      nd0 = *reinterpret_cast<const u32x4_t*>(np + row0 * kRowBytes + 16 * g);
-      nd1 = *reinterpret_cast<const u32x4_t*>(np + (row0 + 16) * kRowBytes + 16 * g);
-      ne0 = np[kScaleOffset + row0 * 4 + g];
-      ne1 = np[kScaleOffset + (row0 + 16) * 4 + g];
+  auto load_batch = [&](Rows* r, int p0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int cp = min(p0 + u - p_begin, n_cp - 1);
+      const uint8_t* pg = pages + (size_t)__builtin_amdgcn_readlane(lane_pid, cp) * kPageBytes;
+      r[u].d[0] = *reinterpret_cast<const u32x4_t*>(pg + off_d0);
+      r[u].d[1] = *reinterpret_cast<const u32x4_t*>(pg + off_d1);
+      r[u].e[0] = pg[off_e0];
+      r[u].e[1] = pg[off_e1];
     }
+  };
+  // Scores of the wave's 32 rows of page p: C = Q K^T with the query tokens
+  // as M and the 16 rows of a tile as N, so lane (g = 0, n) ends with the
+  // scores of row n of the tile for query tokens 0..3 (acc[i]).  The two
+  // tiles' MFMA chains are interleaved.
+  auto score_page = [&](const Rows& r, int p) {
+    const float sc0 = e8m0_scale_operand(r.e[0]);
+    const float sc1 = e8m0_scale_operand(r.e[1]);
+    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
-      const u32x4_t d = tile ? d1 : d0;
-      const float sc = e8m0_scale_operand(tile ? e1 : e0);
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 4; ++s) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[0][s], sc0), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[1][s], sc1), c1, 0, 0, 0);
+    }
+    if (g == 0) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8_bf16(d[s], sc), bq[s], acc, 0, 0, 0);
-      // acc[i] of lane (g, m): row 4g + i of the tile, query column m
-      if (has_q) {
-        const int j0 = p * kPageTokens + 32 * wave + 16 * tile + 4 * g;
-        if (j0 + 3 <= my_pos) {
-          *reinterpret_cast<f32x4_t*>(my_scores + j0) = acc;
+      for (int tile = 0; tile < 2; ++tile) {
+        const f32x4_t c = tile ? c1 : c0;
+        const int j = p * kPageTokens + 32 * wave + 16 * tile + m;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) atomicAdd(&hist[m * kHistBins + (score_key(acc[i]) >> kHistShift)], 1u);
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            if (j0 + i <= my_pos) {
-              my_scores[j0 + i] = acc[i];
-              atomicAdd(&hist[m * kHistBins + (score_key(acc[i]) >> kHistShift)], 1u);
-            }
+        for (int i = 0; i < TQ; ++i) {
+          if (i < tq && j <= pos0 + i) {
+            q_scores[(size_t)i * lcap + j] = c[i];
+            atomicAdd(&hist[i * kHistBins + (score_key(c[i]) >> kHistShift)], 1u);
           }
         }
       }
     }
-    d0 = nd0;
-    d1 = nd1;
-    e0 = ne0;
-    e1 = ne1;
+  };
+
+  // Two register sets used in turn (no copies between them, so a load never
+  // has to wait for the registers it overwrites to drain).
+  Rows ra[kBatch], rb[kBatch];
+  load_batch(ra, p_begin);
+  for (int p0 = p_begin; p0 < p_end; p0 += 2 * kBatch) {
+    load_batch(rb, p0 + kBatch);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) score_page(ra[u], p0 + u);
+    load_batch(ra, p0 + 2 * kBatch);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) score_page(rb[u], p0 + kBatch + u);
   }
   __syncthreads();
 
@@ -179,36 +198,6 @@ __global__ __launch_bounds__(256) void index_scan_kernel(
   for (int x = tid; x < tq * kHistBins; x += kBlock) {
     const uint32_t v = hist[x];
     if (v) atomicAdd(&ghist[x], v);
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.seq_cnt) + (size_t)b * lay.q_groups + qg;
-    const uint32_t prev = atomicAdd(cnt, 1u);
-    s_last = (prev == (uint32_t)(nchunks - 1)) ? 1u : 0u;
-    if (s_last) *cnt = 0u;  // every arrival is in: leave the counter zero for the next call
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // Last workgroup of this request: locate the k-th largest score's bin.
-  int4* meta = reinterpret_cast<int4*>(ws + lay.meta);
-  for (int n = 0; n < tq; ++n) {
-    const int qi = b * T + t0 + n;
-    const int n_valid = L - T + t0 + n + 1;
-    uint32_t* row = ghist + (size_t)n * kHistBins;
-    if (n_valid <= k) {
-      for (int x = tid; x < kHistBins; x += kBlock) row[x] = 0u;
-      if (tid == 0) meta[qi] = make_int4(-1, 0, n_valid, 0);
-      continue;
-    }
-    for (int x = tid; x < kHistBins; x += kBlock) hist[x] = load_coherent(&row[x]);
-    __syncthreads();
-    const BinSplit sp = find_bin_of_rank(hist, kHistBins, (uint32_t)k, scratch);
-    for (int x = tid; x < kHistBins; x += kBlock) row[x] = 0u;
-    if (tid == 0) meta[qi] = make_int4(sp.bin, (int)sp.above, n_valid, (int)sp.count);
-    __syncthreads();
   }
 }
 
@@ -219,13 +208,16 @@ struct Emitter {
   uint32_t k;
   uint32_t* err;
   // Slots past k would mean inconsistent counts; they are refused and flagged.
-  __device__ __forceinline__ void put(uint32_t slot, int j) const {
+  __device__ __forceinline__ void put(uint32_t slot, int j, float score) const {
     if (slot >= k) {
       raise_error(err, kErrSelection);
       return;
     }
     out[slot] = j;
-    if (out_scores) out_scores[slot] = scores[j];
+    if (out_scores) out_scores[slot] = score;
+  }
+  __device__ __forceinline__ void put(uint32_t slot, int j) const {
+    put(slot, j, out_scores ? scores[j] : 0.f);
   }
 };
 
@@ -235,6 +227,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const int32_t* __restr
                                                           TopkLayout lay, int32_t* __restrict__ sel_idx,
                                                           float* __restrict__ sel_scores) {
   __shared__ uint32_t hist[kHistBins];
+  __shared__ uint2 s_cand[kLdsCand];
   __shared__ uint32_t scratch[8];
   __shared__ uint32_t s_last;
   __shared__ uint32_t s_emit;
@@ -248,46 +241,75 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const int32_t* __restr
   const int n_slices = (n_valid + kSlice - 1) / kSlice;
   if (slice >= n_slices) return;
 
-  const int4 mt = reinterpret_cast<const int4*>(ws + lay.meta)[i];
   const float* sc = reinterpret_cast<const float*>(ws + lay.scores) + (size_t)i * lcap;
+  uint32_t* ghist = reinterpret_cast<uint32_t*>(ws + lay.hist) + (size_t)i * kHistBins;
   Emitter em{sel_idx + (size_t)i * k, sel_scores ? sel_scores + (size_t)i * k : nullptr, sc, (uint32_t)k,
              reinterpret_cast<uint32_t*>(ws + lay.err)};
   const int j0 = slice * kSlice, j1 = min(j0 + kSlice, n_valid);
 
-  if (mt.x < 0) {  // at most k valid tokens: all of them, then -1 padding
+  if (n_valid <= k) {  // at most k valid tokens: all of them, then -1 padding
     for (int j = j0 + tid; j < j1; j += kBlock) em.put((uint32_t)j, j);
     if (slice == 0) {
       for (int s = n_valid + tid; s < k; s += kBlock) {
         em.out[s] = -1;
         if (em.out_scores) em.out_scores[s] = __uint_as_float(0x7fc00000u);
       }
+      for (int x = tid; x < kHistBins; x += kBlock) ghist[x] = 0u;  // unused; leave it zero
     }
     return;
   }
 
-  const uint32_t B1 = (uint32_t)mt.x;
-  const uint32_t above = (uint32_t)mt.y;
-  const uint32_t in_bin = (uint32_t)mt.w;
+  // The bin of the k-th largest score, from the histogram the scan built.
+  for (int x = tid; x < kHistBins; x += kBlock) hist[x] = ghist[x];
+  __syncthreads();
+  const BinSplit sp = find_bin_of_rank(hist, kHistBins, (uint32_t)k, scratch);
+  const uint32_t B1 = (uint32_t)sp.bin;
+  const uint32_t above = sp.above;
+  const uint32_t in_bin = sp.count;
   const bool use_cand = in_bin <= (uint32_t)kCandCap;
   uint32_t* out_cnt = reinterpret_cast<uint32_t*>(ws + lay.out_cnt) + i;
   uint32_t* cand_cnt = reinterpret_cast<uint32_t*>(ws + lay.cand_cnt) + i;
   uint2* cand = reinterpret_cast<uint2*>(ws + lay.cand) + (size_t)i * kCandCap;
 
-  for (int jb = j0; jb < j1; jb += kBlock) {
-    const int j = jb + tid;
-    const bool in = j < j1;
-    const uint32_t key = in ? score_key(sc[j]) : 0u;
-    const uint32_t bin = key >> kHistShift;
-    const bool hi = in && bin > B1;
-    const bool eq = in && bin == B1;
-    const uint32_t slot = wave_append(hi, out_cnt);
-    if (hi) em.put(slot, j);
-    if (use_cand) {
-      const uint32_t cs = wave_append(eq, cand_cnt);
-      if (eq && cs < (uint32_t)kCandCap) cand[cs] = make_uint2(key, (uint32_t)j);
+  // Load all of this thread's scores first, classify them, and reserve
+  // output and candidate slots for the whole workgroup with one atomic each.
+  constexpr int kPer = kSlice / kBlock;
+  float v[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int j = j0 + q * kBlock + tid;
+    v[q] = (j < j1) ? sc[j] : 0.f;
+  }
+  uint32_t hi_mask = 0, eq_mask = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int j = j0 + q * kBlock + tid;
+    const uint32_t bin = score_key(v[q]) >> kHistShift;
+    if (j < j1 && bin > B1) hi_mask |= 1u << q;
+    if (j < j1 && bin == B1) eq_mask |= 1u << q;
+  }
+  // counts <= 4096 per workgroup, so both fit one packed 16+16-bit scan
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan(__popc(hi_mask) | (__popc(eq_mask) << 16), scratch, tot);
+  if (tid == 0) {
+    scratch[kWaves] = atomicAdd(out_cnt, tot & 0xFFFFu);
+    scratch[kWaves + 1] = use_cand ? atomicAdd(cand_cnt, tot >> 16) : 0u;
+  }
+  __syncthreads();
+  uint32_t slot = scratch[kWaves] + (before & 0xFFFFu);
+  uint32_t cs = scratch[kWaves + 1] + (before >> 16);
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int j = j0 + q * kBlock + tid;
+    if (hi_mask & (1u << q)) em.put(slot++, j, v[q]);
+    if (use_cand && (eq_mask & (1u << q))) {
+      if (cs < (uint32_t)kCandCap)
+        store_coherent(reinterpret_cast<uint64_t*>(cand + cs),
+                       ((uint64_t)(uint32_t)j << 32) | score_key(v[q]));
+      ++cs;
     }
   }
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (tid == 0) {
     uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + lay.flt_cnt) + i;
@@ -297,19 +319,32 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const int32_t* __restr
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // ---- last workgroup of query i: pick the remaining R tokens of bin B1 ----
   const uint32_t R = (uint32_t)k - above;  // 1 <= R <= in_bin
   if (tid == 0) s_emit = above;
-  // Candidate source: the compacted list, or (if it overflowed) every valid
-  // score filtered by bin.  Both yield the same multiset of (key, j).
+  // Candidate source: the compacted list (staged in LDS when it fits), or,
+  // if it overflowed, every valid score filtered by bin.  All three yield the
+  // same multiset of (key, j).
+  const bool in_lds = use_cand && in_bin <= (uint32_t)kLdsCand;
+  if (in_lds) {
+    for (int e = tid; e < (int)in_bin; e += kBlock) {
+      const uint64_t c = load_coherent(reinterpret_cast<const uint64_t*>(cand + e));
+      s_cand[e] = make_uint2((uint32_t)c, (uint32_t)(c >> 32));
+    }
+  }
   const int n_src = use_cand ? (int)in_bin : n_valid;
   auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
+    if (in_lds) {
+      const uint2 c = s_cand[e];
+      key = c.x;
+      j = (int)c.y;
+      return true;
+    }
     if (use_cand) {
-      const uint2 v = cand[e];
-      key = v.x;
-      j = (int)v.y;
+      const uint64_t c = load_coherent(reinterpret_cast<const uint64_t*>(cand + e));
+      key = (uint32_t)c;
+      j = (int)(c >> 32);
       return true;
     }
     j = e;
@@ -375,6 +410,7 @@ __global__ __launch_bounds__(256) void topk_filter_kernel(const int32_t* __restr
       taken += tot;
     }
   }
+  for (int x = tid; x < kHistBins; x += kBlock) ghist[x] = 0u;  // every slice has read it
   if (tid == 0) {
     *out_cnt = 0u;
     *cand_cnt = 0u;
@@ -388,10 +424,10 @@ int launch_index_topk(const TopkArgs& a, const TopkLayout& lay, hipStream_t stre
                 (unsigned)lay.q_groups);
   if (a.T == 1) {
     hipLaunchKernelGGL(index_scan_kernel<1>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
-                       a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.k, a.ws, lay);
+                       a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.ws, lay);
   } else {
     hipLaunchKernelGGL(index_scan_kernel<4>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
-                       a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.k, a.ws, lay);
+                       a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.ws, lay);
   }
   int rc = check_launch("mono_index_score_topk (scan)");
   if (rc) return rc;

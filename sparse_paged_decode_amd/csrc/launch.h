@@ -23,7 +23,7 @@ int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hi
 
 // ---- index scoring + top-k ----------------------------------------------------
 struct TopkLayout {
-  size_t err, seq_cnt, flt_cnt, out_cnt, cand_cnt, meta, hist, scores, cand, total;
+  size_t err, flt_cnt, out_cnt, cand_cnt, hist, scores, cand, total;
   int q_groups;  // ceil(T / 4)
   int lcap;      // bt_stride * 128
 };

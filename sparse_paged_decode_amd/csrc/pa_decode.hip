@@ -114,37 +114,61 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   const int32_t* sel_row = SPARSE ? a.selected_idx + (size_t)i * a.k : nullptr;
   const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
 
-  for (int it = 0; it < iters; ++it) {
-    const int base = e0 + kGroupTokens * (wave + kWaves * it);
-    // Lane (g, m) loads chunk g of tokens 2m and 2m+1 of the group (tile 0
-    // row m is token 2m, tile 1 row m is token 2m+1).
-    u32x4_t kd[2], vd[2];
-    uint32_t ke[2], ve[2];
-    bool valid[2];
+  // Groups are processed two at a time; the token lookups, block-table
+  // lookups and K/V loads of both are issued before either is computed, so
+  // each stage costs one memory round trip for the pair.
+  struct Tok {
+    u32x4_t kd, vd;
+    uint32_t ke, ve;
+    bool valid;
+  };
+  for (int it0 = 0; it0 < iters; it0 += 2) {
+    Tok tk[2][2];
+    int jj[2][2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int entry = base + 2 * m + u;
-      int j = -1;
-      if (entry < e1) j = SPARSE ? sel_row[entry] : entry;
-      bool ok = j >= 0 && j <= pos;
-      kd[u] = vd[u] = u32x4_t{0u, 0u, 0u, 0u};
-      ke[u] = ve[u] = 127u;
-      if (ok) {
-        const int pid = bt_row[j >> 7];
-        if (pid < 0 || pid >= a.num_pages) {
-          raise_error(err, kErrPageId);
-          ok = false;
-        } else {
-          const size_t off = ((size_t)pid * H + h) * kPageBytes;
-          const int r = j & (kPageTokens - 1);
-          kd[u] = *reinterpret_cast<const u32x4_t*>(a.k_pages + off + r * kRowBytes + 16 * g);
-          vd[u] = *reinterpret_cast<const u32x4_t*>(a.v_pages + off + r * kRowBytes + 16 * g);
-          ke[u] = a.k_pages[off + kScaleOffset + r * 4 + g];
-          ve[u] = a.v_pages[off + kScaleOffset + r * 4 + g];
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        // lane (g, m) handles tokens 2m and 2m+1 of each 32-token group
+        const int entry = e0 + kGroupTokens * (wave + kWaves * (it0 + x)) + 2 * m + u;
+        int j = -1;
+        if (it0 + x < iters && entry < e1) j = SPARSE ? sel_row[entry] : entry;
+        jj[x][u] = (j >= 0 && j <= pos) ? j : -1;
+      }
+    int pid[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pid[x][u] = jj[x][u] >= 0 ? bt_row[jj[x][u] >> 7] : -1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        Tok& t = tk[x][u];
+        t.kd = t.vd = u32x4_t{0u, 0u, 0u, 0u};
+        t.ke = t.ve = 127u;
+        t.valid = false;
+        const int j = jj[x][u];
+        if (j >= 0) {
+          if (pid[x][u] < 0 || pid[x][u] >= a.num_pages) {
+            raise_error(err, kErrPageId);
+          } else {
+            const size_t off = ((size_t)pid[x][u] * H + h) * kPageBytes;
+            const int r = j & (kPageTokens - 1);
+            t.kd = *reinterpret_cast<const u32x4_t*>(a.k_pages + off + r * kRowBytes + 16 * g);
+            t.vd = *reinterpret_cast<const u32x4_t*>(a.v_pages + off + r * kRowBytes + 16 * g);
+            t.ke = a.k_pages[off + kScaleOffset + r * 4 + g];
+            t.ve = a.v_pages[off + kScaleOffset + r * 4 + g];
+            t.valid = true;
+          }
         }
       }
-      valid[u] = ok;
-    }
+#pragma unroll
+  for (int xi = 0; xi < 2; ++xi) {
+    if (it0 + xi >= iters) break;  // uniform across the workgroup
+    u32x4_t kd[2] = {tk[xi][0].kd, tk[xi][1].kd}, vd[2] = {tk[xi][0].vd, tk[xi][1].vd};
+    uint32_t ke[2] = {tk[xi][0].ke, tk[xi][1].ke}, ve[2] = {tk[xi][0].ve, tk[xi][1].ve};
+    bool valid[2] = {tk[xi][0].valid, tk[xi][1].valid};
 
     // S^T tiles: lane (g, n) gets tokens 8g + 2i + u (i = 0..3) of head n.
     f32x4_t c[2];
@@ -216,6 +240,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
     }
     __syncthreads();
   }
+  }
 
   // ---- combine the four waves -------------------------------------------
   l_run += __shfl_xor(l_run, 16);
@@ -259,15 +284,15 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   float* pl = reinterpret_cast<float*>(a.ws + lay.pl);
   float* pacc = reinterpret_cast<float*>(a.ws + lay.pacc);
   if ((tid & 15) == 0) {
-    pm[slot * kQHeads + hd] = M;
-    pl[slot * kQHeads + hd] = lsum;
+    store_coherent(pm + slot * kQHeads + hd, M);
+    store_coherent(pl + slot * kQHeads + hd, lsum);
   }
   {
-    f32x4_t* dst = reinterpret_cast<f32x4_t*>(pacc + (slot * kQHeads + hd) * kHeadDim + d0);
-    dst[0] = f32x4_t{o[0], o[1], o[2], o[3]};
-    dst[1] = f32x4_t{o[4], o[5], o[6], o[7]};
+    float* dst = pacc + (slot * kQHeads + hd) * kHeadDim + d0;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) store_coherent(dst + x, o[x]);
   }
-  __threadfence();
+  wait_vmem();
   __syncthreads();
   if (tid == 0) {
     uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + lay.cnt) + qh;
@@ -277,25 +302,41 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
+  // (partials are read with coherent loads)
+  // Splits are read four at a time so their loads overlap.
   const size_t s0 = qh * lay.n_splits;
   M = -INFINITY;
-  for (int s = 0; s < n_splits; ++s) M = fmaxf(M, pm[(s0 + s) * kQHeads + hd]);
+  for (int s = 0; s < n_splits; s += 4) {
+    float mv[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) mv[y] = (s + y < n_splits) ? load_coherent(pm + (s0 + s + y) * kQHeads + hd) : -INFINITY;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) M = fmaxf(M, mv[y]);
+  }
   Mu = (M == -INFINITY) ? 0.f : M;
   lsum = 0.f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) o[x] = 0.f;
-  for (int s = 0; s < n_splits; ++s) {
-    const float f = __builtin_amdgcn_exp2f(pm[(s0 + s) * kQHeads + hd] - Mu);
-    lsum += pl[(s0 + s) * kQHeads + hd] * f;
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + ((s0 + s) * kQHeads + hd) * kHeadDim + d0);
-    const f32x4_t a0 = src[0], a1 = src[1];
+  for (int s = 0; s < n_splits; s += 4) {
+    float mv[4], lv[4], av[4][8];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      o[x] += a0[x] * f;
-      o[4 + x] += a1[x] * f;
+    for (int y = 0; y < 4; ++y) {
+      const bool in = s + y < n_splits;
+      const size_t sl = s0 + s + (in ? y : 0);
+      mv[y] = in ? load_coherent(pm + sl * kQHeads + hd) : -INFINITY;
+      lv[y] = in ? load_coherent(pl + sl * kQHeads + hd) : 0.f;
+      const float* src = pacc + (sl * kQHeads + hd) * kHeadDim + d0;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) av[y][x] = in ? load_coherent(src + x) : 0.f;
+    }
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const float f = __builtin_amdgcn_exp2f(mv[y] - Mu);
+      lsum += lv[y] * f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[x] += av[y][x] * f;
     }
   }
   store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
