@@ -13,14 +13,16 @@ copies, so each step reads pages that are not in the 256 MB Infinity Cache.
 
 Printed (one JSON line): achieved HBM GB/s over the KV+index bytes the method
 must read (the index pages of every valid token once per request, the K and V
-rows of every selected token once per request), the step time, the roofline
-entry of the index call (its share of the step is the largest), and the CPU
-oracle timed on a bounded sample of the same workload.
+rows of every selected token once per request) and the step time, both from
+the timed region; the roofline entry of the kernel that reads the most bytes
+(the index scan on sparse workloads), timed in a second pass of the same steps
+with per-kernel HIP events; and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 import argparse
+import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -33,6 +35,41 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
 ROW_BYTES = 68  # 64 B e2m1 data + 4 B e8m0 scales per token row
 METRIC = "decode-step µs + achieved HBM GB/s (% of peak), B=64 ctx=32k top-2048"
+CSRC = os.path.join(ROOT, "sparse_paged_decode_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+# Source files that define each kernel; their digest keys the stored counter data.
+KERNEL_SOURCES = {
+    "index_scan_kernel": ["index_topk.hip", "device_common.h", "block_ops.h"],
+    "pa_decode_kernel": ["pa_decode.hip", "device_common.h", "block_ops.h"],
+}
+
+
+def kernel_digest(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload_name):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload_name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("source_digest") != kernel_digest(kernel):
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -42,8 +79,23 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
-    p.add_argument("--cpu-sample", type=int, default=6, help="query tokens timed on the CPU oracle (0 = skip)")
+    p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a plain 128 MiB device copy 10 times (counter calibration) and exit")
     return p.parse_args()
+
+
+def copy_calibration():
+    """A plain copy of known size, to calibrate rocprofv3's FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = 128 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
 
 
 def algorithmic_bytes(w, sel):
@@ -96,6 +148,9 @@ def main():
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import torch
 
@@ -144,6 +199,7 @@ def main():
     sel_np = sel.cpu().numpy() if w.sparse else None
     idx_bytes, kv_bytes = algorithmic_bytes(w, sel_np)
 
+    # Timed region: exactly K steps, events around each call only.
     K = args.steps
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
     torch.cuda.synchronize(dev)
@@ -161,12 +217,23 @@ def main():
     bytes_step = idx_bytes + kv_bytes
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
 
-    if w.sparse:
-        dom_name, dom_ms, dom_bytes = "mono_index_score_topk", float(np.mean(topk_ms)), idx_bytes
-    else:
-        dom_name, dom_ms, dom_bytes = "mono_pa_decode_mxfp4", float(np.mean(pa_ms)), kv_bytes
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    # Kernel-timing pass: the same K steps again, every kernel the library
+    # launches bracketed by HIP events on its stream (the events add launch
+    # gaps, so this pass is not the step time above).
+    torch.cuda.synchronize(dev)
+    with spd.KernelTimer(capacity=4 * K + 16) as kt:
+        for s in range(K):
+            step(s % copies)
+        torch.cuda.synchronize(dev)
 
+    # Roofline entry of the kernel that moves the most bytes: the index scan on
+    # sparse workloads (it reads every index page), attention on dense ones.
+    if w.sparse:
+        dom, dom_bytes = "index_scan_kernel", idx_bytes
+    else:
+        dom, dom_bytes = "pa_decode_kernel", kv_bytes
+    dom_us = kt.mean_us[dom]
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(w, args.cpu_sample)
@@ -201,14 +268,18 @@ def main():
             "mono_index_score_topk": round(float(np.mean(topk_ms)) * 1e3, 2) if w.sparse else 0.0,
             "mono_pa_decode_mxfp4": round(float(np.mean(pa_ms)) * 1e3, 2),
         },
+        "kernels_us_mean": {name: round(us, 2) for name, us in kt.mean_us.items()},
         "roofline": {
             "bound": "hbm",
-            "kernel": dom_name,
+            "kernel": dom,
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(dom, w.name),
+            "algorithmic_bytes_per_launch": dom_bytes,
+            "kernel_us_mean": round(dom_us, 3),
+            "source_digest": kernel_digest(dom),
         },
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

@@ -179,6 +179,24 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev,
                          const int32_t* selected_idx_dev, int k, float scale, uint16_t* out_dev,
                          void* ws_dev, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * Per-kernel timing, for benchmarks and profiling only (not for graph capture).
+ *
+ * mono_profile_start(capacity): from now on every kernel the library launches
+ * is bracketed by a pair of HIP events recorded on its stream, for at most
+ * `capacity` launches (later launches are not timed).  Creates 2*capacity
+ * events.  MONO_EINVAL if already started or capacity is out of [1, 2^20].
+ * mono_profile_stop(total_ms, launches, n): waits for the recorded events and
+ * writes, for kernel ids 0..n-1, the summed milliseconds and the number of
+ * timed launches (host arrays of n entries), then destroys the events.
+ * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
+ * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
+ * ------------------------------------------------------------------------- */
+#define MONO_NUM_KERNELS 7
+int mono_profile_start(int capacity);
+int mono_profile_stop(double* total_ms, int* launches, int n);
+const char* mono_kernel_name(int id);
+
 /* Debug/test only.  Waits for `stream`, then returns the device error bits
  * (MONO_DEVERR_*) accumulated in the workspace and clears them, or a
  * negative MONO_E* code.  ws_dev is a workspace of either call above. */

@@ -17,6 +17,7 @@ from ._binding import (  # noqa: F401
     DEVERR_SEQ_LEN,
     EXPORTED_SYMBOLS,
     HEAD_DIM,
+    KernelTimer,
     PAGE_BYTES,
     PAGE_TOKENS,
     Q_HEADS_PER_KV,

@@ -49,6 +49,9 @@ EXPORTED_SYMBOLS = (
     "mono_pa_decode_workspace",
     "mono_pa_decode_mxfp4",
     "mono_check_device_errors",
+    "mono_profile_start",
+    "mono_profile_stop",
+    "mono_kernel_name",
 )
 
 
@@ -87,6 +90,9 @@ def load_library(path=LIB_PATH):
         "mono_pa_decode_workspace": (SZ, [I, I, I, I, I, I]),
         "mono_pa_decode_mxfp4": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, P, P, SZ, P]),
         "mono_check_device_errors": (I, [P, P]),
+        "mono_profile_start": (I, [I]),
+        "mono_profile_stop": (I, [P, P, I]),
+        "mono_kernel_name": (ctypes.c_char_p, [I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -359,3 +365,37 @@ def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_id
         _ptr(seq_lens), B, T, _ptr(selected_idx), k, ctypes.c_float(float(scale)), _ptr(out),
         _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return out
+
+
+# --- per-kernel timing ---------------------------------------------------------------
+
+
+class KernelTimer:
+    """Times every kernel the library launches with HIP events (context manager).
+
+    ``with KernelTimer() as kt: ...`` then ``kt.mean_us`` maps kernel name to
+    mean microseconds per launch and ``kt.launches`` to launch counts.
+    """
+
+    def __init__(self, capacity=4096):
+        self.capacity = capacity
+        self.mean_us = {}
+        self.launches = {}
+
+    def __enter__(self):
+        _check(load_library().mono_profile_start(self.capacity))
+        return self
+
+    def __exit__(self, *exc):
+        n = 16
+        tot = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int * n)()
+        rc = _lib.mono_profile_stop(tot, cnt, n)
+        if rc < 0:
+            _check(rc)
+        for k in range(min(rc, n)):
+            if cnt[k]:
+                name = _lib.mono_kernel_name(k).decode()
+                self.launches[name] = cnt[k]
+                self.mean_us[name] = tot[k] * 1000.0 / cnt[k]
+        return False

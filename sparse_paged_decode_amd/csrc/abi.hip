@@ -4,6 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <vector>
+
 #include "mono_decode.h"
 #include "launch.h"
 
@@ -26,6 +29,32 @@ int set_error(int code, const char* fmt, ...) {
   vsnprintf(g_error, sizeof(g_error), fmt, ap);
   va_end(ap);
   return code;
+}
+
+namespace {
+// Optional per-kernel timing: pairs of HIP events recorded around launches.
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> ev;  // 2 per slot
+  std::vector<int> kid;        // kernel id per slot
+  int used = 0;
+};
+Profiler g_prof;
+const char* const kKernelNames[kNumKernels] = {"pack_kernel",         "unpack_kernel",      "dequant_f32_kernel",
+                                               "dequant_bf16_kernel", "index_scan_kernel",  "topk_filter_kernel",
+                                               "pa_decode_kernel"};
+}  // namespace
+
+bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof.on) return false;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on || g_prof.used >= (int)g_prof.kid.size()) return false;
+  const int sl = g_prof.used++;
+  g_prof.kid[sl] = id;
+  *start = g_prof.ev[2 * sl];
+  *stop = g_prof.ev[2 * sl + 1];
+  return true;
 }
 
 int check_launch(const char* what) {
@@ -166,6 +195,53 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev, cons
            B, T, selected_idx_dev, sparse ? k : 0, scale, out_dev, static_cast<uint8_t*>(ws_dev)};
   return launch_pa_decode(a, lay, (hipStream_t)stream);
 }
+
+int mono_profile_start(int capacity) {
+  clear_error();
+  if (capacity < 1 || capacity > (1 << 20)) return set_error(MONO_EINVAL, "mono_profile_start: capacity out of range");
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (g_prof.on) return set_error(MONO_EINVAL, "mono_profile_start: already started");
+  g_prof.ev.assign(2 * (size_t)capacity, nullptr);
+  g_prof.kid.assign((size_t)capacity, -1);
+  for (auto& e : g_prof.ev) {
+    if (hipEventCreate(&e) != hipSuccess) return set_error(MONO_EHIP, "mono_profile_start: hipEventCreate failed");
+  }
+  g_prof.used = 0;
+  g_prof.on = true;
+  return MONO_OK;
+}
+
+int mono_profile_stop(double* total_ms, int* launches, int n_kernels) {
+  clear_error();
+  std::lock_guard<std::mutex> lock(g_prof.mu);
+  if (!g_prof.on) return set_error(MONO_EINVAL, "mono_profile_stop: not started");
+  g_prof.on = false;
+  int rc = MONO_OK;
+  for (int k = 0; k < n_kernels && total_ms && launches; ++k) {
+    total_ms[k] = 0.0;
+    launches[k] = 0;
+  }
+  for (int sl = 0; sl < g_prof.used; ++sl) {
+    float ms = 0.f;
+    if (hipEventSynchronize(g_prof.ev[2 * sl + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, g_prof.ev[2 * sl], g_prof.ev[2 * sl + 1]) != hipSuccess) {
+      rc = set_error(MONO_EHIP, "mono_profile_stop: event timing failed");
+      break;
+    }
+    const int k = g_prof.kid[sl];
+    if (k >= 0 && k < n_kernels && total_ms && launches) {
+      total_ms[k] += ms;
+      launches[k] += 1;
+    }
+  }
+  for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
+  g_prof.ev.clear();
+  g_prof.kid.clear();
+  g_prof.used = 0;
+  return rc == MONO_OK ? kNumKernels : rc;
+}
+
+const char* mono_kernel_name(int id) { return (id >= 0 && id < kNumKernels) ? kKernelNames[id] : ""; }
 
 int mono_check_device_errors(void* ws_dev, void* stream) {
   clear_error();

@@ -423,16 +423,16 @@ int launch_index_topk(const TopkArgs& a, const TopkLayout& lay, hipStream_t stre
   const dim3 g1((unsigned)((a.bt_stride + kScanChunkPages - 1) / kScanChunkPages), (unsigned)a.B,
                 (unsigned)lay.q_groups);
   if (a.T == 1) {
-    hipLaunchKernelGGL(index_scan_kernel<1>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
+    MONO_LAUNCH(kKIndexScan, index_scan_kernel<1>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
                        a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.ws, lay);
   } else {
-    hipLaunchKernelGGL(index_scan_kernel<4>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
+    MONO_LAUNCH(kKIndexScan, index_scan_kernel<4>, g1, dim3(kBlock), 0, stream, a.index_q, a.pages,
                        a.num_pages, a.block_table, a.bt_stride, a.seq_lens, a.T, a.ws, lay);
   }
   int rc = check_launch("mono_index_score_topk (scan)");
   if (rc) return rc;
   const dim3 g2((unsigned)(a.B * a.T), (unsigned)((lay.lcap + kSlice - 1) / kSlice));
-  hipLaunchKernelGGL(topk_filter_kernel, g2, dim3(kBlock), 0, stream, a.seq_lens, a.T, a.k, a.ws, lay,
+  MONO_LAUNCH(kKTopkFilter, topk_filter_kernel, g2, dim3(kBlock), 0, stream, a.seq_lens, a.T, a.k, a.ws, lay,
                      a.selected_idx, a.selected_scores);
   return check_launch("mono_index_score_topk (select)");
 }

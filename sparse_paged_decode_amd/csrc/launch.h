@@ -2,6 +2,7 @@
 // kernel files.  Every launcher only enqueues work on `stream`.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -11,6 +12,24 @@ namespace mono {
 // Records `what` and the pending HIP launch error (if any) as the thread's
 // last error; returns MONO_OK or MONO_EHIP.
 int check_launch(const char* what);
+
+// Kernel ids of the optional per-kernel event timing (mono_profile_*).
+enum KernelId { kKPack = 0, kKUnpack, kKDequant, kKDequantBf16, kKIndexScan, kKTopkFilter, kKPaDecode, kNumKernels };
+// When timing is on, takes the next pair of timing events for kernel `id`
+// and returns true; the launch then records them as part of its dispatch.
+bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop);
+
+// Launch through hipExtLaunchKernelGGL with dispatch-attached start/stop
+// events while per-kernel timing is on, plain hipLaunchKernelGGL otherwise.
+#define MONO_LAUNCH(ID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                              \
+  do {                                                                                       \
+    hipEvent_t mono_ev0_ = nullptr, mono_ev1_ = nullptr;                                     \
+    if (::mono::prof_slot((ID), &mono_ev0_, &mono_ev1_))                                     \
+      hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, mono_ev0_, mono_ev1_, 0u,    \
+                            __VA_ARGS__);                                                    \
+    else                                                                                     \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                   \
+  } while (0)
 // Records a formatted error message; returns `code`.
 int set_error(int code, const char* fmt, ...);
 

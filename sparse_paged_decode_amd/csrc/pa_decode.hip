@@ -347,9 +347,9 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
 int launch_pa_decode(const PaArgs& a, const PaLayout& lay, hipStream_t stream) {
   const dim3 grid((unsigned)(a.B * a.T), (unsigned)lay.n_splits, (unsigned)a.kv_heads);
   if (a.selected_idx) {
-    hipLaunchKernelGGL(pa_decode_kernel<true>, grid, dim3(kBlock), 0, stream, a, lay);
+    MONO_LAUNCH(kKPaDecode, pa_decode_kernel<true>, grid, dim3(kBlock), 0, stream, a, lay);
   } else {
-    hipLaunchKernelGGL(pa_decode_kernel<false>, grid, dim3(kBlock), 0, stream, a, lay);
+    MONO_LAUNCH(kKPaDecode, pa_decode_kernel<false>, grid, dim3(kBlock), 0, stream, a, lay);
   }
   return check_launch("mono_pa_decode_mxfp4");
 }

@@ -125,7 +125,7 @@ inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 
 int launch_pack(const uint8_t* codes, const uint8_t* scales, uint8_t* pages, int64_t n_pages,
                 hipStream_t stream) {
   const int64_t n_rows = n_pages * kPageTokens;
-  hipLaunchKernelGGL(pack_kernel, dim3(grid_for(n_rows, 128)), dim3(128), 0, stream, codes, scales,
+  MONO_LAUNCH(kKPack, pack_kernel, dim3(grid_for(n_rows, 128)), dim3(128), 0, stream, codes, scales,
                      pages, n_rows);
   return check_launch("mxfp4_pages_pack");
 }
@@ -133,21 +133,21 @@ int launch_pack(const uint8_t* codes, const uint8_t* scales, uint8_t* pages, int
 int launch_unpack(const uint8_t* pages, uint8_t* codes, uint8_t* scales, int64_t n_pages,
                   hipStream_t stream) {
   const int64_t n_rows = n_pages * kPageTokens;
-  hipLaunchKernelGGL(unpack_kernel, dim3(grid_for(n_rows, 128)), dim3(128), 0, stream, pages, codes,
+  MONO_LAUNCH(kKUnpack, unpack_kernel, dim3(grid_for(n_rows, 128)), dim3(128), 0, stream, pages, codes,
                      scales, n_rows);
   return check_launch("mxfp4_pages_unpack");
 }
 
 int launch_dequant_f32(const uint8_t* pages, float* out, int64_t n_pages, hipStream_t stream) {
   const int64_t n_blocks = n_pages * kPageTokens * 4;
-  hipLaunchKernelGGL(dequant_f32_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
+  MONO_LAUNCH(kKDequant, dequant_f32_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
                      out, n_blocks);
   return check_launch("mxfp4_pages_dequant");
 }
 
 int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream) {
   const int64_t n_blocks = n_pages * kPageTokens * 4;
-  hipLaunchKernelGGL(dequant_bf16_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
+  MONO_LAUNCH(kKDequantBf16, dequant_bf16_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
                      out, n_blocks);
   return check_launch("mxfp4_pages_dequant_bf16");
 }
