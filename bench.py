@@ -2,22 +2,24 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
 
-A step is one pass of the whole path over one batch: mono_index_score_topk
-(index scores + top-k) then mono_pa_decode_mxfp4 (attention over the selected
-tokens); dense workloads run the attention call alone.  The default workload
-is batch 64, context 32768 (256 pages per request), top-2048.
+A step is one pass of the whole path over one batch: on sparse workloads one
+mono_sparse_decode_mxfp4 call (index scores, top-k and attention over the
+selected tokens, in one launch); dense workloads run mono_pa_decode_mxfp4
+alone.  The default workload is batch 64, context 32768 (256 pages per
+request), top-2048.
 
 Inputs are resident in HBM before timing starts.  The K, V and index-key
 pools are replicated ``--copies`` times and the steps rotate through the
 copies, so each step reads pages that are not in the 256 MB Infinity Cache.
 
 Printed (one JSON line): achieved HBM GB/s over the KV+index bytes the method
-must read (the index pages of every valid token once per request, the K and V
+must read (the index rows of every valid token once per request, the K and V
 rows of every selected token once per request) and the step time, both from
-the timed region; the roofline entry of the kernel that reads the most bytes
-(the index scan on sparse workloads), timed in a second pass of the same steps
-with per-kernel HIP events; and the CPU oracle timed on a bounded sample of the
-same workload.
+the timed region; the roofline entry of the step kernel, timed in a second
+pass of the same steps with HIP events recorded around each launch on its
+stream; the two-call form of the step (index call, then attention call)
+timed the same way, for reference; and the CPU oracle timed on a bounded
+sample of the same workload.
 """
 
 import argparse
@@ -38,9 +40,11 @@ METRIC = "decode-step µs + achieved HBM GB/s (% of peak), B=64 ctx=32k top-2048
 CSRC = os.path.join(ROOT, "sparse_paged_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # Source files that define each kernel; their digest keys the stored counter data.
+_STEP_SOURCES = ["step.hip", "topk_device.h", "attn_device.h", "device_common.h", "block_ops.h", "launch.h"]
 KERNEL_SOURCES = {
-    "index_scan_kernel": ["index_topk.hip", "device_common.h", "block_ops.h"],
-    "pa_decode_kernel": ["pa_decode.hip", "device_common.h", "block_ops.h"],
+    "sparse_decode_kernel": _STEP_SOURCES,
+    "index_topk_kernel": _STEP_SOURCES,
+    "pa_decode_kernel": _STEP_SOURCES,
 }
 
 
@@ -178,60 +182,70 @@ def main():
         ip.append(ip[0].clone() if w.sparse else None)
     sel = torch.empty((w.N, w.k), dtype=torch.int32, device=dev) if w.sparse else None
     out = torch.empty_like(q)
+    ws = spd.Workspace(dev)
     ws_topk = spd.Workspace(dev)
     ws_pa = spd.Workspace(dev)
     stream = torch.cuda.current_stream(dev)
 
-    def step(c, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(c):
         if w.sparse:
-            spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
-        if ev is not None:
-            ev[1].record(stream)
+            spd.mono_sparse_decode_mxfp4(iq, ip[c], q, kp[c], vp[c], bt, sl, w.k, w.scale, T=w.T, out=out,
+                                         selected_idx=sel, workspace=ws)
+        else:
+            spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, None, w.scale, T=w.T, out=out, workspace=ws_pa)
+
+    def two_calls(c):
+        spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
         spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, sel, w.scale, T=w.T, out=out, workspace=ws_pa)
-        if ev is not None:
-            ev[2].record(stream)
 
     for s in range(args.warmup):
         step(s % copies)
     torch.cuda.synchronize(dev)
     sel_np = sel.cpu().numpy() if w.sparse else None
     idx_bytes, kv_bytes = algorithmic_bytes(w, sel_np)
+    bytes_step = idx_bytes + kv_bytes
 
-    # Timed region: exactly K steps, events around each call only.
+    # Timed region: exactly K steps, an event pair around each step.
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for s in range(K):
-        step(s % copies, evs[s])
+        evs[s][0].record(stream)
+        step(s % copies)
+        evs[s][1].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
 
-    step_ms = np.array([e[0].elapsed_time(e[2]) for e in evs])
-    topk_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    pa_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
-    total_ms = evs[0][0].elapsed_time(evs[-1][2])
+    step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    total_ms = evs[0][0].elapsed_time(evs[-1][1])
     ms_per_step = total_ms / K
-    bytes_step = idx_bytes + kv_bytes
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     # Kernel-timing pass: the same K steps again, every kernel the library
     # launches bracketed by HIP events on its stream (the events add launch
-    # gaps, so this pass is not the step time above).
+    # gaps, so this pass is not the step time above); then the two-call
+    # form of the step for reference.
     torch.cuda.synchronize(dev)
     with spd.KernelTimer(capacity=4 * K + 16) as kt:
         for s in range(K):
             step(s % copies)
         torch.cuda.synchronize(dev)
-
-    # Roofline entry of the kernel that moves the most bytes: the index scan on
-    # sparse workloads (it reads every index page), attention on dense ones.
+    two = {}
     if w.sparse:
-        dom, dom_bytes = "index_scan_kernel", idx_bytes
-    else:
-        dom, dom_bytes = "pa_decode_kernel", kv_bytes
+        for s in range(args.warmup):
+            two_calls(s % copies)
+        torch.cuda.synchronize(dev)
+        with spd.KernelTimer(capacity=4 * K + 16) as kt2:
+            for s in range(K):
+                two_calls(s % copies)
+            torch.cuda.synchronize(dev)
+        two = {name: round(us, 2) for name, us in kt2.mean_us.items()}
+
+    # Roofline entry of the step kernel (on dense workloads the attention
+    # kernel is the step).
+    dom = "sparse_decode_kernel" if w.sparse else "pa_decode_kernel"
+    dom_bytes = bytes_step
     dom_us = kt.mean_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     cpu = None
@@ -264,11 +278,8 @@ def main():
         "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "bytes_per_step": {"index": idx_bytes, "kv": kv_bytes},
-        "calls_us_mean": {
-            "mono_index_score_topk": round(float(np.mean(topk_ms)) * 1e3, 2) if w.sparse else 0.0,
-            "mono_pa_decode_mxfp4": round(float(np.mean(pa_ms)) * 1e3, 2),
-        },
         "kernels_us_mean": {name: round(us, 2) for name, us in kt.mean_us.items()},
+        "two_call_kernels_us_mean": two,
         "roofline": {
             "bound": "hbm",
             "kernel": dom,

@@ -52,11 +52,13 @@
  *   - The caller owns every buffer, the workspace included.  The library
  *     keeps no state between calls except a thread-local error string.
  *   - Workspaces: ask the *_workspace function for the size; the buffer
- *     must be zero-filled before its first use.  Every call that returns
- *     MONO_OK leaves the workspace's counters and histograms zero again (the
- *     rest holds scratch data that the next call overwrites), so one buffer
- *     serves any sequence of calls of any shape that fits it.  Calls that
- *     share one workspace must not overlap in time.
+ *     must be zero-filled before its first use.  Each call leaves its
+ *     counters and histograms zero again and records, in the workspace's
+ *     first bytes, how far that zero region reaches; a later call whose
+ *     zero region reaches further (another entry point or a larger shape)
+ *     clears the difference itself inside its launch.  So one buffer serves
+ *     any sequence of calls of any shape that fits it.  Calls that share one
+ *     workspace must not overlap in time.
  *   - Return value: MONO_OK (0) or a negative MONO_E* code; on error nothing
  *     was enqueued and mono_last_error() says why.  Nothing aborts.
  *   - Device-side checks: a block-table entry outside [0, num_pages) for a
@@ -87,6 +89,7 @@ extern "C" {
 #define MONO_DEVERR_PAGE_ID 1u     /* block-table entry outside [0, num_pages) */
 #define MONO_DEVERR_SEQ_LEN 2u     /* seq_lens[b] < T or > bt_stride*128 */
 #define MONO_DEVERR_SELECTION 4u   /* internal selection counts disagreed (a bug; output refused) */
+#define MONO_DEVERR_WAIT 8u        /* a bounded wait of one work item on another ran out (a bug) */
 
 /* Geometry of one MXFP4 page (mxfp4_pages page, module docstring). */
 #define MONO_PAGE_TOKENS 128
@@ -180,6 +183,32 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev,
                          void* ws_dev, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * One sparse decode step: index scores and top-k (as mono_index_score_topk)
+ * followed by attention over the selected tokens (as mono_pa_decode_mxfp4
+ * with that selection), in a single launch.  The attention of a query token
+ * starts as soon as its own selection is complete, while other query tokens
+ * are still being scored.  This composes the two operations the
+ * mxfp4_pages page names (index top-k, then the pa_decode gather over the
+ * chosen tokens); the results equal those of the two calls in sequence.
+ *
+ * index_q_dev, index_pages_dev   as for mono_index_score_topk.
+ * q_dev, k_pages_dev, v_pages_dev, kv_heads, scale, out_dev   as for
+ *                  mono_pa_decode_mxfp4.  The index pool and the K/V pools
+ *                  share num_pages and the block table.
+ * selected_idx_dev int32 [B*T, k] out: the selection (as the index call).
+ * ws_dev, ws_bytes workspace of at least mono_sparse_decode_workspace() for
+ *                  the same (B, T, kv_heads, bt_stride, k).
+ * ------------------------------------------------------------------------- */
+size_t mono_sparse_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k);
+int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                             const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                             const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                             const int32_t* block_table_dev, int bt_stride,
+                             const int32_t* seq_lens_dev, int B, int T, int k, float scale,
+                             int32_t* selected_idx_dev, uint16_t* out_dev, void* ws_dev,
+                             size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Per-kernel timing, for benchmarks and profiling only (not for graph capture).
  *
  * mono_profile_start(capacity): from now on every kernel the library launches
@@ -199,7 +228,7 @@ const char* mono_kernel_name(int id);
 
 /* Debug/test only.  Waits for `stream`, then returns the device error bits
  * (MONO_DEVERR_*) accumulated in the workspace and clears them, or a
- * negative MONO_E* code.  ws_dev is a workspace of either call above. */
+ * negative MONO_E* code.  ws_dev is a workspace of any call above. */
 int mono_check_device_errors(void* ws_dev, void* stream);
 
 #ifdef __cplusplus

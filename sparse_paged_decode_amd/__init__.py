@@ -10,11 +10,18 @@ pure-decode steps over one shared block table):
 
     sel = mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, T=T)
     out = mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, sel, scale, T=T)
+
+or both in one launch:
+
+    out, sel = mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages,
+                                        block_table, seq_lens, k, scale, T=T)
 """
 
 from ._binding import (  # noqa: F401
     DEVERR_PAGE_ID,
+    DEVERR_SELECTION,
     DEVERR_SEQ_LEN,
+    DEVERR_WAIT,
     EXPORTED_SYMBOLS,
     HEAD_DIM,
     KernelTimer,
@@ -28,11 +35,13 @@ from ._binding import (  # noqa: F401
     load_library,
     mono_index_score_topk,
     mono_pa_decode_mxfp4,
+    mono_sparse_decode_mxfp4,
     mxfp4_page_views,
     mxfp4_pages_dequant,
     mxfp4_pages_dequant_bf16,
     mxfp4_pages_pack,
     mxfp4_pages_unpack,
     pa_decode_workspace_bytes,
+    sparse_decode_workspace_bytes,
 )
 from .build import LIB_PATH  # noqa: F401

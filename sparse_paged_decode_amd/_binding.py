@@ -36,6 +36,8 @@ MONO_EHIP = -4
 
 DEVERR_PAGE_ID = 1
 DEVERR_SEQ_LEN = 2
+DEVERR_SELECTION = 4
+DEVERR_WAIT = 8
 
 EXPORTED_SYMBOLS = (
     "mono_abi_version",
@@ -48,6 +50,8 @@ EXPORTED_SYMBOLS = (
     "mono_index_score_topk",
     "mono_pa_decode_workspace",
     "mono_pa_decode_mxfp4",
+    "mono_sparse_decode_workspace",
+    "mono_sparse_decode_mxfp4",
     "mono_check_device_errors",
     "mono_profile_start",
     "mono_profile_stop",
@@ -89,6 +93,8 @@ def load_library(path=LIB_PATH):
         "mono_index_score_topk": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
         "mono_pa_decode_workspace": (SZ, [I, I, I, I, I, I]),
         "mono_pa_decode_mxfp4": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, P, P, SZ, P]),
+        "mono_sparse_decode_workspace": (SZ, [I, I, I, I, I]),
+        "mono_sparse_decode_mxfp4": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, SZ, P]),
         "mono_check_device_errors": (I, [P, P]),
         "mono_profile_start": (I, [I]),
         "mono_profile_stop": (I, [P, P, I]),
@@ -365,6 +371,56 @@ def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_id
         _ptr(seq_lens), B, T, _ptr(selected_idx), k, ctypes.c_float(float(scale)), _ptr(out),
         _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return out
+
+
+def sparse_decode_workspace_bytes(B, T, kv_heads, bt_stride, k):
+    return int(load_library().mono_sparse_decode_workspace(B, T, kv_heads, bt_stride, k))
+
+
+def mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k,
+                             scale=1.0 / math.sqrt(HEAD_DIM), *, T=1, out=None, selected_idx=None,
+                             workspace=None):
+    """One sparse decode step in one launch: index top-k, then attention over the selection.
+
+    Arguments as for :func:`mono_index_score_topk` and :func:`mono_pa_decode_mxfp4`.
+    Returns ``(out, selected_idx)``: bf16 ``[B*T, 16*H, 128]`` and int32 ``[B*T, k]``.
+    """
+    lib = load_library()
+    _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM,
+          "index_q must be bf16 [B*T, 128]")
+    _need(index_q.is_contiguous(), "index_q must be contiguous")
+    _check_pages(index_pages, "index_pages", 2)
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be bf16 [B*T, 16*H, 128]")
+    _need(q.is_contiguous(), "q must be contiguous")
+    _check_pages(k_pages, "k_pages", 3)
+    _check_pages(v_pages, "v_pages", 3)
+    _need(k_pages.shape == v_pages.shape, "k_pages and v_pages must have the same shape")
+    _need(index_pages.shape[0] == k_pages.shape[0], "the index pool and the K/V pools must have the same page count")
+    H = k_pages.shape[1]
+    _need(q.shape[1] == Q_HEADS_PER_KV * H, f"q has {q.shape[1]} heads; the pools have {H} KV heads x 16")
+    N = q.shape[0]
+    _need(index_q.shape[0] == N, "index_q and q must have the same number of query tokens")
+    B = _check_tables(block_table, seq_lens, N, T)
+    dev = _on_gpu(index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens)
+    k = int(k)
+    _need(k >= 1, "k must be >= 1")
+    bt_stride = block_table.shape[1]
+    if selected_idx is None:
+        selected_idx = torch.empty((N, k), dtype=torch.int32, device=dev)
+    _on_gpu(q, selected_idx)
+    _need(selected_idx.dtype == torch.int32 and tuple(selected_idx.shape) == (N, k) and selected_idx.is_contiguous(),
+          "selected_idx must be int32 [B*T, k]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out.dtype == torch.bfloat16 and out.shape == q.shape and out.is_contiguous(), "out must match q")
+    nbytes = lib.mono_sparse_decode_workspace(B, T, H, bt_stride, k)
+    _need(nbytes > 0, "invalid shape for mono_sparse_decode_mxfp4")
+    ws = _workspace(workspace, dev, nbytes, "step")
+    _check(lib.mono_sparse_decode_mxfp4(
+        _ptr(index_q), _ptr(index_pages), _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H,
+        _ptr(block_table), bt_stride, _ptr(seq_lens), B, T, k, ctypes.c_float(float(scale)),
+        _ptr(selected_idx), _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    return out, selected_idx
 
 
 # --- per-kernel timing ---------------------------------------------------------------

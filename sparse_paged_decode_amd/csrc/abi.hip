@@ -41,9 +41,10 @@ struct Profiler {
   int used = 0;
 };
 Profiler g_prof;
-const char* const kKernelNames[kNumKernels] = {"pack_kernel",         "unpack_kernel",      "dequant_f32_kernel",
-                                               "dequant_bf16_kernel", "index_scan_kernel",  "topk_filter_kernel",
-                                               "pa_decode_kernel"};
+// The step kernel is one kernel; it is timed under the name of the call.
+const char* const kKernelNames[kNumKernels] = {"pack_kernel",         "unpack_kernel",     "dequant_f32_kernel",
+                                               "dequant_bf16_kernel", "index_topk_kernel", "pa_decode_kernel",
+                                               "sparse_decode_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -137,7 +138,7 @@ int mxfp4_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_
 
 size_t mono_index_score_topk_workspace(int B, int T, int bt_stride, int k) {
   if (check_step_shape(B, T, bt_stride, k, true) != MONO_OK) return 0;
-  return topk_layout(B, T, bt_stride, k).total;
+  return step_layout(kModeIndex, B, T, 1, bt_stride, k, 1).total;
 }
 
 int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
@@ -154,18 +155,26 @@ int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_page
       !aligned(selected_scores_dev, 4))
     return set_error(MONO_EINVAL,
                      "mono_index_score_topk: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment");
-  const TopkLayout lay = topk_layout(B, T, bt_stride, k);
+  const StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
   if (ws_bytes < lay.total)
     return set_error(MONO_ENOSPC, "mono_index_score_topk: workspace %zu B < %zu B", ws_bytes, lay.total);
-  TopkArgs a{index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride, seq_lens_dev,
-             B, T, k, selected_idx_dev, selected_scores_dev, static_cast<uint8_t*>(ws_dev)};
-  return launch_index_topk(a, lay, (hipStream_t)stream);
+  StepArgs a{};
+  a.index_q = index_q_dev;
+  a.index_pages = index_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = selected_idx_dev;
+  a.sel_scores = selected_scores_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, "mono_index_score_topk");
 }
 
 size_t mono_pa_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k, int sparse) {
   if (check_step_shape(B, T, bt_stride, k, sparse != 0) != MONO_OK) return 0;
   if (kv_heads < 1 || kv_heads > kMaxHeads) return 0;
-  return pa_layout(B, T, kv_heads, bt_stride, k, sparse != 0).total;
+  return step_layout(kModeAttn, B, T, kv_heads, bt_stride, sparse ? k : 0, sparse != 0).total;
 }
 
 int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev, const uint8_t* v_pages_dev,
@@ -188,12 +197,70 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev, cons
       !aligned(selected_idx_dev, 4))
     return set_error(MONO_EINVAL,
                      "mono_pa_decode_mxfp4: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment");
-  const PaLayout lay = pa_layout(B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
+  const StepLayout lay = step_layout(kModeAttn, B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
   if (ws_bytes < lay.total)
     return set_error(MONO_ENOSPC, "mono_pa_decode_mxfp4: workspace %zu B < %zu B", ws_bytes, lay.total);
-  PaArgs a{q_dev, k_pages_dev, v_pages_dev, num_pages, kv_heads, block_table_dev, bt_stride, seq_lens_dev,
-           B, T, selected_idx_dev, sparse ? k : 0, scale, out_dev, static_cast<uint8_t*>(ws_dev)};
-  return launch_pa_decode(a, lay, (hipStream_t)stream);
+  StepArgs a{};
+  a.q = q_dev;
+  a.k_pages = k_pages_dev;
+  a.v_pages = v_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = const_cast<int32_t*>(selected_idx_dev);
+  a.scale = scale;
+  a.out = out_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, "mono_pa_decode_mxfp4");
+}
+
+size_t mono_sparse_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k) {
+  if (check_step_shape(B, T, bt_stride, k, true) != MONO_OK) return 0;
+  if (kv_heads < 1 || kv_heads > kMaxHeads) return 0;
+  return step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1).total;
+}
+
+int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, const uint16_t* q_dev,
+                             const uint8_t* k_pages_dev, const uint8_t* v_pages_dev, int64_t num_pages,
+                             int kv_heads, const int32_t* block_table_dev, int bt_stride,
+                             const int32_t* seq_lens_dev, int B, int T, int k, float scale,
+                             int32_t* selected_idx_dev, uint16_t* out_dev, void* ws_dev, size_t ws_bytes,
+                             void* stream) {
+  clear_error();
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (kv_heads < 1 || kv_heads > kMaxHeads)
+    return set_error(MONO_ENOTSUP, "mono_sparse_decode_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads,
+                     kv_heads);
+  if (!index_q_dev || !index_pages_dev || !q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev ||
+      !seq_lens_dev || !selected_idx_dev || !out_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: NULL buffer");
+  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: num_pages must be >= 1");
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: scale must be finite");
+  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(q_dev, 16) ||
+      !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) || !aligned(ws_dev, 256) ||
+      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4))
+    return set_error(MONO_EINVAL,
+                     "mono_sparse_decode_mxfp4: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment");
+  const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
+  if (ws_bytes < lay.total)
+    return set_error(MONO_ENOSPC, "mono_sparse_decode_mxfp4: workspace %zu B < %zu B", ws_bytes, lay.total);
+  StepArgs a{};
+  a.index_q = index_q_dev;
+  a.index_pages = index_pages_dev;
+  a.q = q_dev;
+  a.k_pages = k_pages_dev;
+  a.v_pages = v_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = selected_idx_dev;
+  a.scale = scale;
+  a.out = out_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, "mono_sparse_decode_mxfp4");
 }
 
 int mono_profile_start(int capacity) {

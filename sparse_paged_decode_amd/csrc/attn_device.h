@@ -1,4 +1,5 @@
-// Paged GQA decode attention over MXFP4 K/V pages (gfx950).
+// Paged GQA decode attention over MXFP4 K/V pages: one split of one query
+// token and KV head (gfx950).
 //
 // The pa_decode the mxfp4_pages page names reads [pages, heads, 8704] K and V
 // pools as [pages, heads, 128, 64] data and [pages, heads, 128, 4] scales
@@ -7,8 +8,7 @@
 // head over the candidate tokens (a selection list, or every token
 // 0..pos), softmax, and the probability-weighted sum of the V rows.
 //
-// Work split: one workgroup per (query token, split of `split_tokens`
-// candidates, KV head); each wave takes groups of 32 candidates.  Per group:
+// A split covers candidates [e0, e1); each wave takes groups of 32.  Per group:
 //   * QK^T on bf16 MFMA 16x16x32 with the *tokens* as the M dimension (two
 //     16-token tiles) and the 16 query heads as N, so each lane ends with the
 //     logits of one head for 8 tokens -- exactly the B-operand layout the PV
@@ -19,45 +19,55 @@
 //     tokens per lane with one 16-byte LDS load per 16-dim tile.
 // Dequantised K/V are exact in bf16, so the only roundings are fp32
 // accumulation, exp2, and the bf16 rounding of the probabilities (the row
-// sums use the same rounded values).  Workgroup partials (max, sum, 16x128
-// accumulator) are merged by the last workgroup of each (query, KV head).
+// sums use the same rounded values).  Split partials (max, sum, 16x128
+// accumulator) are handed over with coherent stores; the last split to
+// arrive merges them and writes the bf16 output.
+#pragma once
+
 #include "block_ops.h"
 #include "launch.h"
 
 namespace mono {
 
 constexpr int kGroupTokens = 32;
-constexpr int kVtRowBytes = 80;        // 16 token pairs x 4 B + 16 B pad
-constexpr int kVtRegionBytes = 10496;  // 128 rows + 3 x 64 B group pad, per wave
+constexpr int kVtRowBytes = 64;        // 16 token pairs x 4 B
+constexpr int kVtRegionBytes = 8384;   // 128 rows + 3 x 64 B group pad, per wave
+// After the token loop the same memory holds the four waves' partial
+// accumulators (32 KiB) and their running maxima and sums.
+constexpr int kSoBytes = kWaves * kQHeads * kHeadDim * 4;
+static_assert(kSoBytes + 2 * kWaves * kQHeads * 4 + 4 <= kWaves * kVtRegionBytes, "attention LDS overlap");
 
-PaLayout pa_layout(int B, int T, int kv_heads, int bt_stride, int k, int sparse) {
-  PaLayout l{};
-  const size_t NH = (size_t)B * T * kv_heads;
-  const long list_max = sparse ? (long)k : (long)bt_stride * kPageTokens;
-  int split = 256;
-  while (split < 8192 && NH * (size_t)((list_max + split - 1) / split) > 4096) split *= 2;
-  l.split_tokens = split;
-  l.n_splits = (int)((list_max + split - 1) / split);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return o;
-  };
-  const size_t S = (size_t)l.n_splits;
-  l.err = take(256);
-  l.cnt = take(NH * 4);
-  l.pm = take(NH * S * kQHeads * 4);
-  l.pl = take(NH * S * kQHeads * 4);
-  l.pacc = take(NH * S * kQHeads * kHeadDim * 4);
-  l.total = off;
-  return l;
-}
+struct AttnLds {
+  __attribute__((aligned(16))) uint8_t vt[kWaves * kVtRegionBytes];
+};
 
-namespace {
+struct AttnArgs {
+  const uint16_t* q;        // this query token's 16 heads of KV head h: [16, 128]
+  const uint8_t* k_pages;   // [num_pages, H, 8704]
+  const uint8_t* v_pages;
+  int64_t num_pages;
+  int H, h;
+  const int32_t* bt_row;    // block-table row of the request
+  const int32_t* sel_row;   // selection list (coherent reads) or nullptr: dense
+  int pos;                  // position of the query token
+  int e0, e1;               // candidates of this split
+  int split, n_splits;
+  float scale;
+  uint16_t* out;            // [16, 128] bf16 output of (query token, KV head)
+  float* pm;                // [n_splits, 16] partial maxima of (query token, KV head)
+  float* pl;                // [n_splits, 16] partial sums
+  float* pacc;              // [n_splits, 16, 128] partial accumulators
+  uint32_t* split_cnt;      // arrivals of (query token, KV head)
+  uint32_t* err;
+};
 
+// V^T element (dim, token pair) in a wave's region.  Rows are 64 B; the
+// 16-byte chunk of a pair is XOR-swizzled by bits 2..3 of the row so the
+// 16-row x 16-byte reads of one MFMA tile hit 64 distinct banks, and each
+// group of 32 rows is shifted by 64 B so the four lane groups writing rows
+// 32 apart do too.
 __device__ __forceinline__ int vt_offset(int dim, int pair) {
-  return dim * kVtRowBytes + (dim >> 5) * 64 + pair * 4;
+  return dim * kVtRowBytes + (dim >> 5) * 64 + ((((pair >> 2) ^ (dim >> 2)) & 3) << 4) + (pair & 3) * 4;
 }
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float* o, float inv) {
@@ -67,40 +77,18 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float* o, floa
   *reinterpret_cast<u32x4_t*>(dst) = w;
 }
 
-// grid (B*T, splits, kv_heads); 256 threads.
-template <bool SPARSE>
-__global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kVtRegionBytes];
-  __shared__ float s_m[kWaves][kQHeads];
-  __shared__ float s_l[kWaves][kQHeads];
-  __shared__ uint32_t s_last;
-
-  const int i = blockIdx.x, split = blockIdx.y, h = blockIdx.z;
+__device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
-  uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
-  const int b = i / a.T, t = i % a.T;
-  const int L = a.seq_lens[b];
-  if (L < a.T || L > a.bt_stride * kPageTokens) {
-    if (split == 0 && h == 0 && tid == 0) raise_error(err, kErrSeqLen);
-    return;
-  }
-  const int pos = L - a.T + t;
-  const int list_len = SPARSE ? a.k : pos + 1;
-  const int n_splits = SPARSE ? lay.n_splits : (list_len + lay.split_tokens - 1) / lay.split_tokens;
-  if (split >= n_splits) return;
-  const int e0 = split * lay.split_tokens;
-  const int e1 = min(e0 + lay.split_tokens, list_len);
+  const int e0 = a.e0, e1 = a.e1, pos = a.pos, H = a.H, h = a.h, split = a.split, n_splits = a.n_splits;
   const int n_groups = (e1 - e0 + kGroupTokens - 1) / kGroupTokens;
   const int iters = (n_groups + kWaves - 1) / kWaves;
-  const int H = a.kv_heads;
 
-  // B operand of QK^T: column n = m is query head 16h + m; k-slot (g, e) of
-  // k-step s holds q element 32g + 8s + e.
+  // B operand of QK^T: column n = m is query head m; k-slot (g, e) of k-step
+  // s holds q element 32g + 8s + e.
   bf16x8_t qb[4];
   {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(
-        a.q + ((size_t)i * H * kQHeads + (size_t)h * kQHeads + m) * kHeadDim + 32 * g);
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.q + (size_t)m * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, src[s]);
   }
@@ -109,10 +97,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   f32x4_t acc[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint8_t* vt = lds + wave * kVtRegionBytes;
-  const int32_t* sel_row = SPARSE ? a.selected_idx + (size_t)i * a.k : nullptr;
-  const int32_t* bt_row = a.block_table + (size_t)b * a.bt_stride;
+  uint8_t* vt = lds.vt + wave * kVtRegionBytes;
 
   // Groups are processed two at a time; the token lookups, block-table
   // lookups and K/V loads of both are issued before either is computed, so
@@ -132,14 +117,14 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
         // lane (g, m) handles tokens 2m and 2m+1 of each 32-token group
         const int entry = e0 + kGroupTokens * (wave + kWaves * (it0 + x)) + 2 * m + u;
         int j = -1;
-        if (it0 + x < iters && entry < e1) j = SPARSE ? sel_row[entry] : entry;
+        if (it0 + x < iters && entry < e1) j = a.sel_row ? (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + entry)) : entry;
         jj[x][u] = (j >= 0 && j <= pos) ? j : -1;
       }
     int pid[2][2];
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) pid[x][u] = jj[x][u] >= 0 ? bt_row[jj[x][u] >> 7] : -1;
+      for (int u = 0; u < 2; ++u) pid[x][u] = jj[x][u] >= 0 ? a.bt_row[jj[x][u] >> 7] : -1;
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
@@ -151,7 +136,7 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
         const int j = jj[x][u];
         if (j >= 0) {
           if (pid[x][u] < 0 || pid[x][u] >= a.num_pages) {
-            raise_error(err, kErrPageId);
+            raise_error(a.err, kErrPageId);
           } else {
             const size_t off = ((size_t)pid[x][u] * H + h) * kPageBytes;
             const int r = j & (kPageTokens - 1);
@@ -245,7 +230,10 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   // ---- combine the four waves -------------------------------------------
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  float* so = reinterpret_cast<float*>(lds);  // [wave][dim][head], 8 KiB per wave
+  float* so = reinterpret_cast<float*>(lds.vt);  // [wave][dim][head], 8 KiB per wave
+  float(*s_m)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.vt + kSoBytes);
+  float(*s_l)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.vt + kSoBytes + kWaves * kQHeads * 4);
+  uint32_t* s_last = reinterpret_cast<uint32_t*>(lds.vt + kSoBytes + 2 * kWaves * kQHeads * 4);
 #pragma unroll
   for (int x = 0; x < 8; ++x)
 #pragma unroll
@@ -272,17 +260,16 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
     for (int x = 0; x < 8; ++x) o[x] += so[w * 2048 + (d0 + x) * kQHeads + hd] * f;
   }
 
-  const size_t qh = (size_t)i * H + h;
-  uint16_t* orow = a.out + (qh * kQHeads + hd) * kHeadDim + d0;
+  uint16_t* orow = a.out + (size_t)hd * kHeadDim + d0;
   if (n_splits == 1) {
     store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
     return;
   }
 
-  const size_t slot = qh * lay.n_splits + split;
-  float* pm = reinterpret_cast<float*>(a.ws + lay.pm);
-  float* pl = reinterpret_cast<float*>(a.ws + lay.pl);
-  float* pacc = reinterpret_cast<float*>(a.ws + lay.pacc);
+  const size_t slot = (size_t)split;
+  float* pm = a.pm;
+  float* pl = a.pl;
+  float* pacc = a.pacc;
   if ((tid & 15) == 0) {
     store_coherent(pm + slot * kQHeads + hd, M);
     store_coherent(pl + slot * kQHeads + hd, lsum);
@@ -295,18 +282,16 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
   wait_vmem();
   __syncthreads();
   if (tid == 0) {
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(a.ws + lay.cnt) + qh;
-    const uint32_t prev = atomicAdd(cnt, 1u);
-    s_last = (prev == (uint32_t)(n_splits - 1)) ? 1u : 0u;
-    if (s_last) *cnt = 0u;
+    const uint32_t prev = atomicAdd(a.split_cnt, 1u);
+    *s_last = (prev == (uint32_t)(n_splits - 1)) ? 1u : 0u;
   }
   __syncthreads();
-  if (!s_last) return;
+  if (!*s_last) return;
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
   // (partials are read with coherent loads)
   // Splits are read four at a time so their loads overlap.
-  const size_t s0 = qh * lay.n_splits;
+  const size_t s0 = 0;
   M = -INFINITY;
   for (int s = 0; s < n_splits; s += 4) {
     float mv[4];
@@ -340,18 +325,6 @@ __global__ __launch_bounds__(256) void pa_decode_kernel(PaArgs a, PaLayout lay) 
     }
   }
   store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
-}
-
-}  // namespace
-
-int launch_pa_decode(const PaArgs& a, const PaLayout& lay, hipStream_t stream) {
-  const dim3 grid((unsigned)(a.B * a.T), (unsigned)lay.n_splits, (unsigned)a.kv_heads);
-  if (a.selected_idx) {
-    MONO_LAUNCH(kKPaDecode, pa_decode_kernel<true>, grid, dim3(kBlock), 0, stream, a, lay);
-  } else {
-    MONO_LAUNCH(kKPaDecode, pa_decode_kernel<false>, grid, dim3(kBlock), 0, stream, a, lay);
-  }
-  return check_launch("mono_pa_decode_mxfp4");
 }
 
 }  // namespace mono

@@ -22,6 +22,7 @@ constexpr int kQHeads = 16;          // query heads per KV head
 constexpr uint32_t kErrPageId = 1u;
 constexpr uint32_t kErrSeqLen = 2u;
 constexpr uint32_t kErrSelection = 4u;  // selection counts inconsistent (never expected)
+constexpr uint32_t kErrWait = 8u;       // a bounded wait for another work item ran out
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

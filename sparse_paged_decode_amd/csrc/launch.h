@@ -14,7 +14,7 @@ namespace mono {
 int check_launch(const char* what);
 
 // Kernel ids of the optional per-kernel event timing (mono_profile_*).
-enum KernelId { kKPack = 0, kKUnpack, kKDequant, kKDequantBf16, kKIndexScan, kKTopkFilter, kKPaDecode, kNumKernels };
+enum KernelId { kKPack = 0, kKUnpack, kKDequant, kKDequantBf16, kKIndexScan, kKPaDecode, kKStep, kNumKernels };
 // When timing is on, takes the next pair of timing events for kernel `id`
 // and returns true; the launch then records them as part of its dispatch.
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -40,52 +40,49 @@ int launch_unpack(const uint8_t* pages, uint8_t* codes, uint8_t* scales, int64_t
 int launch_dequant_f32(const uint8_t* pages, float* out, int64_t n_pages, hipStream_t stream);
 int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
 
-// ---- index scoring + top-k ----------------------------------------------------
-struct TopkLayout {
-  size_t err, flt_cnt, out_cnt, cand_cnt, hist, scores, cand, total;
-  int q_groups;  // ceil(T / 4)
-  int lcap;      // bt_stride * 128
-};
-TopkLayout topk_layout(int B, int T, int bt_stride, int k);
+// ---- the persistent step kernel (step.hip) -----------------------------------
+enum StepMode { kModeIndex = 1, kModeAttn = 2, kModeFused = 3 };
+// Header words of the control block (the same offset in every layout).
+constexpr uint32_t kHdrTicket = 0;   // next work-item ticket
+constexpr uint32_t kHdrExits = 1;    // workgroups that have left
+constexpr uint32_t kHdrCleared = 2;  // clear items done
+constexpr uint32_t kHdrZeroed = 3;   // zero region the last call left clean, in 256-B units
+constexpr uint32_t kHdrWords = 4;
 
-struct TopkArgs {
+struct StepLayout {
+  int mode, B, T, H, k, sparse;
+  int q_groups;      // ceil(T / 4) query-token groups per request
+  int chunks;        // scan chunks per request (bt_stride / 16 pages, rounded up)
+  int lcap;          // bt_stride * 128: capacity of a score row
+  int slices;        // filter slices per query token (lcap / 4096, rounded up)
+  int split_tokens;  // attention candidates per split
+  int n_splits;      // attention splits per (query token, KV head)
+  uint32_t n_clear, n_scan, n_filter, n_attn;  // work items of each kind (clear: when needed)
+  size_t zero_end;      // [ctrl_base + header, zero_end) must be zero when items start
+  uint64_t zero_units;  // zero_end / 256
+  // control block (u32 words from ctrl_base): word offsets
+  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, sel_ready, attn_cnt, ctrl_words;
+  // byte offsets in the workspace
+  size_t err, ctrl_base, hist, scores, cand, pm, pl, pacc, total;
+};
+StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
+
+struct StepArgs {
   const uint16_t* index_q;
-  const uint8_t* pages;
-  int64_t num_pages;
-  const int32_t* block_table;
-  int bt_stride;
-  const int32_t* seq_lens;
-  int B, T, k;
-  int32_t* selected_idx;
-  float* selected_scores;
-  uint8_t* ws;
-};
-int launch_index_topk(const TopkArgs& a, const TopkLayout& lay, hipStream_t stream);
-
-// ---- paged decode attention ---------------------------------------------------
-struct PaLayout {
-  size_t err, cnt, pm, pl, pacc, total;
-  int split_tokens;  // list entries per workgroup
-  int n_splits;      // workgroups per (query token, KV head)
-};
-PaLayout pa_layout(int B, int T, int kv_heads, int bt_stride, int k, int sparse);
-
-struct PaArgs {
+  const uint8_t* index_pages;
   const uint16_t* q;
   const uint8_t* k_pages;
   const uint8_t* v_pages;
   int64_t num_pages;
-  int kv_heads;
   const int32_t* block_table;
   int bt_stride;
   const int32_t* seq_lens;
-  int B, T;
-  const int32_t* selected_idx;
-  int k;
+  int32_t* sel;        // selection: written by the index items, read by sparse attention
+  float* sel_scores;   // nullable
   float scale;
   uint16_t* out;
   uint8_t* ws;
 };
-int launch_pa_decode(const PaArgs& a, const PaLayout& lay, hipStream_t stream);
+int launch_step(const StepArgs& a, const StepLayout& lay, hipStream_t stream, const char* what);
 
 }  // namespace mono

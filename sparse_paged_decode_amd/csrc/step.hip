@@ -1,0 +1,356 @@
+// One persistent work-queue kernel runs every step of the path (gfx950).
+//
+// Work items, handed out in ticket order by one atomic counter:
+//   scan   (request b, query group, chunk of 16 index pages)  -> scan_chunk
+//   filter (query token i, slice of 4096 scores)               -> filter_slice,
+//          and the last slice of i to finish                   -> resolve_query
+//   attn   (query token i, KV head h, split of candidates)    -> attn_split
+//          (the last split of (i, h) to finish merges them)
+// mono_index_score_topk runs the scan and filter items, mono_pa_decode_mxfp4
+// the attention items, mono_sparse_decode_mxfp4 all three in one launch.
+//
+// A filter item waits until every scan item of its request and query group
+// is done; a fused attention item waits until its query token's selection
+// is complete.  Items only ever wait for items with smaller tickets, which
+// were handed to running workgroups that never wait on later items, so every
+// wait ends; each wait is also bounded and flags MONO_DEVERR_WAIT if the
+// bound is reached, so the kernel always terminates.  The last workgroup to
+// leave resets the queue and all counters for the next call.
+#include "attn_device.h"
+#include "mono_decode.h"
+#include "topk_device.h"
+
+#include <mutex>
+
+namespace mono {
+
+constexpr uint32_t kMaxSpins = 1u << 21;  // bound of one wait (seconds, far above any step)
+constexpr size_t kClearBytes = 32768;     // bytes zeroed by one clear item
+
+StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse) {
+  StepLayout l{};
+  l.mode = mode;
+  l.B = B;
+  l.T = T;
+  l.H = H;
+  l.k = k;
+  l.sparse = sparse;
+  const size_t N = (size_t)B * T;
+  l.q_groups = (T + 3) / 4;
+  l.chunks = (bt_stride + kScanChunkPages - 1) / kScanChunkPages;
+  l.lcap = bt_stride * kPageTokens;
+  l.slices = (l.lcap + kSlice - 1) / kSlice;
+  const bool index = (mode & kModeIndex) != 0, attn = (mode & kModeAttn) != 0;
+  // Attention splits: 256 candidates per workgroup unless that makes more
+  // than 4096 items.
+  const long list_max = sparse ? (long)k : (long)l.lcap;
+  const size_t NH = N * H;
+  int split = 256;
+  while (split < 8192 && NH * (size_t)((list_max + split - 1) / split) > 4096) split *= 2;
+  l.split_tokens = split;
+  l.n_splits = (int)((list_max + split - 1) / split);
+
+  l.n_scan = index ? (uint32_t)(B * l.q_groups * l.chunks) : 0u;
+  l.n_filter = index ? (uint32_t)(N * l.slices) : 0u;
+  l.n_attn = attn ? (uint32_t)(NH * l.n_splits) : 0u;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  };
+  l.err = take(256);
+  // Control block: u32 words zeroed by the last workgroup of every call.
+  // Its 4-word header sits at the same offset in every layout.
+  size_t w = 0;
+  l.ctrl = w;
+  w += kHdrWords;
+  l.scan_done = w;
+  w += index ? (size_t)B * l.q_groups : 0;
+  l.filter_cnt = w;
+  w += index ? N : 0;
+  l.out_cnt = w;
+  w += index ? N : 0;
+  l.cand_cnt = w;
+  w += index ? N : 0;
+  l.sel_ready = w;
+  w += index ? N : 0;
+  l.attn_cnt = w;
+  w += attn ? NH : 0;
+  l.ctrl_words = w;
+  l.ctrl_base = take(w * 4);
+  l.hist = take(index ? N * kHistBins * 4 : 0);
+  // Everything from the end of the header to here must be zero when the
+  // items start; the rest is scratch that each call overwrites.
+  l.zero_end = off;
+  l.zero_units = (uint64_t)(off >> 8);
+  const size_t zero_bytes = off - (l.ctrl_base + kHdrWords * 4);
+  l.n_clear = (uint32_t)((zero_bytes + kClearBytes - 1) / kClearBytes);
+  l.scores = take(index ? N * (size_t)l.lcap * 4 : 0);
+  l.cand = take(index ? N * (size_t)kCandCap * 8 : 0);
+  const size_t S = (size_t)l.n_splits;
+  l.pm = take(attn ? NH * S * kQHeads * 4 : 0);
+  l.pl = take(attn ? NH * S * kQHeads * 4 : 0);
+  l.pacc = take(attn ? NH * S * kQHeads * kHeadDim * 4 : 0);
+  l.total = off;
+  return l;
+}
+
+namespace {
+
+// A clear item: zero bytes [c * kClearBytes, ...) of the region that must
+// start at zero.  Coherent stores, so atomics of other workgroups that run
+// on other dies see the zeros rather than stale data.
+__device__ __forceinline__ void clear_item(const StepLayout& lay, uint32_t c, uint8_t* ws, uint32_t* ctrl) {
+  const size_t begin = lay.ctrl_base + kHdrWords * 4 + (size_t)c * kClearBytes;
+  const size_t end = min(begin + (size_t)kClearBytes, lay.zero_end);
+  uint32_t* p = reinterpret_cast<uint32_t*>(ws + begin);
+  const int n = (int)((end - begin) / 4);
+  for (int x = threadIdx.x; x < n; x += kBlock) store_coherent(p + x, 0u);
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(ctrl + kHdrCleared, 1u);
+}
+
+// Thread 0 waits until *p >= target; everyone leaves together.
+__device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target, uint32_t* err) {
+  if (threadIdx.x == 0) {
+    uint32_t spins = 0;
+    while (load_coherent(p) < target) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++spins > kMaxSpins) {
+        raise_error(err, kErrWait);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Chunks of request b's query group qg (pages seen by the group's last query token).
+__device__ __forceinline__ int group_chunks(int L, int T, int qg, int& tq, int& n_pages) {
+  const int t0 = qg * 4;
+  tq = min(4, T - t0);
+  const int n_tok = L - T + t0 + tq;
+  n_pages = (n_tok + kPageTokens - 1) / kPageTokens;
+  return (n_pages + kScanChunkPages - 1) / kScanChunkPages;
+}
+
+template <int TQ>
+union StepLds {
+  ScanLds<TQ> scan;
+  FilterLds filter;
+  ResolveLds resolve;
+  AttnLds attn;
+};
+
+template <int TQ>
+__device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& lay, uint32_t t, ScanLds<TQ>& lds,
+                                          uint32_t* ctrl, uint32_t* err) {
+  const int per_b = lay.q_groups * lay.chunks;
+  const int b = (int)(t / per_b);
+  const int rem = (int)(t % per_b);
+  const int qg = rem / lay.chunks, c = rem % lay.chunks;
+  const int T = lay.T;
+  const int L = a.seq_lens[b];
+  if (L < T || L > lay.lcap) {
+    if (c == 0 && qg == 0 && threadIdx.x == 0) raise_error(err, kErrSeqLen);
+    return;
+  }
+  int tq, n_pages;
+  const int nchunks = group_chunks(L, T, qg, tq, n_pages);
+  if (c >= nchunks) return;
+  const int t0 = qg * 4;
+  const int q0 = b * T + t0;
+  ScanArgs sa;
+  sa.index_q = a.index_q;
+  sa.pages = a.index_pages;
+  sa.num_pages = a.num_pages;
+  sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
+  sa.q_scores = reinterpret_cast<float*>(a.ws + lay.scores) + (size_t)q0 * lay.lcap;
+  sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)q0 * kHistBins;
+  sa.err = err;
+  sa.lcap = lay.lcap;
+  sa.q0 = q0;
+  sa.pos0 = L - T + t0;
+  sa.tq = tq;
+  sa.p_begin = c * kScanChunkPages;
+  sa.p_end = min(sa.p_begin + kScanChunkPages, n_pages);
+  scan_chunk<TQ>(sa, lds);
+  wait_vmem();  // scores and histogram updates are complete before the arrival
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, 1u);
+}
+
+template <int TQ>
+__device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout& lay, uint32_t u, StepLds<TQ>& lds,
+                                            uint32_t* ctrl, uint32_t* err, uint32_t& s_flag) {
+  const int i = (int)(u / lay.slices), s = (int)(u % lay.slices);
+  const int T = lay.T, b = i / T, t = i % T;
+  const int L = a.seq_lens[b];
+  if (L < T || L > lay.lcap) return;  // reported by the scan items
+  const int n_valid = L - T + t + 1;
+  const int n_slices = (n_valid + kSlice - 1) / kSlice;
+  if (s >= n_slices) return;
+  const int qg = t / 4;
+  int tq, n_pages;
+  const int nchunks = group_chunks(L, T, qg, tq, n_pages);
+  wait_counter(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, (uint32_t)nchunks, err);
+
+  SelectArgs sa;
+  sa.scores = reinterpret_cast<const float*>(a.ws + lay.scores) + (size_t)i * lay.lcap;
+  sa.lcap = lay.lcap;
+  sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)i * kHistBins;
+  sa.out = a.sel + (size_t)i * lay.k;
+  sa.out_scores = a.sel_scores ? a.sel_scores + (size_t)i * lay.k : nullptr;
+  sa.out_cnt = ctrl + lay.out_cnt + i;
+  sa.cand = reinterpret_cast<uint64_t*>(a.ws + lay.cand) + (size_t)i * kCandCap;
+  sa.cand_cnt = ctrl + lay.cand_cnt + i;
+  sa.err = err;
+  sa.n_valid = n_valid;
+  sa.k = lay.k;
+  filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) s_flag = (atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(n_slices - 1)) ? 1u : 0u;
+  __syncthreads();
+  if (!s_flag) return;
+  resolve_query(sa, lds.resolve);
+  wait_vmem();
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(ctrl + lay.sel_ready + i, 1u);
+}
+
+template <int TQ>
+__device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& lay, uint32_t v, StepLds<TQ>& lds,
+                                          uint32_t* ctrl, uint32_t* err) {
+  const int H = lay.H, S = lay.n_splits;
+  const int i = (int)(v / (uint32_t)(H * S));
+  const int rem = (int)(v % (uint32_t)(H * S));
+  const int h = rem / S, split = rem % S;
+  const int T = lay.T, b = i / T, t = i % T;
+  const int L = a.seq_lens[b];
+  if (L < T || L > lay.lcap) {
+    if (split == 0 && h == 0 && threadIdx.x == 0) raise_error(err, kErrSeqLen);
+    return;
+  }
+  const int pos = L - T + t;
+  const int list_len = lay.sparse ? lay.k : pos + 1;
+  const int n_splits = lay.sparse ? S : (list_len + lay.split_tokens - 1) / lay.split_tokens;
+  if (split >= n_splits) return;
+  if (lay.mode == kModeFused) wait_counter(ctrl + lay.sel_ready + i, 1u, err);
+
+  const size_t qh = (size_t)i * H + h;
+  AttnArgs aa;
+  aa.q = a.q + qh * kQHeads * kHeadDim;
+  aa.k_pages = a.k_pages;
+  aa.v_pages = a.v_pages;
+  aa.num_pages = a.num_pages;
+  aa.H = H;
+  aa.h = h;
+  aa.bt_row = a.block_table + (size_t)b * a.bt_stride;
+  aa.sel_row = lay.sparse ? a.sel + (size_t)i * lay.k : nullptr;
+  aa.pos = pos;
+  aa.e0 = split * lay.split_tokens;
+  aa.e1 = min(aa.e0 + lay.split_tokens, list_len);
+  aa.split = split;
+  aa.n_splits = n_splits;
+  aa.scale = a.scale;
+  aa.out = a.out + qh * kQHeads * kHeadDim;
+  aa.pm = reinterpret_cast<float*>(a.ws + lay.pm) + qh * S * kQHeads;
+  aa.pl = reinterpret_cast<float*>(a.ws + lay.pl) + qh * S * kQHeads;
+  aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
+  aa.split_cnt = ctrl + lay.attn_cnt + qh;
+  aa.err = err;
+  attn_split(aa, lds.attn);
+}
+
+template <int TQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
+  __shared__ StepLds<TQ> lds;
+  __shared__ uint32_t s_item, s_flag, s_clear;
+  const int tid = threadIdx.x;
+  uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
+  uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + lay.ctrl_base);
+
+  // The header records how much of the workspace the previous call left
+  // zero.  If that does not cover this layout's zero region (first use, or
+  // a larger shape than before), the first tickets clear it and every other
+  // item waits for them.  The record only changes after every workgroup has
+  // read it, so all workgroups agree.
+  if (tid == 0) s_clear = load_coherent(ctrl + kHdrZeroed) < (uint32_t)lay.zero_units ? lay.n_clear : 0u;
+  __syncthreads();
+  const uint32_t n_clear = s_clear;
+  const uint32_t n_items = n_clear + lay.n_scan + lay.n_filter + lay.n_attn;
+
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(ctrl + kHdrTicket, 1u);
+    __syncthreads();
+    const uint32_t t = s_item;
+    __syncthreads();
+    if (t >= n_items) break;
+    if (t < n_clear) {
+      clear_item(lay, t, a.ws, ctrl);
+    } else {
+      const uint32_t u = t - n_clear;
+      if (n_clear) wait_counter(ctrl + kHdrCleared, n_clear, err);
+      if (u < lay.n_scan) {
+        scan_item<TQ>(a, lay, u, lds.scan, ctrl, err);
+      } else if (u < lay.n_scan + lay.n_filter) {
+        filter_item<TQ>(a, lay, u - lay.n_scan, lds, ctrl, err, s_flag);
+      } else {
+        attn_item<TQ>(a, lay, u - lay.n_scan - lay.n_filter, lds, ctrl, err);
+      }
+    }
+    __syncthreads();  // the next item reuses the LDS
+  }
+
+  // Every workgroup has taken its last ticket before it counts itself out,
+  // so the last one to leave can reset the control block for the next call
+  // and record this layout's zero region as clean.
+  if (tid == 0) s_flag = (atomicAdd(ctrl + kHdrExits, 1u) == gridDim.x - 1) ? 1u : 0u;
+  __syncthreads();
+  if (s_flag) {
+    for (size_t x = tid; x < lay.ctrl_words; x += kBlock) ctrl[x] = x == kHdrZeroed ? (uint32_t)lay.zero_units : 0u;
+  }
+}
+
+// Workgroups that fit on the device at once (cached per device and kernel).
+int resident_workgroups(const void* kernel, int variant) {
+  static std::mutex mu;
+  static int cache[64][4] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev][variant] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    cache[dev][variant] = cus * per_cu;
+  }
+  return cache[dev][variant];
+}
+
+}  // namespace
+
+int launch_step(const StepArgs& a, const StepLayout& lay, hipStream_t stream, const char* what) {
+  const uint32_t n_items = lay.n_clear + lay.n_scan + lay.n_filter + lay.n_attn;
+  if (n_items == 0) return MONO_OK;
+  if (lay.zero_units > 0xFFFFFFFFull || lay.ctrl_base != 256)
+    return set_error(MONO_ENOTSUP, "%s: workspace layout too large", what);
+  const bool tq4 = lay.T > 1 && (lay.mode & kModeIndex);
+  const void* kern = tq4 ? reinterpret_cast<const void*>(&step_kernel<4>) : reinterpret_cast<const void*>(&step_kernel<1>);
+  const int cap = resident_workgroups(kern, tq4 ? 1 : 0);
+  const unsigned grid = (unsigned)std::min<uint64_t>(n_items, (uint64_t)cap);
+  const int kid = lay.mode == kModeIndex ? kKIndexScan : (lay.mode == kModeAttn ? kKPaDecode : kKStep);
+  if (tq4) {
+    MONO_LAUNCH(kid, step_kernel<4>, dim3(grid), dim3(kBlock), 0, stream, a, lay);
+  } else {
+    MONO_LAUNCH(kid, step_kernel<1>, dim3(grid), dim3(kBlock), 0, stream, a, lay);
+  }
+  return check_launch(what);
+}
+
+}  // namespace mono

@@ -1,0 +1,393 @@
+// Device building blocks of index scoring and top-k selection (gfx950).
+//
+// The mxfp4_pages page ("vllm.models.minimax_m3.amd.ops.mxfp4_pages", module
+// docstring and mxfp4_page_views) names index scorers that read the
+// single-head index-key pool as [pages, 128, 64] data and [pages, 128, 4]
+// scales, without giving their rule.  The rule implemented here: the score
+// of token j for query token i is the fp32 dot product of the bf16 index-q
+// row i with the dequantised index-key row j, and the selection is the k
+// highest scores among tokens 0..pos_i (ties to the lower token index).
+//
+//   scan_chunk   -- one workgroup scores a chunk of a request's index pages
+//                   for up to 4 of its query tokens on bf16 MFMA, stores the
+//                   fp32 scores and adds them to per-query histograms of the
+//                   top 11 bits of the order-preserving score key.
+//   filter_slice  -- one workgroup per slice of a query token's scores: the
+//                    histogram gives the bin of the k-th largest score,
+//                    tokens above it are selected outright, tokens in it
+//                    become candidates.
+//   resolve_query -- once every slice is done: the remaining tokens of that
+//                    bin by two more radix passes (11 + 10 key bits); exact
+//                    ties at the threshold go to the lowest token indices.
+//
+// Scores, histograms and selections cross workgroups, so they are written
+// and read with coherent (agent-scope) operations.
+#pragma once
+
+#include "block_ops.h"
+#include "launch.h"
+
+namespace mono {
+
+constexpr int kScanChunkPages = 16;  // index pages per scan work item
+constexpr int kBatch = 4;            // pages per prefetch batch
+constexpr int kHistBins = 2048;      // top 11 bits of the score key
+constexpr int kHistShift = 21;
+
+template <int TQ>
+struct ScanLds {
+  uint32_t hist[TQ * kHistBins];
+};
+
+// ---------------------------------------------------------------------------
+// scan_chunk: pages [p_begin, p_end) of request b for query tokens t0..t0+tq-1.
+// Wave w scores rows 32w..32w+31 of every page as two 16-row MFMA tiles; lane
+// (g = lane/16, m = lane%16) loads the 16-byte chunk g (elements 32g..32g+31,
+// one e8m0 block) of row m of a tile, which is that row's B-operand slot for
+// the four k-steps.  Scores: C = Q K^T with the query tokens as M and the 16
+// rows of a tile as N, so lane (0, n) ends with row n's scores for query
+// tokens 0..3 (acc[i]).
+// ---------------------------------------------------------------------------
+struct ScanArgs {
+  const uint16_t* index_q;  // bf16 [B*T, 128]
+  const uint8_t* pages;     // [num_pages, 8704]
+  int64_t num_pages;
+  const int32_t* bt_row;    // block-table row of request b
+  float* q_scores;          // scores of query token t0, rows lcap apart
+  uint32_t* ghist;          // histogram rows of query tokens t0.., kHistBins apart
+  uint32_t* err;
+  int lcap;
+  int q0;                   // flat index b*T + t0 of the group's first query token
+  int pos0;                 // position of query token t0
+  int tq;                   // query tokens in the group (1..4)
+  int p_begin, p_end;       // pages of the chunk
+};
+
+template <int TQ>
+__device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, m = lane & 15;
+
+  // A operand: row m is query token t0 + m (zero when m >= tq); its k-slot
+  // (g, e) of k-step s holds index-q element 32g + 8s + e.
+  const bool has_q = m < a.tq;
+  bf16x8_t aq[4];
+  {
+    const u32x4_t* src =
+        reinterpret_cast<const u32x4_t*>(a.index_q + (size_t)(a.q0 + (has_q ? m : 0)) * kHeadDim + 32 * g);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4_t v = src[s];
+      if (!has_q) v = u32x4_t{0u, 0u, 0u, 0u};
+      aq[s] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  for (int x = tid; x < TQ * kHistBins; x += kBlock) lds.hist[x] = 0;
+  __syncthreads();
+
+  const int row0 = 32 * wave + m;  // tile 0 row; tile 1 is row0 + 16
+  // 32-bit lane offsets inside a page, so each load is (page base in SGPRs) +
+  // (fixed lane offset) with no per-load address arithmetic.
+  const uint32_t off_d0 = (uint32_t)(row0 * kRowBytes + 16 * g);
+  const uint32_t off_d1 = off_d0 + 16u * kRowBytes;
+  const uint32_t off_e0 = (uint32_t)(kScaleOffset + row0 * 4 + g);
+  const uint32_t off_e1 = off_e0 + 16u * 4u;
+
+  // The chunk's physical page ids, one per lane (lanes past the chunk repeat
+  // its last page); each page's id is then taken with readlane, so no load
+  // waits on a block-table lookup.
+  const int p_begin = a.p_begin, p_end = a.p_end;
+  const int n_cp = p_end - p_begin;
+  int lane_pid = a.bt_row[p_begin + min(lane, n_cp - 1)];
+  if (lane_pid < 0 || lane_pid >= a.num_pages) {
+    raise_error(a.err, kErrPageId);
+    lane_pid = 0;
+  }
+
+  // Pages are fetched in batches of kBatch, one batch ahead of the one being
+  // scored.  Loads are unconditional (past the chunk end they repeat its last
+  // page, whose rows are then all masked), so the compiler can count the
+  // outstanding loads exactly and wait only for the batch being scored.
+  struct Rows {
+    u32x4_t d[2];
+    uint32_t e[2];
+  };
+  auto load_batch = [&](Rows* r, int p0) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int cp = min(p0 + u - p_begin, n_cp - 1);
+      const uint8_t* pg = a.pages + (size_t)__builtin_amdgcn_readlane(lane_pid, cp) * kPageBytes;
+      r[u].d[0] = *reinterpret_cast<const u32x4_t*>(pg + off_d0);
+      r[u].d[1] = *reinterpret_cast<const u32x4_t*>(pg + off_d1);
+      r[u].e[0] = pg[off_e0];
+      r[u].e[1] = pg[off_e1];
+    }
+  };
+  auto score_page = [&](const Rows& r, int p) {
+    const float sc0 = e8m0_scale_operand(r.e[0]);
+    const float sc1 = e8m0_scale_operand(r.e[1]);
+    f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[0][s], sc0), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[1][s], sc1), c1, 0, 0, 0);
+    }
+    if (g == 0) {
+#pragma unroll
+      for (int tile = 0; tile < 2; ++tile) {
+        const f32x4_t c = tile ? c1 : c0;
+        const int j = p * kPageTokens + 32 * wave + 16 * tile + m;
+#pragma unroll
+        for (int i = 0; i < TQ; ++i) {
+          if (i < a.tq && j <= a.pos0 + i) {
+            store_coherent(a.q_scores + (size_t)i * a.lcap + j, c[i]);
+            atomicAdd(&lds.hist[i * kHistBins + (score_key(c[i]) >> kHistShift)], 1u);
+          }
+        }
+      }
+    }
+  };
+
+  // Two register sets used in turn (no copies between them, so a load never
+  // has to wait for the registers it overwrites to drain).
+  Rows ra[kBatch], rb[kBatch];
+  load_batch(ra, p_begin);
+  for (int p0 = p_begin; p0 < p_end; p0 += 2 * kBatch) {
+    load_batch(rb, p0 + kBatch);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) score_page(ra[u], p0 + u);
+    load_batch(ra, p0 + 2 * kBatch);
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) score_page(rb[u], p0 + kBatch + u);
+  }
+  __syncthreads();
+
+  for (int x = tid; x < a.tq * kHistBins; x += kBlock) {
+    const uint32_t v = lds.hist[x];
+    if (v) atomicAdd(&a.ghist[x], v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Selection of one query token's top k over tokens 0..n_valid-1, in two
+// steps.  filter_slice runs on every slice of kSlice scores: it finds the
+// histogram bin B1 that holds the k-th largest score, writes the tokens of
+// higher bins straight to the output and appends the tokens of bin B1 to a
+// candidate list.  resolve_query runs once all slices are done: it picks the
+// remaining tokens from the candidates with two more radix passes.
+// ---------------------------------------------------------------------------
+constexpr int kSlice = 4096;     // scores per filter work item
+constexpr int kCandCap = 8192;   // candidates kept per query token
+constexpr int kLdsCand = 3840;   // candidates the resolving workgroup stages in LDS
+
+struct FilterLds {
+  uint32_t hist[kHistBins];
+  uint32_t scratch[8];
+};
+
+struct ResolveLds {
+  uint32_t hist[kHistBins];
+  uint2 cand[kLdsCand];
+  uint32_t scratch[8];
+  uint32_t cnt;
+};
+
+struct SelectArgs {
+  const float* scores;  // the query token's scores (coherent), lcap floats
+  int lcap;             // capacity of the score row (a multiple of 128)
+  uint32_t* ghist;      // its histogram row
+  int32_t* out;         // [k] selected token positions, then -1 padding
+  float* out_scores;    // [k] or nullptr
+  uint32_t* out_cnt;    // slots taken by filter items
+  uint64_t* cand;       // [kCandCap] (key, j) candidates
+  uint32_t* cand_cnt;   // candidates appended
+  uint32_t* err;
+  int n_valid;
+  int k;
+};
+
+// Slots past k would mean inconsistent counts; they are refused and flagged.
+__device__ __forceinline__ void put_selection(const SelectArgs& a, uint32_t slot, int j, float score) {
+  if (slot >= (uint32_t)a.k) {
+    raise_error(a.err, kErrSelection);
+    return;
+  }
+  store_coherent(reinterpret_cast<uint32_t*>(a.out + slot), (uint32_t)j);
+  if (a.out_scores) store_coherent(a.out_scores + slot, score);
+}
+
+// Loads a histogram row into LDS and finds the bin of the k-th largest score.
+__device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* hist, uint32_t* scratch) {
+  const int tid = threadIdx.x;
+  uint32_t h[kHistBins / kBlock];
+#pragma unroll
+  for (int u = 0; u < kHistBins / kBlock; ++u) h[u] = load_coherent(a.ghist + u * kBlock + tid);
+#pragma unroll
+  for (int u = 0; u < kHistBins / kBlock; ++u) hist[u * kBlock + tid] = h[u];
+  __syncthreads();
+  return find_bin_of_rank(hist, kHistBins, (uint32_t)a.k, scratch);
+}
+
+// Slice [j0, j1) of the scores.
+__device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds) {
+  const int tid = threadIdx.x;
+  if (a.n_valid <= a.k) {  // at most k valid tokens: all of them, then -1 padding
+    for (int j = j0 + tid; j < j1; j += kBlock) put_selection(a, (uint32_t)j, j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
+    if (j0 == 0) {
+      for (int s = a.n_valid + tid; s < a.k; s += kBlock) {
+        store_coherent(reinterpret_cast<uint32_t*>(a.out + s), 0xffffffffu);
+        if (a.out_scores) store_coherent(a.out_scores + s, __uint_as_float(0x7fc00000u));
+      }
+    }
+    return;
+  }
+  // The slice's scores are loaded unconditionally (indices clamped inside the
+  // row's capacity, masked below) so the loads overlap the histogram's.
+  constexpr int kPer = kSlice / kBlock;
+  float v[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) v[u] = load_coherent(a.scores + min(j0 + u * kBlock + tid, a.lcap - 1));
+  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  const uint32_t B1 = (uint32_t)sp.bin;
+  const bool use_cand = sp.count <= (uint32_t)kCandCap;
+
+  uint32_t hi_mask = 0, eq_mask = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + u * kBlock + tid;
+    const uint32_t bin = score_key(v[u]) >> kHistShift;
+    hi_mask |= (j < j1 && bin > B1) ? (1u << u) : 0u;
+    eq_mask |= (j < j1 && bin == B1) ? (1u << u) : 0u;
+  }
+  if (!use_cand) eq_mask = 0;
+  // counts <= kSlice per workgroup: both fit one packed 16+16-bit scan
+  uint32_t tot;
+  const uint32_t before = block_exclusive_scan(__popc(hi_mask) | (__popc(eq_mask) << 16), lds.scratch, tot);
+  if (tid == 0) {
+    lds.scratch[kWaves] = (tot & 0xFFFFu) ? atomicAdd(a.out_cnt, tot & 0xFFFFu) : 0u;
+    lds.scratch[kWaves + 1] = (tot >> 16) ? atomicAdd(a.cand_cnt, tot >> 16) : 0u;
+  }
+  __syncthreads();
+  uint32_t slot = lds.scratch[kWaves] + (before & 0xFFFFu);
+  uint32_t cs = lds.scratch[kWaves + 1] + (before >> 16);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = j0 + u * kBlock + tid;
+    if (hi_mask & (1u << u)) put_selection(a, slot++, j, v[u]);
+    if (eq_mask & (1u << u)) {
+      if (cs < (uint32_t)kCandCap) store_coherent(a.cand + cs, ((uint64_t)(uint32_t)j << 32) | score_key(v[u]));
+      ++cs;
+    }
+  }
+}
+
+// The remaining tokens of bin B1, once every slice is done.  Leaves the
+// histogram row zero.
+__device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& lds) {
+  const int tid = threadIdx.x;
+  const int n_valid = a.n_valid;
+  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
+  if (n_valid <= a.k) return;  // the filter items wrote everything
+  const uint32_t B1 = (uint32_t)sp.bin;
+  const uint32_t above = sp.above;
+  const uint32_t in_bin = sp.count;
+  const bool use_cand = in_bin <= (uint32_t)kCandCap;
+  const bool in_lds = in_bin <= (uint32_t)kLdsCand;
+  if (in_lds) {
+    constexpr int kPer = kLdsCand / kBlock;
+    uint64_t c[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lds.cand[u * kBlock + tid] = make_uint2((uint32_t)c[u], (uint32_t)(c[u] >> 32));
+  }
+  if (tid == 0) lds.cnt = above;
+  __syncthreads();
+
+  // Candidate source: the LDS copy, the global list, or (if it overflowed)
+  // every valid score filtered by bin; all yield the same multiset of (key, j).
+  const uint32_t R = (uint32_t)a.k - above;  // 1 <= R <= in_bin
+  const int n_src = use_cand ? (int)in_bin : n_valid;
+  auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
+    if (in_lds) {
+      const uint2 c = lds.cand[e];
+      key = c.x;
+      j = (int)c.y;
+      return true;
+    }
+    if (use_cand) {
+      const uint64_t c = load_coherent(a.cand + e);
+      key = (uint32_t)c;
+      j = (int)(c >> 32);
+      return true;
+    }
+    j = e;
+    key = score_key(load_coherent(a.scores + e));
+    return (key >> kHistShift) == B1;
+  };
+  auto emit = [&](int j) {
+    put_selection(a, atomicAdd(&lds.cnt, 1u), j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
+  };
+
+  // pass 2: key bits 20..10
+  for (int x = tid; x < kHistBins; x += kBlock) lds.hist[x] = 0u;
+  __syncthreads();
+  for (int e = tid; e < n_src; e += kBlock) {
+    uint32_t key;
+    int j;
+    if (fetch(e, key, j)) atomicAdd(&lds.hist[(key >> 10) & 0x7FFu], 1u);
+  }
+  __syncthreads();
+  const BinSplit s2 = find_bin_of_rank(lds.hist, kHistBins, R, lds.scratch);
+  for (int e = tid; e < n_src; e += kBlock) {
+    uint32_t key;
+    int j;
+    if (fetch(e, key, j) && ((key >> 10) & 0x7FFu) > (uint32_t)s2.bin) emit(j);
+  }
+  const uint32_t R2 = R - s2.above;
+  const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;  // key >> 10 of the survivors
+
+  // pass 3: key bits 9..0
+  __syncthreads();
+  for (int x = tid; x < 1024; x += kBlock) lds.hist[x] = 0u;
+  __syncthreads();
+  for (int e = tid; e < n_src; e += kBlock) {
+    uint32_t key;
+    int j;
+    if (fetch(e, key, j) && (key >> 10) == pre2) atomicAdd(&lds.hist[key & 0x3FFu], 1u);
+  }
+  __syncthreads();
+  const BinSplit s3 = find_bin_of_rank(lds.hist, 1024, R2, lds.scratch);
+  const uint32_t kstar = (pre2 << 10) | (uint32_t)s3.bin;
+  for (int e = tid; e < n_src; e += kBlock) {
+    uint32_t key;
+    int j;
+    if (fetch(e, key, j) && (key >> 10) == pre2 && (key & 0x3FFu) > (uint32_t)s3.bin) emit(j);
+  }
+  const uint32_t R3 = R2 - s3.above;  // tokens to take among those with key == kstar
+
+  if (s3.count == R3) {
+    for (int e = tid; e < n_src; e += kBlock) {
+      uint32_t key;
+      int j;
+      if (fetch(e, key, j) && key == kstar) emit(j);
+    }
+  } else {
+    // More exact ties than places: take the lowest token indices, scanning
+    // the scores in index order.
+    __syncthreads();
+    uint32_t taken = 0;
+    for (int jb = 0; jb < n_valid && taken < R3; jb += kBlock) {
+      const int j = jb + tid;
+      const bool f = j < n_valid && score_key(load_coherent(a.scores + j)) == kstar;
+      uint32_t tot;
+      const uint32_t before = block_exclusive_scan(f ? 1u : 0u, lds.scratch, tot);
+      if (f && taken + before < R3) emit(j);
+      taken += tot;
+    }
+  }
+}
+
+}  // namespace mono

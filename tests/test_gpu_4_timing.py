@@ -20,8 +20,10 @@ def test_kernel_timer_sees_every_kernel_of_a_step():
             sel = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], w.k, T=w.T)
             spd.mono_pa_decode_mxfp4(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], sel, w.scale,
                                      T=w.T)
+        spd.mono_sparse_decode_mxfp4(d["index_q"], d["index_pool"], d["q"], d["k_pool"], d["v_pool"],
+                                     d["block_table"], d["seq_lens"], w.k, w.scale, T=w.T)
         torch.cuda.synchronize()
-    assert kt.launches == {"index_scan_kernel": 3, "topk_filter_kernel": 3, "pa_decode_kernel": 3}
+    assert kt.launches == {"index_topk_kernel": 3, "pa_decode_kernel": 3, "sparse_decode_kernel": 1}
     assert all(0 < us < 1e5 for us in kt.mean_us.values())
     # timing off again: launches are not recorded and nothing fails
     sel = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], w.k, T=w.T)

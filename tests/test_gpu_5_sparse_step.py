@@ -1,0 +1,175 @@
+"""GPU parity of the one-launch sparse decode step (index top-k, then
+attention over the selection) against the oracle.
+
+The selection is checked as the index call's is (the oracle's top-k up to
+exact-tie order, within a 1e-6 relative band of the k-th score); the output
+is checked against the oracle's attention over the selection the call
+returned, to the attention tolerance (relative L2 <= 5e-3, max |err| <=
+1e-2 max|V|).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import bf16_bits, check_topk_row, to_device
+from oracle import decode, mxfp4
+from workloads import make_workload, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def spd():
+    import sparse_paged_decode_amd as spd
+
+    spd.load_library()
+    assert torch.cuda.is_available()
+    return spd
+
+
+def _step(spd, w, d, ws):
+    out, sel = spd.mono_sparse_decode_mxfp4(d["index_q"], d["index_pool"], d["q"], d["k_pool"], d["v_pool"],
+                                            d["block_table"], d["seq_lens"], w.k, w.scale, T=w.T, workspace=ws)
+    torch.cuda.synchronize()
+    return out, sel
+
+
+def _check_token(w, i, sel_row, out_bits):
+    b = i // w.T
+    pos = int(w.seq_lens[b]) - w.T + i % w.T
+    check_topk_row(sel_row, w, i, w.k)
+    ref = decode.decode_one(w.q[i], w.k_pool, w.v_pool, w.block_table[b], pos, w.scale, sel_row)
+    vmax = float(np.abs(decode.sequence_rows(w.v_pool, w.block_table[b], pos + 1, 0)).max())
+    o = mxfp4.bf16_bits_to_f64(out_bits[i])
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(o - ref) / nref if nref > 0 else np.linalg.norm(o)
+    assert rel <= 5e-3 and np.max(np.abs(o - ref)) <= 1e-2 * vmax, (i, rel)
+
+
+SMALL = [
+    # name, B, T, seq_lens, bt_width, k, exps
+    ("one_page", 1, 1, [100], 1, 10, (124, 127)),
+    ("k_ge_valid", 2, 1, [50, 129], 2, 200, (122, 132)),
+    ("k_one", 3, 1, [1, 128, 700], 6, 1, (124, 127)),
+    ("ragged_multi_token", 4, 4, [4, 300, 1000, 2049], 17, 37, (124, 127)),
+    ("several_chunks", 2, 1, [5000, 4097], 40, 700, (122, 132)),
+    ("several_slices", 2, 1, [9000, 12289], 97, 300, (124, 126)),
+    ("t3_group", 2, 3, [640, 3001], 24, 250, (124, 127)),
+    ("t6_two_groups", 2, 6, [900, 2300], 18, 128, (122, 132)),
+]
+
+
+@pytest.mark.parametrize("name,B,T,lens,W,k,exps", SMALL, ids=[c[0] for c in SMALL])
+def test_step_small(spd, name, B, T, lens, W, k, exps):
+    w = make_workload(name, B=B, T=T, seq_lens=lens, bt_width=W, k=k, seed=sum(map(ord, name)) + 7,
+                      exp_range=exps)
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(w.N):
+        _check_token(w, i, sel_np[i], out_bits)
+    # The same selection as the index call (as sets), and the workspace
+    # serves the next call: the queue and every counter were reset.
+    sel2 = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], w.k, T=w.T)
+    np.testing.assert_array_equal(np.sort(sel2.cpu().numpy(), axis=1), np.sort(sel_np, axis=1))
+    out3, sel3 = _step(spd, w, d, ws)
+    np.testing.assert_array_equal(np.sort(sel3.cpu().numpy(), axis=1), np.sort(sel_np, axis=1))
+    a = mxfp4.bf16_bits_to_f64(bf16_bits(out3))
+    b = mxfp4.bf16_bits_to_f64(out_bits)
+    assert np.max(np.abs(a - b)) <= 1e-2 * max(np.max(np.abs(b)), 1e-30)
+
+
+def test_step_equals_two_calls(spd):
+    """Fused output matches the index call followed by the attention call."""
+    w = make_workload("two", B=3, T=2, seq_lens=[3000, 5000, 4100], bt_width=40, k=512, seed=8,
+                      exp_range=(124, 126))
+    d = to_device(w)
+    out, sel = _step(spd, w, d, spd.Workspace("cuda"))
+    sel2 = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], w.k, T=w.T)
+    out2 = spd.mono_pa_decode_mxfp4(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], sel2,
+                                    w.scale, T=w.T)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(np.sort(sel2.cpu().numpy(), axis=1), np.sort(sel.cpu().numpy(), axis=1))
+    a = mxfp4.bf16_bits_to_f64(bf16_bits(out))
+    b = mxfp4.bf16_bits_to_f64(bf16_bits(out2))
+    # same tokens in another order: equal up to fp32 summation order
+    assert np.max(np.abs(a - b)) <= 1e-2 * np.max(np.abs(b))
+
+
+def test_step_bad_page_id_is_flagged(spd):
+    w = make_workload("badstep", B=2, T=1, seq_lens=[300, 300], bt_width=3, k=16, seed=9)
+    d = to_device(w)
+    d["block_table"][1, 1] = 10**6
+    ws = spd.Workspace("cuda")
+    _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) & spd.DEVERR_PAGE_ID
+
+
+def test_step_bad_seq_len_is_flagged_and_others_complete(spd):
+    """A request whose length exceeds its block-table row is skipped and
+    flagged; the other requests are still decoded."""
+    w = make_workload("badlen", B=2, T=1, seq_lens=[300, 200], bt_width=3, k=64, seed=10, exp_range=(124, 127))
+    d = to_device(w)
+    d["seq_lens"][1] = 3 * 128 + 1
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) & spd.DEVERR_SEQ_LEN
+    _check_token(w, 0, sel.cpu().numpy()[0], bf16_bits(out))
+    # the workspace is usable again after the flagged call
+    d["seq_lens"][1] = 200
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(2):
+        _check_token(w, i, sel_np[i], out_bits)
+
+
+@pytest.mark.parametrize("number,samples", [(3, [0, 31, 63]), (4, [0, 3, 101, 511]), (5, [0, 7])])
+def test_step_full_size_sampled(spd, number, samples):
+    """Full-size workloads in the configuration the benchmark times."""
+    w = workload(number)
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in samples:
+        _check_token(w, i, sel_np[i], out_bits)
+    pos = decode.query_positions(w.seq_lens, w.T)
+    for i in range(w.N):
+        n = min(w.k, pos[i] + 1)
+        row = sel_np[i]
+        assert np.all(row[n:] == -1) and np.all((row[:n] >= 0) & (row[:n] <= pos[i]))
+        assert np.unique(row[:n]).size == n
+    assert torch.isfinite(out.float()).all()
+
+
+def test_one_workspace_across_shapes_and_entry_points(spd):
+    """One buffer for every call, shapes growing and shrinking: each call
+    clears what the previous ones left in its zero region."""
+    ws = spd.Workspace("cuda", 64 << 20)
+    shapes = [
+        dict(B=1, T=1, seq_lens=[700], bt_width=6, k=64),
+        dict(B=3, T=4, seq_lens=[300, 5000, 2100], bt_width=40, k=256),
+        dict(B=2, T=1, seq_lens=[9000, 129], bt_width=71, k=100),
+        dict(B=1, T=2, seq_lens=[400], bt_width=4, k=32),
+    ]
+    for n, kw in enumerate(shapes):
+        w = make_workload(f"ws{n}", seed=100 + n, exp_range=(124, 127), **kw)
+        d = to_device(w)
+        sel_i = spd.mono_index_score_topk(d["index_q"], d["index_pool"], d["block_table"], d["seq_lens"], w.k, T=w.T,
+                                          workspace=ws)
+        out_d = spd.mono_pa_decode_mxfp4(d["q"], d["k_pool"], d["v_pool"], d["block_table"], d["seq_lens"], None,
+                                         w.scale, T=w.T, workspace=ws)
+        out, sel = _step(spd, w, d, ws)
+        assert spd.check_device_errors(ws) == 0
+        sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+        np.testing.assert_array_equal(np.sort(sel_i.cpu().numpy(), axis=1), np.sort(sel_np, axis=1))
+        for i in range(w.N):
+            _check_token(w, i, sel_np[i], out_bits)
+        ref = decode.pa_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.T, w.scale, None)
+        o = mxfp4.bf16_bits_to_f64(bf16_bits(out_d))
+        assert np.linalg.norm(o - ref) <= 5e-3 * np.linalg.norm(ref), f"dense attention, shape {n}"
