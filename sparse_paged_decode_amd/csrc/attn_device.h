@@ -8,20 +8,23 @@
 // head over the candidate tokens (a selection list, or every token
 // 0..pos), softmax, and the probability-weighted sum of the V rows.
 //
-// A split covers candidates [e0, e1); each wave takes groups of 32.  Per group:
-//   * QK^T on bf16 MFMA 16x16x32 with the *tokens* as the M dimension (two
-//     16-token tiles) and the 16 query heads as N, so each lane ends with the
-//     logits of one head for 8 tokens -- exactly the B-operand layout the PV
-//     product needs for the probabilities;
+// A split covers candidates [e0, e1); each wave takes groups of 16.  Per
+// group, with lane (g = lane/16, m = lane%16):
+//   * QK^T on bf16 MFMA 16x16x32 with the 16 *tokens* as M (lane (g, m)
+//     loads the 16-byte chunk g of token m's K row, one e8m0 block) and the
+//     16 query heads as N, so lane (g, n) ends with the logits of head n for
+//     tokens 4g..4g+3 -- exactly the A-operand slots of a 16x16x16 MFMA;
 //   * online softmax in the log2 domain (running max and sum per head);
-//   * PV as O^T = V^T P^T on the same MFMA: V is dequantised to bf16 and
-//     written transposed into LDS (dims x token pairs), then read back 8
-//     tokens per lane with one 16-byte LDS load per 16-dim tile.
-// Dequantised K/V are exact in bf16, so the only roundings are fp32
-// accumulation, exp2, and the bf16 rounding of the probabilities (the row
-// sums use the same rounded values).  Split partials (max, sum, 16x128
-// accumulator) are handed over with coherent stores; the last split to
-// arrive merges them and writes the bf16 output.
+//   * P V on bf16 MFMA 16x16x16 with heads as M and dims as N: the B operand
+//     of lane (g, m) in tile x is dim 8m + x of tokens 4g..4g+3, so each lane
+//     reads 4 bytes (dims 8m..8m+7) of four tokens' V rows straight from the
+//     pool and no transpose through LDS is needed.
+// The block-table row is staged in LDS before any wait, so token lookups
+// cost one LDS read.  Dequantised K/V are exact in bf16, so the only
+// roundings are fp32 accumulation, exp2, and the bf16 rounding of the
+// probabilities (the row sums use the same rounded values).  Split partials
+// (max, sum, 16x128 accumulator) are handed over with coherent stores; the
+// last split to arrive merges them and writes the bf16 output.
 #pragma once
 
 #include "block_ops.h"
@@ -29,16 +32,20 @@
 
 namespace mono {
 
-constexpr int kGroupTokens = 32;
-constexpr int kVtRowBytes = 64;        // 16 token pairs x 4 B
-constexpr int kVtRegionBytes = 8384;   // 128 rows + 3 x 64 B group pad, per wave
-// After the token loop the same memory holds the four waves' partial
-// accumulators (32 KiB) and their running maxima and sums.
+constexpr int kGroupTokens = 16;
+constexpr int kPassGroups = 4;  // groups of one wave whose entries are fetched together
+constexpr int kBtCache = 4096;  // block-table entries staged in LDS (longer rows read global memory)
+constexpr int kMergeBatch = 8;  // splits whose partials the merge requests at once
+// After the token loop the LDS holds the four waves' partial accumulators
+// (32 KiB, [wave][head][dim]) and their running maxima and sums.
 constexpr int kSoBytes = kWaves * kQHeads * kHeadDim * 4;
-static_assert(kSoBytes + 2 * kWaves * kQHeads * 4 + 4 <= kWaves * kVtRegionBytes, "attention LDS overlap");
+constexpr int kCombineBytes = kSoBytes + 2 * kWaves * kQHeads * 4 + 16;
 
 struct AttnLds {
-  __attribute__((aligned(16))) uint8_t vt[kWaves * kVtRegionBytes];
+  union {
+    int32_t bt[kBtCache];
+    __attribute__((aligned(16))) uint8_t combine[kCombineBytes];
+  };
 };
 
 struct AttnArgs {
@@ -61,14 +68,7 @@ struct AttnArgs {
   uint32_t* err;
 };
 
-// V^T element (dim, token pair) in a wave's region.  Rows are 64 B; the
-// 16-byte chunk of a pair is XOR-swizzled by bits 2..3 of the row so the
-// 16-row x 16-byte reads of one MFMA tile hit 64 distinct banks, and each
-// group of 32 rows is shifted by 64 B so the four lane groups writing rows
-// 32 apart do too.
-__device__ __forceinline__ int vt_offset(int dim, int pair) {
-  return dim * kVtRowBytes + (dim >> 5) * 64 + ((((pair >> 2) ^ (dim >> 2)) & 3) << 4) + (pair & 3) * 4;
-}
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float* o, float inv) {
   u32x4_t w;
@@ -77,13 +77,35 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float* o, floa
   *reinterpret_cast<u32x4_t*>(dst) = w;
 }
 
+// The K and V data of one group as one lane needs them.
+struct AttnGroup {
+  u32x4_t kd;      // K chunk g of token m
+  uint32_t ke;     // its e8m0 scale
+  uint32_t vd[4];  // V bytes 4m..4m+3 of tokens 4g..4g+3
+  uint32_t ve[4];  // their e8m0 scales (block m/4)
+  uint32_t valid;  // token m is a candidate
+};
+
 __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
   const int e0 = a.e0, e1 = a.e1, pos = a.pos, H = a.H, h = a.h, split = a.split, n_splits = a.n_splits;
   const int n_groups = (e1 - e0 + kGroupTokens - 1) / kGroupTokens;
-  const int iters = (n_groups + kWaves - 1) / kWaves;
 
+  // The first pass's selection entries are requested first; the block-table
+  // row (into LDS) and the q operand (into registers) load meanwhile.
+  auto entry_of = [&](int grp) -> int {
+    const int entry = e0 + kGroupTokens * grp + m;
+    if (grp >= n_groups || entry >= e1) return -1;
+    return a.sel_row ? (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + entry)) : entry;
+  };
+  int jv[kPassGroups];
+#pragma unroll
+  for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(wave + kWaves * x);
+  const int bt_len = (pos >> 7) + 1;
+  const bool bt_lds = bt_len <= kBtCache;
+  if (bt_lds)
+    for (int x = tid; x < bt_len; x += kBlock) lds.bt[x] = a.bt_row[x];
   // B operand of QK^T: column n = m is query head m; k-slot (g, e) of k-step
   // s holds q element 32g + 8s + e.
   bf16x8_t qb[4];
@@ -92,152 +114,149 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, src[s]);
   }
+  __syncthreads();
+
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
   float m_run = -INFINITY, l_run = 0.f;
   f32x4_t acc[8];
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  uint8_t* vt = lds.vt + wave * kVtRegionBytes;
 
-  // Groups are processed two at a time; the token lookups, block-table
-  // lookups and K/V loads of both are issued before either is computed, so
-  // each stage costs one memory round trip for the pair.
-  struct Tok {
-    u32x4_t kd, vd;
-    uint32_t ke, ve;
-    bool valid;
-  };
-  for (int it0 = 0; it0 < iters; it0 += 2) {
-    Tok tk[2][2];
-    int jj[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        // lane (g, m) handles tokens 2m and 2m+1 of each 32-token group
-        const int entry = e0 + kGroupTokens * (wave + kWaves * (it0 + x)) + 2 * m + u;
-        int j = -1;
-        if (it0 + x < iters && entry < e1) j = a.sel_row ? (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + entry)) : entry;
-        jj[x][u] = (j >= 0 && j <= pos) ? j : -1;
-      }
-    int pid[2][2];
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) pid[x][u] = jj[x][u] >= 0 ? a.bt_row[jj[x][u] >> 7] : -1;
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        Tok& t = tk[x][u];
-        t.kd = t.vd = u32x4_t{0u, 0u, 0u, 0u};
-        t.ke = t.ve = 127u;
-        t.valid = false;
-        const int j = jj[x][u];
-        if (j >= 0) {
-          if (pid[x][u] < 0 || pid[x][u] >= a.num_pages) {
-            raise_error(a.err, kErrPageId);
-          } else {
-            const size_t off = ((size_t)pid[x][u] * H + h) * kPageBytes;
-            const int r = j & (kPageTokens - 1);
-            t.kd = *reinterpret_cast<const u32x4_t*>(a.k_pages + off + r * kRowBytes + 16 * g);
-            t.vd = *reinterpret_cast<const u32x4_t*>(a.v_pages + off + r * kRowBytes + 16 * g);
-            t.ke = a.k_pages[off + kScaleOffset + r * 4 + g];
-            t.ve = a.v_pages[off + kScaleOffset + r * 4 + g];
-            t.valid = true;
-          }
-        }
-      }
-#pragma unroll
-  for (int xi = 0; xi < 2; ++xi) {
-    if (it0 + xi >= iters) break;  // uniform across the workgroup
-    u32x4_t kd[2] = {tk[xi][0].kd, tk[xi][1].kd}, vd[2] = {tk[xi][0].vd, tk[xi][1].vd};
-    uint32_t ke[2] = {tk[xi][0].ke, tk[xi][1].ke}, ve[2] = {tk[xi][0].ve, tk[xi][1].ve};
-    bool valid[2] = {tk[xi][0].valid, tk[xi][1].valid};
+  const size_t kv_stride = (size_t)H * kPageBytes;
+  const uint8_t* kbase = a.k_pages + (size_t)h * kPageBytes;
+  const uint8_t* vbase = a.v_pages + (size_t)h * kPageBytes;
 
-    // S^T tiles: lane (g, n) gets tokens 8g + 2i + u (i = 0..3) of head n.
-    f32x4_t c[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const float sc = e8m0_scale_operand(ke[u]);
-      c[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        c[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8_bf16(kd[u][s], sc), qb[s], c[u], 0, 0, 0);
+  // Token j of lane (g, m) -> its pool row, packed as page << 7 | row, or
+  // ~0u when it is not a candidate.
+  auto token_ref = [&](int j) -> uint32_t {
+    if (j < 0 || j > pos) return ~0u;
+    const int pid = bt_lds ? lds.bt[j >> 7] : a.bt_row[j >> 7];
+    if (pid < 0 || pid >= a.num_pages) {
+      raise_error(a.err, kErrPageId);
+      return ~0u;
     }
-    // Validity of token 2r + u sits in bit r of these ballots (lanes 0..15).
-    const uint32_t vm0 = (uint32_t)__ballot(valid[0]);
-    const uint32_t vm1 = (uint32_t)__ballot(valid[1]);
-    float z[2][4];
+    return ((uint32_t)pid << 7) | (uint32_t)(j & (kPageTokens - 1));
+  };
+  // Loads are unconditional (a non-candidate reads page 0, row 0, and is
+  // zeroed afterwards) so the compiler can count outstanding loads exactly.
+  auto load_group = [&](uint32_t ref) -> AttnGroup {
+    AttnGroup t;
+    t.valid = ref != ~0u;
+    const uint32_t r0 = t.valid ? ref : 0u;
+    {
+      const uint8_t* row = kbase + (size_t)(r0 >> 7) * kv_stride;
+      const uint32_t rr = r0 & 127u;
+      t.kd = *reinterpret_cast<const u32x4_t*>(row + rr * kRowBytes + 16 * g);
+      t.ke = row[kScaleOffset + rr * 4 + g];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ri = __shfl(ref, 4 * g + i);
+      const uint32_t r1 = ri != ~0u ? ri : 0u;
+      const uint8_t* row = vbase + (size_t)(r1 >> 7) * kv_stride;
+      const uint32_t rr = r1 & 127u;
+      t.vd[i] = *reinterpret_cast<const uint32_t*>(row + rr * kRowBytes + 4 * m);
+      t.ve[i] = row[kScaleOffset + rr * 4 + (m >> 2)];
+      if (ri == ~0u) {
+        t.vd[i] = 0u;
+        t.ve[i] = 127u;
+      }
+    }
+    if (!t.valid) {
+      t.kd = u32x4_t{0u, 0u, 0u, 0u};
+      t.ke = 127u;
+    }
+    return t;
+  };
+  // S^T tile of a group: lane (g, n) gets tokens 4g + i (i = 0..3) of head n.
+  auto qk_group = [&](const AttnGroup& t) -> f32x4_t {
+    const float sc = e8m0_scale_operand(t.ke);
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8_bf16(t.kd[s], sc), qb[s], c, 0, 0, 0);
+    // Validity of token r sits in bit r of this ballot (lanes 0..15).
+    const uint32_t vm = (uint32_t)__ballot(t.valid);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = ((vm >> (4 * g + i)) & 1u) ? c[i] * sl2 : -INFINITY;
+    return c;
+  };
+  // acc += P V of a group; pa is the A operand (row n = head n, k-slot (g, i)
+  // = token 4g + i).
+  auto pv_group = [&](const AttnGroup& t, s16x4_t pa) {
+    // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1).
+    u32x4_t vv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vv[i] = __builtin_bit_cast(u32x4_t, dequant8_bf16(t.vd[i], e8m0_scale_operand(t.ve[i])));
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int p = x >> 1;
+      // tokens (0, 1) and (2, 3) of dim 8m + x: low or high halves of the pairs
+      const uint32_t sel = (x & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t b01 = __builtin_amdgcn_perm(vv[1][p], vv[0][p], sel);
+      const uint32_t b23 = __builtin_amdgcn_perm(vv[3][p], vv[2][p], sel);
+      const s16x4_t vb = __builtin_bit_cast(s16x4_t, (uint64_t)b01 | ((uint64_t)b23 << 32));
+      acc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[x], 0, 0, 0);
+    }
+  };
+
+  // A pass covers kPassGroups groups of this wave: page lookups, the K/V
+  // loads of all of them at once, QK^T of all, one online-softmax update,
+  // then P V of all.
+  for (int gb = wave; gb < n_groups; gb += kWaves * kPassGroups) {
+    if (gb != wave) {
+#pragma unroll
+      for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(gb + kWaves * x);
+    }
+    AttnGroup grp[kPassGroups];
+#pragma unroll
+    for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(jv[x]));
+    f32x4_t z[kPassGroups];
     float mx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t vm = u ? vm1 : vm0;
+    for (int x = 0; x < kPassGroups; ++x) {
+      z[x] = qk_group(grp[x]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool v = (vm >> (4 * g + r)) & 1u;
-        z[u][r] = v ? c[u][r] * sl2 : -INFINITY;
-        mx = fmaxf(mx, z[u][r]);
-      }
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[x][i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    u32x4_t pw;
+    m_run = m_new;
+    // The accumulator rows are heads 4g..4g+3: their rescale factors sit in
+    // lanes 4g..4g+3.
+    f32x4_t al;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) acc[x] *= al;
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      pw[r] = bf16x2_bits(__builtin_amdgcn_exp2f(z[0][r] - m_use), __builtin_amdgcn_exp2f(z[1][r] - m_use));
-      psum += bf16_lo_to_f32(pw[r]) + bf16_hi_to_f32(pw[r]);
+    for (int x = 0; x < kPassGroups; ++x) {
+      const uint32_t p01 = bf16x2_bits(__builtin_amdgcn_exp2f(z[x][0] - m_use), __builtin_amdgcn_exp2f(z[x][1] - m_use));
+      const uint32_t p23 = bf16x2_bits(__builtin_amdgcn_exp2f(z[x][2] - m_use), __builtin_amdgcn_exp2f(z[x][3] - m_use));
+      psum += (bf16_lo_to_f32(p01) + bf16_hi_to_f32(p01)) + (bf16_lo_to_f32(p23) + bf16_hi_to_f32(p23));
+      pv_group(grp[x], __builtin_bit_cast(s16x4_t, (uint64_t)p01 | ((uint64_t)p23 << 32)));
     }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] *= alpha;
-    // k-slot (g, e) of P^T is token 8g + e, e = 2r + u.
-    const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, pw);
-
-    // V^T into LDS: row = dim, column = token pair m (tokens 2m, 2m+1).
-    {
-      const float sv0 = e8m0_scale_operand(ve[0]);
-      const float sv1 = e8m0_scale_operand(ve[1]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const u32x4_t w0 = __builtin_bit_cast(u32x4_t, dequant8_bf16(vd[0][s], sv0));
-        const u32x4_t w1 = __builtin_bit_cast(u32x4_t, dequant8_bf16(vd[1][s], sv1));
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d = 32 * g + 8 * s + 2 * q;
-          *reinterpret_cast<uint32_t*>(vt + vt_offset(d, m)) = (w0[q] & 0xffffu) | (w1[q] << 16);
-          *reinterpret_cast<uint32_t*>(vt + vt_offset(d + 1, m)) = (w0[q] >> 16) | (w1[q] & 0xffff0000u);
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      // A operand: row m is dim 16x + m, k-slot (g, e) is token 8g + e.
-      const bf16x8_t va =
-          __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(vt + vt_offset(16 * x + m, 4 * g)));
-      acc[x] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, acc[x], 0, 0, 0);
-    }
-    __syncthreads();
-  }
   }
 
   // ---- combine the four waves -------------------------------------------
+  __syncthreads();  // the block-table copy is no longer read
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  float* so = reinterpret_cast<float*>(lds.vt);  // [wave][dim][head], 8 KiB per wave
-  float(*s_m)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.vt + kSoBytes);
-  float(*s_l)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.vt + kSoBytes + kWaves * kQHeads * 4);
-  uint32_t* s_last = reinterpret_cast<uint32_t*>(lds.vt + kSoBytes + 2 * kWaves * kQHeads * 4);
+  float* so = reinterpret_cast<float*>(lds.combine);  // [wave][head][dim]
+  float(*s_m)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes);
+  float(*s_l)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes + kWaves * kQHeads * 4);
+  uint32_t* s_last = reinterpret_cast<uint32_t*>(lds.combine + kSoBytes + 2 * kWaves * kQHeads * 4);
+  // acc[x][i] is head 4g + i, dim 8m + x.
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) so[wave * 2048 + (16 * x + 4 * g + r) * kQHeads + m] = acc[x][r];
+  for (int i = 0; i < 4; ++i) {
+    float* dst = so + wave * 2048 + (4 * g + i) * kHeadDim + 8 * m;
+    *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
+    *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
+  }
   if (g == 0) {
     s_m[wave][m] = m_run;
     s_l[wave][m] = l_run;
@@ -256,8 +275,9 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   for (int w = 0; w < kWaves; ++w) {
     const float f = __builtin_amdgcn_exp2f(s_m[w][hd] - Mu);
     lsum += s_l[w][hd] * f;
+    const float* src = so + w * 2048 + hd * kHeadDim + d0;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) o[x] += so[w * 2048 + (d0 + x) * kQHeads + hd] * f;
+    for (int x = 0; x < 8; ++x) o[x] += src[x] * f;
   }
 
   uint16_t* orow = a.out + (size_t)hd * kHeadDim + d0;
@@ -289,40 +309,47 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   if (!*s_last) return;
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
-  // (partials are read with coherent loads)
-  // Splits are read four at a time so their loads overlap.
-  const size_t s0 = 0;
+  // All partials are requested at once (up to kMergeBatch splits a round
+  // trip).  The maxima and sums of two splits share cache lines, so they
+  // are read coherently; each accumulator slot is written by one split only
+  // and read by this workgroup only, so plain 16-byte loads are current.
   M = -INFINITY;
-  for (int s = 0; s < n_splits; s += 4) {
-    float mv[4];
-#pragma unroll
-    for (int y = 0; y < 4; ++y) mv[y] = (s + y < n_splits) ? load_coherent(pm + (s0 + s + y) * kQHeads + hd) : -INFINITY;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) M = fmaxf(M, mv[y]);
-  }
-  Mu = (M == -INFINITY) ? 0.f : M;
   lsum = 0.f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) o[x] = 0.f;
-  for (int s = 0; s < n_splits; s += 4) {
-    float mv[4], lv[4], av[4][8];
+  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    f32x4_t av[kMergeBatch][2];
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const bool in = s + y < n_splits;
-      const size_t sl = s0 + s + (in ? y : 0);
-      mv[y] = in ? load_coherent(pm + sl * kQHeads + hd) : -INFINITY;
-      lv[y] = in ? load_coherent(pl + sl * kQHeads + hd) : 0.f;
-      const float* src = pacc + (sl * kQHeads + hd) * kHeadDim + d0;
-#pragma unroll
-      for (int x = 0; x < 8; ++x) av[y][x] = in ? load_coherent(src + x) : 0.f;
+    for (int y = 0; y < kMergeBatch; ++y) {
+      const bool in = s0 + y < n_splits;
+      const size_t sl = (size_t)(in ? s0 + y : s0);
+      mv[y] = load_coherent(pm + sl * kQHeads + hd);
+      lv[y] = load_coherent(pl + sl * kQHeads + hd);
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + (sl * kQHeads + hd) * kHeadDim + d0);
+      av[y][0] = src[0];
+      av[y][1] = src[1];
+      if (!in) mv[y] = -INFINITY;
     }
+    float Mb = M;
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const float f = __builtin_amdgcn_exp2f(mv[y] - Mu);
+    for (int y = 0; y < kMergeBatch; ++y) Mb = fmaxf(Mb, mv[y]);
+    const float Mu_b = (Mb == -INFINITY) ? 0.f : Mb;
+    const float fo = __builtin_amdgcn_exp2f(M - Mu_b);  // rescale what was merged so far
+    lsum *= fo;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) o[x] *= fo;
+#pragma unroll
+    for (int y = 0; y < kMergeBatch; ++y) {
+      const float f = __builtin_amdgcn_exp2f(mv[y] - Mu_b);
       lsum += lv[y] * f;
 #pragma unroll
-      for (int x = 0; x < 8; ++x) o[x] += av[y][x] * f;
+      for (int x = 0; x < 4; ++x) {
+        o[x] += av[y][0][x] * f;
+        o[4 + x] += av[y][1][x] * f;
+      }
     }
+    M = Mb;
   }
   store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
 }

@@ -28,7 +28,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
 // Must be reached by every thread of the workgroup.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* scratch,
                                                          uint32_t& total) {
-  const int wave = threadIdx.x >> 6;
+  const int wave = thread_index() >> 6;
   const uint32_t incl = wave_inclusive_scan(v);
   if (lane_id() == 63) scratch[wave] = incl;
   __syncthreads();
@@ -69,14 +69,14 @@ struct BinSplit {
 // `scratch` is __shared__ uint32_t[kWaves + 3].
 __device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int nbins, uint32_t R,
                                                      uint32_t* scratch) {
-  if (threadIdx.x == 0) {  // defined result even if R exceeded the count
+  if (thread_index() == 0) {  // defined result even if R exceeded the count
     scratch[kWaves] = 0u;
     scratch[kWaves + 1] = 0u;
     scratch[kWaves + 2] = 0u;
   }
   const int per = nbins / kBlock;
   // thread t owns the t-th group of `per` bins counted from the top
-  const int hi = nbins - 1 - threadIdx.x * per;
+  const int hi = nbins - 1 - thread_index() * per;
   uint32_t sum = 0;
   for (int q = 0; q < per; ++q) sum += hist[hi - q];
   uint32_t total;

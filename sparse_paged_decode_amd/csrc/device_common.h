@@ -84,6 +84,16 @@ __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
 __device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// threadIdx.x read through an empty asm statement.  Values derived from it
+// then cannot be hoisted out of the persistent kernel's work-item loop,
+// where they would stay live across every kind of item and crowd out the
+// registers each item needs.
+__device__ __forceinline__ int thread_index() {
+  int t = __builtin_amdgcn_workitem_id_x();
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Set device error bits in the workspace error word.
 __device__ __forceinline__ void raise_error(uint32_t* err, uint32_t bits) {
   atomicOr(err, bits);

@@ -48,20 +48,29 @@ constexpr uint32_t kHdrExits = 1;    // workgroups that have left
 constexpr uint32_t kHdrCleared = 2;  // clear items done
 constexpr uint32_t kHdrZeroed = 3;   // zero region the last call left clean, in 256-B units
 constexpr uint32_t kHdrWords = 4;
+// Work-item descriptors: kind in the top bits, index below.
+constexpr uint32_t kItemScan = 1, kItemFilter = 2, kItemAttn = 3, kItemSelect = 4;
+constexpr uint32_t kKindShift = 28;
+constexpr uint32_t kIndexMask = (1u << kKindShift) - 1u;
 
 struct StepLayout {
   int mode, B, T, H, k, sparse;
   int q_groups;      // ceil(T / 4) query-token groups per request
-  int chunks;        // scan chunks per request (bt_stride / 16 pages, rounded up)
+  int chunk_pages;   // index pages per scan chunk
+  int chunks;        // scan chunks per query group (bt_stride / chunk_pages, rounded up)
   int lcap;          // bt_stride * 128: capacity of a score row
   int slices;        // filter slices per query token (lcap / 4096, rounded up)
   int split_tokens;  // attention candidates per split
   int n_splits;      // attention splits per (query token, KV head)
-  uint32_t n_clear, n_scan, n_filter, n_attn;  // work items of each kind (clear: when needed)
+  int select_mode;   // 1: one workgroup selects each query token's top k
+  uint32_t n_clear, n_scan, n_select, n_filter, n_attn;  // work items of each kind (clear: when needed)
+  uint32_t n_ready0;    // items ready at the start (the first tickets after the clear items)
+  uint32_t ready_kind;  // their kind
+  uint32_t n_queue;     // items published into the ready queue while the kernel runs
   size_t zero_end;      // [ctrl_base + header, zero_end) must be zero when items start
   uint64_t zero_units;  // zero_end / 256
   // control block (u32 words from ctrl_base): word offsets
-  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, sel_ready, attn_cnt, ctrl_words;
+  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, pub, queue, ctrl_words;
   // byte offsets in the workspace
   size_t err, ctrl_base, hist, scores, cand, pm, pl, pacc, total;
 };

@@ -1,21 +1,27 @@
 // One persistent work-queue kernel runs every step of the path (gfx950).
 //
-// Work items, handed out in ticket order by one atomic counter:
+// Work items:
 //   scan   (request b, query group, chunk of 16 index pages)  -> scan_chunk
-//   filter (query token i, slice of 4096 scores)               -> filter_slice,
+//   select (query token i), for score rows of at most 64K      -> select_query
+//   filter (query token i, slice of 4096 scores), longer rows  -> filter_slice,
 //          and the last slice of i to finish                   -> resolve_query
 //   attn   (query token i, KV head h, split of candidates)    -> attn_split
 //          (the last split of (i, h) to finish merges them)
 // mono_index_score_topk runs the scan and filter items, mono_pa_decode_mxfp4
 // the attention items, mono_sparse_decode_mxfp4 all three in one launch.
 //
-// A filter item waits until every scan item of its request and query group
-// is done; a fused attention item waits until its query token's selection
-// is complete.  Items only ever wait for items with smaller tickets, which
-// were handed to running workgroups that never wait on later items, so every
-// wait ends; each wait is also bounded and flags MONO_DEVERR_WAIT if the
-// bound is reached, so the kernel always terminates.  The last workgroup to
-// leave resets the queue and all counters for the next call.
+// Workgroups take tickets from one atomic counter.  The first tickets are
+// the items that are ready at the start (the scans, or the attention splits
+// of the attention call); every later ticket is a slot of a ready queue.
+// An item that completes a dependency publishes the items it unblocks: the
+// last scan chunk of a query group publishes the group's select items or
+// filter slices (or, with one query token per request and a short row,
+// selects it at once), and whoever completes a query token's selection
+// publishes the token's attention splits.  So no item ever waits
+// for another; a workgroup only waits for its queue slot to be filled, and
+// the number of published items is fixed by the shapes, so every slot is
+// filled (every wait is also bounded and flags MONO_DEVERR_WAIT).  The last
+// workgroup to leave resets the queue and all counters for the next call.
 #include "attn_device.h"
 #include "mono_decode.h"
 #include "topk_device.h"
@@ -37,7 +43,8 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.sparse = sparse;
   const size_t N = (size_t)B * T;
   l.q_groups = (T + 3) / 4;
-  l.chunks = (bt_stride + kScanChunkPages - 1) / kScanChunkPages;
+  l.chunk_pages = kScanChunkPages;  // launch_step re-balances this to the resident workgroups
+  l.chunks = (bt_stride + l.chunk_pages - 1) / l.chunk_pages;
   l.lcap = bt_stride * kPageTokens;
   l.slices = (l.lcap + kSlice - 1) / kSlice;
   const bool index = (mode & kModeIndex) != 0, attn = (mode & kModeAttn) != 0;
@@ -50,9 +57,18 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.split_tokens = split;
   l.n_splits = (int)((list_max + split - 1) / split);
 
+  // Selection by slices and a resolve; launch_step may switch to one
+  // workgroup per query token instead (the queue is sized for slices, the
+  // larger of the two).
+  l.select_mode = 0;
   l.n_scan = index ? (uint32_t)(B * l.q_groups * l.chunks) : 0u;
+  l.n_select = 0u;
   l.n_filter = index ? (uint32_t)(N * l.slices) : 0u;
   l.n_attn = attn ? (uint32_t)(NH * l.n_splits) : 0u;
+  // Items ready at the start take the first tickets; the rest are published.
+  l.n_ready0 = index ? l.n_scan : l.n_attn;
+  l.ready_kind = index ? kItemScan : kItemAttn;
+  l.n_queue = index ? l.n_select + l.n_filter + l.n_attn : 0u;
 
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -74,10 +90,12 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   w += index ? N : 0;
   l.cand_cnt = w;
   w += index ? N : 0;
-  l.sel_ready = w;
-  w += index ? N : 0;
   l.attn_cnt = w;
   w += attn ? NH : 0;
+  l.pub = w;
+  w += 1;
+  l.queue = w;
+  w += l.n_queue;
   l.ctrl_words = w;
   l.ctrl_base = take(w * 4);
   l.hist = take(index ? N * kHistBins * 4 : 0);
@@ -107,15 +125,15 @@ __device__ __forceinline__ void clear_item(const StepLayout& lay, uint32_t c, ui
   const size_t end = min(begin + (size_t)kClearBytes, lay.zero_end);
   uint32_t* p = reinterpret_cast<uint32_t*>(ws + begin);
   const int n = (int)((end - begin) / 4);
-  for (int x = threadIdx.x; x < n; x += kBlock) store_coherent(p + x, 0u);
+  for (int x = thread_index(); x < n; x += kBlock) store_coherent(p + x, 0u);
   wait_vmem();
   __syncthreads();
-  if (threadIdx.x == 0) atomicAdd(ctrl + kHdrCleared, 1u);
+  if (thread_index() == 0) atomicAdd(ctrl + kHdrCleared, 1u);
 }
 
 // Thread 0 waits until *p >= target; everyone leaves together.
 __device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target, uint32_t* err) {
-  if (threadIdx.x == 0) {
+  if (thread_index() == 0) {
     uint32_t spins = 0;
     while (load_coherent(p) < target) {
       __builtin_amdgcn_s_sleep(2);
@@ -128,13 +146,49 @@ __device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target,
   __syncthreads();
 }
 
+// Thread 0 waits until queue slot q is filled; returns its descriptor to
+// every thread (0 if the bounded wait ran out: the slot is then skipped).
+__device__ __forceinline__ uint32_t wait_slot(const uint32_t* q, uint32_t* err, uint32_t& s_desc) {
+  if (thread_index() == 0) {
+    uint32_t spins = 0, d;
+    while ((d = load_coherent(q)) == 0u) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kMaxSpins) {
+        raise_error(err, kErrWait);
+        break;
+      }
+    }
+    s_desc = d;
+  }
+  __syncthreads();
+  const uint32_t d = s_desc;
+  __syncthreads();
+  return d;
+}
+
+// Publish items first..first+count-1 of one kind into the ready queue.
+// Called by every thread of the workgroup after its own results are
+// complete (wait_vmem and a barrier), so consumers see them.
+__device__ __forceinline__ void publish(const StepLayout& lay, uint32_t* ctrl, uint32_t kind, uint32_t first,
+                                        uint32_t count, uint32_t* err, uint32_t& s_base) {
+  if (thread_index() == 0) s_base = atomicAdd(ctrl + lay.pub, count);
+  __syncthreads();
+  const uint32_t base = s_base;
+  if (base + count > lay.n_queue) {  // never expected: the counts are fixed by the shapes
+    if (thread_index() == 0) raise_error(err, kErrSelection);
+    return;
+  }
+  for (uint32_t x = thread_index(); x < count; x += kBlock)
+    store_coherent(ctrl + lay.queue + base + x, (kind << kKindShift) | (first + x));
+}
+
 // Chunks of request b's query group qg (pages seen by the group's last query token).
-__device__ __forceinline__ int group_chunks(int L, int T, int qg, int& tq, int& n_pages) {
+__device__ __forceinline__ int group_chunks(int L, int T, int qg, int chunk_pages, int& tq, int& n_pages) {
   const int t0 = qg * 4;
   tq = min(4, T - t0);
   const int n_tok = L - T + t0 + tq;
   n_pages = (n_tok + kPageTokens - 1) / kPageTokens;
-  return (n_pages + kScanChunkPages - 1) / kScanChunkPages;
+  return (n_pages + chunk_pages - 1) / chunk_pages;
 }
 
 template <int TQ>
@@ -145,59 +199,9 @@ union StepLds {
   AttnLds attn;
 };
 
-template <int TQ>
-__device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& lay, uint32_t t, ScanLds<TQ>& lds,
-                                          uint32_t* ctrl, uint32_t* err) {
-  const int per_b = lay.q_groups * lay.chunks;
-  const int b = (int)(t / per_b);
-  const int rem = (int)(t % per_b);
-  const int qg = rem / lay.chunks, c = rem % lay.chunks;
-  const int T = lay.T;
-  const int L = a.seq_lens[b];
-  if (L < T || L > lay.lcap) {
-    if (c == 0 && qg == 0 && threadIdx.x == 0) raise_error(err, kErrSeqLen);
-    return;
-  }
-  int tq, n_pages;
-  const int nchunks = group_chunks(L, T, qg, tq, n_pages);
-  if (c >= nchunks) return;
-  const int t0 = qg * 4;
-  const int q0 = b * T + t0;
-  ScanArgs sa;
-  sa.index_q = a.index_q;
-  sa.pages = a.index_pages;
-  sa.num_pages = a.num_pages;
-  sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
-  sa.q_scores = reinterpret_cast<float*>(a.ws + lay.scores) + (size_t)q0 * lay.lcap;
-  sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)q0 * kHistBins;
-  sa.err = err;
-  sa.lcap = lay.lcap;
-  sa.q0 = q0;
-  sa.pos0 = L - T + t0;
-  sa.tq = tq;
-  sa.p_begin = c * kScanChunkPages;
-  sa.p_end = min(sa.p_begin + kScanChunkPages, n_pages);
-  scan_chunk<TQ>(sa, lds);
-  wait_vmem();  // scores and histogram updates are complete before the arrival
-  __syncthreads();
-  if (threadIdx.x == 0) atomicAdd(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, 1u);
-}
-
-template <int TQ>
-__device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout& lay, uint32_t u, StepLds<TQ>& lds,
-                                            uint32_t* ctrl, uint32_t* err, uint32_t& s_flag) {
-  const int i = (int)(u / lay.slices), s = (int)(u % lay.slices);
-  const int T = lay.T, b = i / T, t = i % T;
-  const int L = a.seq_lens[b];
-  if (L < T || L > lay.lcap) return;  // reported by the scan items
-  const int n_valid = L - T + t + 1;
-  const int n_slices = (n_valid + kSlice - 1) / kSlice;
-  if (s >= n_slices) return;
-  const int qg = t / 4;
-  int tq, n_pages;
-  const int nchunks = group_chunks(L, T, qg, tq, n_pages);
-  wait_counter(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, (uint32_t)nchunks, err);
-
+// Selection arguments of query token i.
+__device__ __forceinline__ SelectArgs select_args(const StepArgs& a, const StepLayout& lay, int i, int n_valid,
+                                                  uint32_t* ctrl, uint32_t* err) {
   SelectArgs sa;
   sa.scores = reinterpret_cast<const float*>(a.ws + lay.scores) + (size_t)i * lay.lcap;
   sa.lcap = lay.lcap;
@@ -210,16 +214,108 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   sa.err = err;
   sa.n_valid = n_valid;
   sa.k = lay.k;
-  filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
-  wait_vmem();
+  return sa;
+}
+
+// Whole selection of query token i (if its request is valid), then, in the
+// one-launch step, publication of its attention splits.
+template <int TQ>
+__device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout& lay, uint32_t i, StepLds<TQ>& lds,
+                                            uint32_t* ctrl, uint32_t* err, uint32_t& s_pub) {
+  const int T = lay.T, b = (int)i / T, t = (int)i % T;
+  const int L = a.seq_lens[b];
+  if (L >= T && L <= lay.lcap) {  // an invalid length was reported by the scan items
+    select_query(select_args(a, lay, (int)i, L - T + t + 1, ctrl, err), lds.resolve);
+    wait_vmem();
+  }
   __syncthreads();
-  if (threadIdx.x == 0) s_flag = (atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(n_slices - 1)) ? 1u : 0u;
+  if (lay.mode == kModeFused)
+    publish(lay, ctrl, kItemAttn, i * (uint32_t)(lay.H * lay.n_splits), (uint32_t)(lay.H * lay.n_splits), err, s_pub);
+}
+
+template <int TQ>
+__device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& lay, uint32_t t, StepLds<TQ>& slds,
+                                          uint32_t* ctrl, uint32_t* err, uint32_t& s_flag, uint32_t& s_pub) {
+  ScanLds<TQ>& lds = slds.scan;
+  const int per_b = lay.q_groups * lay.chunks;
+  const int b = (int)(t / per_b);
+  const int rem = (int)(t % per_b);
+  const int qg = rem / lay.chunks, c = rem % lay.chunks;
+  const int T = lay.T;
+  const int L = a.seq_lens[b];
+  const int t0 = qg * 4;
+  const int tq_all = min(4, T - t0);
+  if (L < T || L > lay.lcap) {
+    if (c == 0 && qg == 0 && thread_index() == 0) raise_error(err, kErrSeqLen);
+  } else {
+    int tq, n_pages;
+    const int nchunks = group_chunks(L, T, qg, lay.chunk_pages, tq, n_pages);
+    if (c < nchunks) {
+      const int q0 = b * T + t0;
+      ScanArgs sa;
+      sa.index_q = a.index_q;
+      sa.pages = a.index_pages;
+      sa.num_pages = a.num_pages;
+      sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
+      sa.q_scores = reinterpret_cast<float*>(a.ws + lay.scores) + (size_t)q0 * lay.lcap;
+      sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)q0 * kHistBins;
+      sa.err = err;
+      sa.lcap = lay.lcap;
+      sa.q0 = q0;
+      sa.pos0 = L - T + t0;
+      sa.tq = tq;
+      sa.p_begin = c * lay.chunk_pages;
+      sa.p_end = min(sa.p_begin + lay.chunk_pages, n_pages);
+      scan_chunk<TQ>(sa, lds);
+      wait_vmem();  // scores and histogram updates are complete before the arrival
+    }
+  }
+  // Every chunk slot of the group arrives, with or without work; the last
+  // one publishes the group's filter slices.
+  __syncthreads();
+  if (thread_index() == 0)
+    s_flag = atomicAdd(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, 1u) == (uint32_t)(lay.chunks - 1);
   __syncthreads();
   if (!s_flag) return;
-  resolve_query(sa, lds.resolve);
-  wait_vmem();
+  const uint32_t q0 = (uint32_t)(b * T + t0);
+  if (!lay.select_mode) {
+    publish(lay, ctrl, kItemFilter, q0 * (uint32_t)lay.slices, (uint32_t)(tq_all * lay.slices), err, s_pub);
+  } else if (T == 1) {
+    select_item<TQ>(a, lay, q0, slds, ctrl, err, s_pub);
+  } else {
+    publish(lay, ctrl, kItemSelect, q0, (uint32_t)tq_all, err, s_pub);
+  }
+}
+
+template <int TQ>
+__device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout& lay, uint32_t u, StepLds<TQ>& lds,
+                                            uint32_t* ctrl, uint32_t* err, uint32_t& s_flag, uint32_t& s_pub) {
+  const int i = (int)(u / lay.slices), s = (int)(u % lay.slices);
+  const int T = lay.T, b = i / T, t = i % T;
+  const int L = a.seq_lens[b];
+  const bool valid = L >= T && L <= lay.lcap;  // an invalid length was reported by the scan items
+  const int n_valid = L - T + t + 1;
+  const int n_slices = valid ? (n_valid + kSlice - 1) / kSlice : 0;
+
+  const SelectArgs sa = select_args(a, lay, i, n_valid, ctrl, err);
+  if (s < n_slices) {
+    filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
+    wait_vmem();
+  }
+  // Every slice slot arrives; the last one resolves the selection and
+  // publishes the token's attention splits.
   __syncthreads();
-  if (threadIdx.x == 0) atomicAdd(ctrl + lay.sel_ready + i, 1u);
+  if (thread_index() == 0) s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(lay.slices - 1);
+  __syncthreads();
+  if (!s_flag) return;
+  if (valid) {
+    resolve_query(sa, lds.resolve);
+    wait_vmem();
+    __syncthreads();
+  }
+  if (lay.mode == kModeFused)
+    publish(lay, ctrl, kItemAttn, (uint32_t)i * (uint32_t)(lay.H * lay.n_splits), (uint32_t)(lay.H * lay.n_splits),
+            err, s_pub);
 }
 
 template <int TQ>
@@ -232,14 +328,13 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   const int T = lay.T, b = i / T, t = i % T;
   const int L = a.seq_lens[b];
   if (L < T || L > lay.lcap) {
-    if (split == 0 && h == 0 && threadIdx.x == 0) raise_error(err, kErrSeqLen);
+    if (split == 0 && h == 0 && thread_index() == 0) raise_error(err, kErrSeqLen);
     return;
   }
   const int pos = L - T + t;
   const int list_len = lay.sparse ? lay.k : pos + 1;
   const int n_splits = lay.sparse ? S : (list_len + lay.split_tokens - 1) / lay.split_tokens;
   if (split >= n_splits) return;
-  if (lay.mode == kModeFused) wait_counter(ctrl + lay.sel_ready + i, 1u, err);
 
   const size_t qh = (size_t)i * H + h;
   AttnArgs aa;
@@ -269,8 +364,8 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
 template <int TQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
   __shared__ StepLds<TQ> lds;
-  __shared__ uint32_t s_item, s_flag, s_clear;
-  const int tid = threadIdx.x;
+  __shared__ uint32_t s_item, s_flag, s_clear, s_desc, s_pub;
+  const int tid = thread_index();
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + lay.ctrl_base);
 
@@ -282,28 +377,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (tid == 0) s_clear = load_coherent(ctrl + kHdrZeroed) < (uint32_t)lay.zero_units ? lay.n_clear : 0u;
   __syncthreads();
   const uint32_t n_clear = s_clear;
-  const uint32_t n_items = n_clear + lay.n_scan + lay.n_filter + lay.n_attn;
+  const uint32_t n_items = n_clear + lay.n_ready0 + lay.n_queue;
 
+  // A workgroup's first ticket is its index (no start-up rush on the
+  // counter); later tickets come from the counter, offset by the grid size,
+  // and are taken only when the workgroup is free, so a published item
+  // never waits behind a busy workgroup.
+  uint32_t t = blockIdx.x;
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(ctrl + kHdrTicket, 1u);
-    __syncthreads();
-    const uint32_t t = s_item;
-    __syncthreads();
     if (t >= n_items) break;
     if (t < n_clear) {
       clear_item(lay, t, a.ws, ctrl);
     } else {
       const uint32_t u = t - n_clear;
       if (n_clear) wait_counter(ctrl + kHdrCleared, n_clear, err);
-      if (u < lay.n_scan) {
-        scan_item<TQ>(a, lay, u, lds.scan, ctrl, err);
-      } else if (u < lay.n_scan + lay.n_filter) {
-        filter_item<TQ>(a, lay, u - lay.n_scan, lds, ctrl, err, s_flag);
-      } else {
-        attn_item<TQ>(a, lay, u - lay.n_scan - lay.n_filter, lds, ctrl, err);
+      const uint32_t d =
+          u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, s_desc);
+      const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
+      if (kind == kItemScan) {
+        scan_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
+      } else if (kind == kItemSelect) {
+        select_item<TQ>(a, lay, idx, lds, ctrl, err, s_pub);
+      } else if (kind == kItemFilter) {
+        filter_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
+      } else if (kind == kItemAttn) {
+        attn_item<TQ>(a, lay, idx, lds, ctrl, err);
       }
     }
     __syncthreads();  // the next item reuses the LDS
+    if (tid == 0) s_item = gridDim.x + atomicAdd(ctrl + kHdrTicket, 1u);
+    __syncthreads();
+    t = s_item;
   }
 
   // Every workgroup has taken its last ticket before it counts itself out,
@@ -335,14 +439,40 @@ int resident_workgroups(const void* kernel, int variant) {
 
 }  // namespace
 
-int launch_step(const StepArgs& a, const StepLayout& lay, hipStream_t stream, const char* what) {
-  const uint32_t n_items = lay.n_clear + lay.n_scan + lay.n_filter + lay.n_attn;
-  if (n_items == 0) return MONO_OK;
-  if (lay.zero_units > 0xFFFFFFFFull || lay.ctrl_base != 256)
-    return set_error(MONO_ENOTSUP, "%s: workspace layout too large", what);
-  const bool tq4 = lay.T > 1 && (lay.mode & kModeIndex);
+int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream, const char* what) {
+  const bool tq4 = lay_in.T > 1 && (lay_in.mode & kModeIndex);
   const void* kern = tq4 ? reinterpret_cast<const void*>(&step_kernel<4>) : reinterpret_cast<const void*>(&step_kernel<1>);
   const int cap = resident_workgroups(kern, tq4 ? 1 : 0);
+  StepLayout lay = lay_in;
+  if (lay.mode & kModeIndex) {
+    // Scan chunks sized so the scan items make about one round of the
+    // resident workgroups (all of them start together and end together).
+    const int groups = lay.B * lay.q_groups;
+    const int bt_stride = lay.lcap / kPageTokens;
+    const int per_group = std::max(1, cap / std::max(1, groups));
+    lay.chunk_pages = std::min(kMaxChunkPages, std::max(1, (bt_stride + per_group - 1) / per_group));
+    lay.chunks = (bt_stride + lay.chunk_pages - 1) / lay.chunk_pages;
+    lay.n_scan = (uint32_t)((size_t)groups * lay.chunks);
+    lay.n_ready0 = lay.n_scan;
+    // Rows of at most kSelectMax scores are selected by one workgroup each
+    // (inline in the last scan chunk when a request has one query token)
+    // once the slices would take more than two rounds of the resident
+    // workgroups; with fewer query tokens, slices spread each selection
+    // over more compute units and finish sooner.
+    const size_t N = (size_t)lay.B * lay.T;
+    if (lay.lcap <= kSelectMax && N * (size_t)lay.slices > 2 * (size_t)cap) {
+      lay.select_mode = 1;
+      lay.n_filter = 0u;
+      lay.n_select = lay.T > 1 ? (uint32_t)N : 0u;
+      lay.n_queue = lay.n_select + lay.n_attn;
+    }
+  }
+  const uint32_t n_items = lay.n_clear + lay.n_ready0 + lay.n_queue;
+  if (n_items == 0) return MONO_OK;
+  if ((uint64_t)lay.n_scan + lay.n_select + lay.n_filter + lay.n_attn > kIndexMask)
+    return set_error(MONO_ENOTSUP, "%s: too many work items", what);
+  if (lay.zero_units > 0xFFFFFFFFull || lay.ctrl_base != 256)
+    return set_error(MONO_ENOTSUP, "%s: workspace layout too large", what);
   const unsigned grid = (unsigned)std::min<uint64_t>(n_items, (uint64_t)cap);
   const int kid = lay.mode == kModeIndex ? kKIndexScan : (lay.mode == kModeAttn ? kKPaDecode : kKStep);
   if (tq4) {

@@ -27,9 +27,12 @@
 #include "block_ops.h"
 #include "launch.h"
 
+#include <type_traits>
+
 namespace mono {
 
-constexpr int kScanChunkPages = 16;  // index pages per scan work item
+constexpr int kScanChunkPages = 16;  // index pages per scan work item (default)
+constexpr int kMaxChunkPages = 64;   // one page id per lane of a wave
 constexpr int kBatch = 4;            // pages per prefetch batch
 constexpr int kHistBins = 2048;      // top 11 bits of the score key
 constexpr int kHistShift = 21;
@@ -65,7 +68,7 @@ struct ScanArgs {
 
 template <int TQ>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
 
   // A operand: row m is query token t0 + m (zero when m >= tq); its k-slot
@@ -107,8 +110,9 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
 
   // Pages are fetched in batches of kBatch, one batch ahead of the one being
   // scored.  Loads are unconditional (past the chunk end they repeat its last
-  // page, whose rows are then all masked), so the compiler can count the
-  // outstanding loads exactly and wait only for the batch being scored.
+  // page, and those slots are skipped when scoring), so the compiler can
+  // count the outstanding loads exactly and wait only for the batch being
+  // scored.
   struct Rows {
     u32x4_t d[2];
     uint32_t e[2];
@@ -125,6 +129,7 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
     }
   };
   auto score_page = [&](const Rows& r, int p) {
+    if (p >= p_end) return;  // past the chunk: the registers hold a repeat of its last page
     const float sc0 = e8m0_scale_operand(r.e[0]);
     const float sc1 = e8m0_scale_operand(r.e[1]);
     f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
@@ -186,11 +191,14 @@ struct FilterLds {
   uint32_t scratch[8];
 };
 
+constexpr int kSelBatchesMax = 16;  // select_query batches (kSelectMax / (kBlock * 16))
+
 struct ResolveLds {
   uint32_t hist[kHistBins];
-  uint2 cand[kLdsCand];
+  uint2 cand[kLdsCand + 1];  // + a spare entry for branch-free writes
   uint32_t scratch[8];
   uint32_t cnt;
+  uint16_t marks[kSelBatchesMax][kBlock];  // select_query: tokens above the threshold bin
 };
 
 struct SelectArgs {
@@ -219,7 +227,7 @@ __device__ __forceinline__ void put_selection(const SelectArgs& a, uint32_t slot
 
 // Loads a histogram row into LDS and finds the bin of the k-th largest score.
 __device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* hist, uint32_t* scratch) {
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   uint32_t h[kHistBins / kBlock];
 #pragma unroll
   for (int u = 0; u < kHistBins / kBlock; ++u) h[u] = load_coherent(a.ghist + u * kBlock + tid);
@@ -231,7 +239,7 @@ __device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* hist,
 
 // Slice [j0, j1) of the scores.
 __device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds) {
-  const int tid = threadIdx.x;
+  const int tid = thread_index();
   if (a.n_valid <= a.k) {  // at most k valid tokens: all of them, then -1 padding
     for (int j = j0 + tid; j < j1; j += kBlock) put_selection(a, (uint32_t)j, j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
     if (j0 == 0) {
@@ -282,42 +290,32 @@ __device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1
   }
 }
 
-// The remaining tokens of bin B1, once every slice is done.  Leaves the
-// histogram row zero.
-__device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& lds) {
-  const int tid = threadIdx.x;
+// Where pick_in_bin reads the tokens of the threshold bin from.
+enum : int { kSrcLds = 0, kSrcList = 1, kSrcScores = 2 };
+
+// The remaining k - above tokens, all in histogram bin B1 (which holds
+// in_bin tokens), by two more radix passes (key bits 20..10, then 9..0);
+// exact ties at the threshold go to the lowest token indices.  Slots
+// above..k-1 of the output are filled.  With kSrcLds the candidates are in
+// lds.cand[0..in_bin) already.
+__device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds, uint32_t B1, uint32_t above,
+                                            uint32_t in_bin, int src) {
+  const int tid = thread_index();
   const int n_valid = a.n_valid;
-  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
-  for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
-  if (n_valid <= a.k) return;  // the filter items wrote everything
-  const uint32_t B1 = (uint32_t)sp.bin;
-  const uint32_t above = sp.above;
-  const uint32_t in_bin = sp.count;
-  const bool use_cand = in_bin <= (uint32_t)kCandCap;
-  const bool in_lds = in_bin <= (uint32_t)kLdsCand;
-  if (in_lds) {
-    constexpr int kPer = kLdsCand / kBlock;
-    uint64_t c[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) lds.cand[u * kBlock + tid] = make_uint2((uint32_t)c[u], (uint32_t)(c[u] >> 32));
-  }
   if (tid == 0) lds.cnt = above;
   __syncthreads();
 
-  // Candidate source: the LDS copy, the global list, or (if it overflowed)
-  // every valid score filtered by bin; all yield the same multiset of (key, j).
   const uint32_t R = (uint32_t)a.k - above;  // 1 <= R <= in_bin
-  const int n_src = use_cand ? (int)in_bin : n_valid;
+  const int n_src = src == kSrcScores ? n_valid : (int)in_bin;
+  // All three sources yield the same multiset of (key, j).
   auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
-    if (in_lds) {
+    if (src == kSrcLds) {
       const uint2 c = lds.cand[e];
       key = c.x;
       j = (int)c.y;
       return true;
     }
-    if (use_cand) {
+    if (src == kSrcList) {
       const uint64_t c = load_coherent(a.cand + e);
       key = (uint32_t)c;
       j = (int)(c >> 32);
@@ -388,6 +386,145 @@ __device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& l
       taken += tot;
     }
   }
+}
+
+// The remaining tokens of bin B1, once every slice is done.  Leaves the
+// histogram row zero.
+__device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& lds) {
+  const int tid = thread_index();
+  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
+  if (a.n_valid <= a.k) return;  // the filter items wrote everything
+  const uint32_t in_bin = sp.count;
+  const bool use_cand = in_bin <= (uint32_t)kCandCap;
+  const bool in_lds = in_bin <= (uint32_t)kLdsCand;
+  if (in_lds) {
+    constexpr int kPer = kLdsCand / kBlock;
+    uint64_t c[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) lds.cand[u * kBlock + tid] = make_uint2((uint32_t)c[u], (uint32_t)(c[u] >> 32));
+  }
+  pick_in_bin(a, lds, (uint32_t)sp.bin, sp.above, in_bin, in_lds ? kSrcLds : (use_cand ? kSrcList : kSrcScores));
+}
+
+// ---------------------------------------------------------------------------
+// select_query: the whole top-k of one query token in one workgroup, for
+// score rows of at most kSelectMax: the histogram gives bin B1 of the k-th
+// largest score, one streaming pass over the scores marks the tokens of
+// higher bins and collects bin B1's tokens in LDS, then the marked tokens
+// are written and pick_in_bin takes the rest.  Leaves the histogram row zero.
+// ---------------------------------------------------------------------------
+constexpr int kSelectMax = 65536;      // longest score row a single workgroup selects from
+constexpr int kSelPer = 16;            // scores per thread per batch
+constexpr int kSelBatch = kBlock * kSelPer;
+static_assert(kSelectMax / kSelBatch == kSelBatchesMax, "select batches");
+constexpr int kSelAhead = 3;           // batches in flight beyond the one being classified
+
+__device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& lds) {
+  const int tid = thread_index();
+  const int n_valid = a.n_valid, k = a.k;
+  if (n_valid <= k) {  // at most k valid tokens: all of them, then -1 padding
+    for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
+    for (int j = tid; j < k; j += kBlock) {
+      if (j < n_valid) {
+        put_selection(a, (uint32_t)j, j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
+      } else {
+        store_coherent(reinterpret_cast<uint32_t*>(a.out + j), 0xffffffffu);
+        if (a.out_scores) store_coherent(a.out_scores + j, __uint_as_float(0x7fc00000u));
+      }
+    }
+    return;
+  }
+  // Each score line was written whole by one scan workgroup earlier in this
+  // launch and is not cached on this die before, so plain 16-byte loads
+  // read it current.  The loop issues no store and no barrier, so the loads
+  // of kSelAhead batches stay in flight while one is classified; the first
+  // ones are issued before the histogram is read.
+  // Loads are unconditional (past the valid scores they all read the row's
+  // last valid 64 bytes, one cache line) so the compiler can count the
+  // outstanding loads exactly and keep kSelAhead batches in flight.
+  const int last = ((n_valid + kSelPer - 1) & ~(kSelPer - 1)) - kSelPer;
+  auto load_batch = [&](f32x4_t* v, int b) {
+    const int j0 = min(b * kSelBatch + tid * kSelPer, last);
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(a.scores + j0);
+#pragma unroll
+    for (int q = 0; q < kSelPer / 4; ++q) v[q] = src[q];
+  };
+  f32x4_t v[kSelAhead + 1][kSelPer / 4];
+#pragma unroll
+  for (int b = 0; b < kSelAhead; ++b) load_batch(v[b], b);
+  if (tid == 0) lds.cnt = 0u;  // candidate count while streaming
+  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
+  const uint32_t B1 = (uint32_t)sp.bin, above = sp.above, in_bin = sp.count;
+  const bool in_lds = in_bin <= (uint32_t)kLdsCand;
+  const int nb = (n_valid + kSelBatch - 1) / kSelBatch;
+
+  // Bit u of lds.marks[b][tid]: token b * kSelBatch + tid * kSelPer + u is
+  // above B1.  The batch loop is rolled over groups of kSelAhead + 1 batches
+  // (a static ring of registers within a group).
+  uint32_t mine = 0;
+  for (int b0 = 0; b0 < nb; b0 += kSelAhead + 1) {
+#pragma unroll
+    for (int bb = 0; bb <= kSelAhead; ++bb) {
+      const int b = b0 + bb;
+      load_batch(v[(bb + kSelAhead) % (kSelAhead + 1)], b + kSelAhead);
+      if (b >= nb) continue;  // uniform
+      const f32x4_t* cur = v[bb];
+      const int j0 = b * kSelBatch + tid * kSelPer;
+      uint32_t hi = 0, eq = 0;
+#pragma unroll
+      for (int u = 0; u < kSelPer; ++u) {
+        const uint32_t bin = score_key(cur[u >> 2][u & 3]) >> kHistShift;
+        const bool in = j0 + u < n_valid;
+        hi |= (in && bin > B1) ? (1u << u) : 0u;
+        eq |= (in && bin == B1) ? (1u << u) : 0u;
+      }
+      lds.marks[b][tid] = (uint16_t)hi;
+      mine += __popc(hi);
+      // Candidates go to LDS now (an LDS atomic, no memory wait), without
+      // branches: lanes write every slot u, the ones that are not
+      // candidates into a spare entry.
+      if (in_lds && __ballot(eq != 0u) != 0ull) {
+        uint32_t c = 0;
+        if (eq) c = atomicAdd(&lds.cnt, (uint32_t)__popc(eq));
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+          const uint32_t pos = ((eq >> u) & 1u) ? c + (uint32_t)__popc(eq & ((1u << u) - 1u)) : (uint32_t)kLdsCand;
+          lds.cand[min(pos, (uint32_t)kLdsCand)] = make_uint2(score_key(cur[u >> 2][u & 3]), (uint32_t)(j0 + u));
+        }
+      }
+    }
+  }
+  // The marked tokens take slots 0..above-1.
+  uint32_t n_hi;
+  uint32_t slot = block_exclusive_scan(mine, lds.scratch, n_hi);
+  const uint32_t n_cand = lds.cnt;
+  // Two copies of the write loop: without the score output it holds no load,
+  // so its stores need not wait for one another.
+  auto write_marked = [&](auto with_scores) {
+    for (int b = 0; b < nb; ++b) {
+      uint32_t bits = lds.marks[b][tid];
+      while (bits) {
+        const int u = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        const int j = b * kSelBatch + tid * kSelPer + u;
+        put_selection(a, slot++, j, with_scores ? load_coherent(a.scores + j) : 0.f);
+      }
+    }
+  };
+  if (a.out_scores) {
+    write_marked(std::true_type{});
+  } else {
+    write_marked(std::false_type{});
+  }
+  if (n_hi != above || (in_lds && n_cand != in_bin)) {  // never expected: counts disagree with the histogram
+    if (tid == 0) raise_error(a.err, kErrSelection);
+    return;
+  }
+  pick_in_bin(a, lds, B1, above, in_bin, in_lds ? kSrcLds : kSrcScores);
 }
 
 }  // namespace mono

@@ -49,6 +49,9 @@ SMALL = [
     ("several_chunks", 2, 1, [5000, 4097], 40, 700),
     ("t3_group", 2, 3, [640, 3001], 24, 250),
     ("t6_two_groups", 2, 6, [900, 2300], 18, 128),
+    # score rows longer than 64K: the slice-and-resolve selection
+    ("wide_table_slices", 2, 1, [3000, 9000], 520, 700),
+    ("wide_table_slices_t2", 2, 2, [5000, 9100], 520, 300),
 ]
 
 
@@ -131,3 +134,32 @@ def test_topk_full_size_sampled(spd, number, samples):
         row = sel[i]
         assert np.all(row[n:] == -1) and np.all((row[:n] >= 0) & (row[:n] <= pos[i]))
         assert np.unique(row[:n]).size == n
+
+
+# Many query tokens: more filter slices than two rounds of the resident
+# workgroups, so each token's top k is taken by one workgroup.
+MANY = [
+    ("many_queries_t1", 300, 1, (100, 3000), 100, 300),
+    ("many_queries_t2", 150, 2, (100, 5000), 100, 500),
+]
+
+
+@pytest.mark.parametrize("name,B,T,lens,W,k", MANY, ids=[c[0] for c in MANY])
+def test_topk_many_query_tokens(spd, name, B, T, lens, W, k):
+    w = make_workload(name, B=B, T=T, seq_lens=lens, bt_width=W, k=k, seed=sum(map(ord, name)))
+    sel, _ = _run(spd, w, k)
+    for i in range(w.N):
+        check_topk_row(sel[i], w, i, k)
+
+
+def test_topk_many_query_tokens_all_equal():
+    """Every score equal in every row: the threshold bin overflows LDS, ties go to the lowest indices."""
+    import sparse_paged_decode_amd as spd
+
+    w = make_workload("eqmany", B=300, T=1, seq_lens=5000, bt_width=100, k=1000, seed=15)
+    codes = np.full((w.num_pages, 128, 128), 3, dtype=np.uint8)
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+    sel, _ = _run(spd, w, 1000)
+    ref = np.arange(1000)
+    for i in range(w.N):
+        assert np.array_equal(np.sort(sel[i]), ref), f"query {i}"

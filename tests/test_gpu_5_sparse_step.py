@@ -57,6 +57,9 @@ SMALL = [
     ("several_slices", 2, 1, [9000, 12289], 97, 300, (124, 126)),
     ("t3_group", 2, 3, [640, 3001], 24, 250, (124, 127)),
     ("t6_two_groups", 2, 6, [900, 2300], 18, 128, (122, 132)),
+    # score rows longer than 64K: the slice-and-resolve selection
+    ("wide_table_slices", 2, 1, [3000, 9000], 520, 700, (124, 127)),
+    ("wide_table_slices_t3", 2, 3, [5000, 9100], 520, 300, (122, 132)),
 ]
 
 
@@ -173,3 +176,21 @@ def test_one_workspace_across_shapes_and_entry_points(spd):
         ref = decode.pa_decode(w.q, w.k_pool, w.v_pool, w.block_table, w.seq_lens, w.T, w.scale, None)
         o = mxfp4.bf16_bits_to_f64(bf16_bits(out_d))
         assert np.linalg.norm(o - ref) <= 5e-3 * np.linalg.norm(ref), f"dense attention, shape {n}"
+
+
+def test_step_many_query_tokens(spd):
+    """More filter slices than two rounds of the resident workgroups: one
+    workgroup selects each token, inline in the last scan chunk (T = 1) or
+    as a published item (T = 2)."""
+    for name, B, T in (("many_step_t1", 300, 1), ("many_step_t2", 150, 2)):
+        w = make_workload(name, B=B, T=T, seq_lens=(100, 3000), bt_width=100, k=300, seed=sum(map(ord, name)),
+                          exp_range=(124, 127))
+        d = to_device(w)
+        ws = spd.Workspace("cuda")
+        out, sel = _step(spd, w, d, ws)
+        assert spd.check_device_errors(ws) == 0
+        sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+        for i in range(0, w.N, 7):
+            _check_token(w, i, sel_np[i], out_bits)
+        for i in range(w.N):
+            check_topk_row(sel_np[i], w, i, w.k)
