@@ -84,6 +84,8 @@ def parse():
     p.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
     p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
+    p.add_argument("--skip-two-call", action="store_true",
+                   help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 128 MiB device copy 10 times (counter calibration) and exit")
     return p.parse_args()
@@ -232,7 +234,7 @@ def main():
             step(s % copies)
         torch.cuda.synchronize(dev)
     two = {}
-    if w.sparse:
+    if w.sparse and not args.skip_two_call:
         for s in range(args.warmup):
             two_calls(s % copies)
         torch.cuda.synchronize(dev)
