@@ -84,6 +84,7 @@ def parse():
     p.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
     p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
     p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
+    p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
     p.add_argument("--skip-two-call", action="store_true",
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -244,6 +245,27 @@ def main():
             torch.cuda.synchronize(dev)
         two = {name: round(us, 2) for name, us in kt2.mean_us.items()}
 
+    # The same steps replayed from HIP graphs (one captured step per pool
+    # copy), timed like the plain launches.
+    graph_ms = None
+    if not args.skip_graph:
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for s in range(args.warmup):
+            graphs[s % copies].replay()
+        torch.cuda.synchronize(dev)
+        ge = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ge[0].record(stream)
+        for s in range(K):
+            graphs[s % copies].replay()
+        ge[1].record(stream)
+        torch.cuda.synchronize(dev)
+        graph_ms = ge[0].elapsed_time(ge[1]) / K
+
     # Roofline entry of the step kernel (on dense workloads the attention
     # kernel is the step).
     dom = "sparse_decode_kernel" if w.sparse else "pa_decode_kernel"
@@ -278,6 +300,7 @@ def main():
         "step_us": round(ms_per_step * 1e3, 2),
         "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
         "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
+        "graph_step_us": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "bytes_per_step": {"index": idx_bytes, "kv": kv_bytes},
         "kernels_us_mean": {name: round(us, 2) for name, us in kt.mean_us.items()},
@@ -297,6 +320,8 @@ def main():
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
         "device": torch.cuda.get_device_name(dev),
+        "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+        "hip": torch.version.hip,
     }
     print(json.dumps(line))
 

@@ -94,10 +94,14 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 
   // The first pass's selection entries are requested first; the block-table
   // row (into LDS) and the q operand (into registers) load meanwhile.
+  // The entry load is unconditional (clamped inside the split, masked
+  // after) so the compiler can count outstanding loads exactly.
   auto entry_of = [&](int grp) -> int {
     const int entry = e0 + kGroupTokens * grp + m;
-    if (grp >= n_groups || entry >= e1) return -1;
-    return a.sel_row ? (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + entry)) : entry;
+    const bool in = grp < n_groups && entry < e1;
+    if (!a.sel_row) return in ? entry : -1;
+    const int j = (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + min(entry, e1 - 1)));
+    return in ? j : -1;
   };
   int jv[kPassGroups];
 #pragma unroll
@@ -201,15 +205,14 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 
   // A pass covers kPassGroups groups of this wave: page lookups, the K/V
   // loads of all of them at once, QK^T of all, one online-softmax update,
-  // then P V of all.
+  // then P V of all.  The first pass's entries were requested at the start.
   for (int gb = wave; gb < n_groups; gb += kWaves * kPassGroups) {
-    if (gb != wave) {
-#pragma unroll
-      for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(gb + kWaves * x);
-    }
     AttnGroup grp[kPassGroups];
 #pragma unroll
     for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(jv[x]));
+    // The next pass's entries load while this pass computes.
+#pragma unroll
+    for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(gb + kWaves * kPassGroups + kWaves * x);
     f32x4_t z[kPassGroups];
     float mx = -INFINITY;
 #pragma unroll

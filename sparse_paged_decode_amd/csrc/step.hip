@@ -32,6 +32,8 @@ namespace mono {
 
 constexpr uint32_t kMaxSpins = 1u << 21;  // bound of one wait (seconds, far above any step)
 constexpr size_t kClearBytes = 32768;     // bytes zeroed by one clear item
+constexpr int kMinSplitTokens = 256;      // attention candidates per split: one pass of 4 waves x 4 groups of 16
+constexpr int kMaxSplitTokens = 8192;
 
 StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse) {
   StepLayout l{};
@@ -49,11 +51,12 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.slices = (l.lcap + kSlice - 1) / kSlice;
   const bool index = (mode & kModeIndex) != 0, attn = (mode & kModeAttn) != 0;
   // Attention splits: 256 candidates per workgroup unless that makes more
-  // than 4096 items.
+  // than 4096 items (launch_step may enlarge them; the partial buffers are
+  // sized for this count).
   const long list_max = sparse ? (long)k : (long)l.lcap;
   const size_t NH = N * H;
-  int split = 256;
-  while (split < 8192 && NH * (size_t)((list_max + split - 1) / split) > 4096) split *= 2;
+  int split = kMinSplitTokens;
+  while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > 4096) split *= 2;
   l.split_tokens = split;
   l.n_splits = (int)((list_max + split - 1) / split);
 
@@ -466,6 +469,20 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
       lay.n_select = lay.T > 1 ? (uint32_t)N : 0u;
       lay.n_queue = lay.n_select + lay.n_attn;
     }
+  }
+  if (lay.mode & kModeAttn) {
+    // Attention splits as large as it takes to make about one round of the
+    // resident workgroups (never smaller than the layout's, whose partial
+    // buffers are sized for the most splits).
+    const size_t NH = (size_t)lay.B * lay.T * lay.H;
+    const long list_max = lay.sparse ? (long)lay.k : (long)lay.lcap;
+    int split = lay.split_tokens;
+    while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > (size_t)cap) split *= 2;
+    lay.split_tokens = split;
+    lay.n_splits = (int)((list_max + split - 1) / split);
+    lay.n_attn = (uint32_t)(NH * lay.n_splits);
+    if (!(lay.mode & kModeIndex)) lay.n_ready0 = lay.n_attn;
+    lay.n_queue = (lay.mode & kModeIndex) ? lay.n_select + lay.n_filter + lay.n_attn : 0u;
   }
   const uint32_t n_items = lay.n_clear + lay.n_ready0 + lay.n_queue;
   if (n_items == 0) return MONO_OK;
