@@ -1,4 +1,5 @@
-"""MXFP4 page geometry and exact dequantisation (CPU oracle, test infrastructure).
+"""MXFP4 page geometry, exact dequantisation and the cache insert (CPU oracle,
+test infrastructure).
 
 Source: page *vllm.models.minimax_m3.amd.ops.mxfp4_pages*, module docstring
 and the function ``mxfp4_page_views``.  One 128-token page of one head holds
@@ -145,3 +146,94 @@ def bf16_bits_to_f64(bits):
     """bfloat16 bit patterns (uint16) -> float64 (exact)."""
     bits = np.asarray(bits, dtype=np.uint16)
     return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Writing rows into pages (the cache insert).
+#
+# The dispatch page (vllm.models.minimax_m3.amd.mono.dispatch, _slots_shared
+# and _step_refusal) says the kernels insert K/V and the index key through
+# one int64 page-128 slot mapping shared by both caches; the mxfp4_pages page
+# names the writer but prints no rule for choosing the scale or rounding.
+# The reading taken is the OCP Microscaling Formats v1.0 conversion for
+# MXFP4: per block of 32 elements the shared exponent is
+# floor(log2(max |v|)) - 2 (2 = the largest exponent of e2m1), and each
+# element v / 2**shared is rounded to the nearest e2m1 value, ties to the
+# even code, magnitudes above 6 saturating to 6.  Readings where that
+# specification leaves a choice:
+#   * an all-zero block gets scale byte 0 and codes 0 (or 8 for -0.0);
+#   * a block holding NaN or +-inf gets scale byte 0xFF (NaN) and codes 0;
+#   * the scale byte is clamped to 0..254.
+# Slot s is row s % 128 of page s // 128; a negative slot is skipped.
+# ---------------------------------------------------------------------------
+def quantize_block(v):
+    """(codes [32] uint8, scale byte) of one 32-element block of float values."""
+    v = np.asarray(v, dtype=np.float64)
+    assert v.shape == (SCALE_BLOCK,)
+    sign = np.signbit(v)
+    if not np.all(np.isfinite(v)):
+        return np.zeros(SCALE_BLOCK, dtype=np.uint8), 0xFF
+    amax = float(np.max(np.abs(v)))
+    if amax == 0.0:
+        return np.where(sign, 8, 0).astype(np.uint8), 0
+    # floor(log2 amax), exactly: frexp gives amax = m * 2**e with m in [0.5, 1).
+    shared = (int(np.frexp(amax)[1]) - 1) - 2
+    byte = min(max(shared + 127, 0), 254)
+    q = np.abs(v) / 2.0 ** (byte - 127)
+    codes = np.empty(SCALE_BLOCK, dtype=np.uint8)
+    for n, x in enumerate(q):
+        codes[n] = _nearest_e2m1(x) | (8 if sign[n] else 0)
+    return codes, byte
+
+
+def _nearest_e2m1(x):
+    """Code 0..7 of the e2m1 magnitude nearest x >= 0, ties to the even code, saturating."""
+    if x >= E2M1_MAGNITUDES[-1]:
+        # Saturation, stated directly: for very large x the float64 distances
+        # to 4 and to 6 round to the same number and would tie.
+        return 7
+    best = None
+    for code, mag in enumerate(E2M1_MAGNITUDES):
+        d = abs(x - mag)
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, code)
+    return best[1]
+
+
+def quantize_rows(rows):
+    """(codes [..., 128] uint8, scales [..., 4] uint8) of float rows [..., 128]."""
+    rows = np.asarray(rows, dtype=np.float64)
+    lead = rows.shape[:-1]
+    flat = rows.reshape(-1, SCALE_BYTES, SCALE_BLOCK)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty(flat.shape[:-1], dtype=np.uint8)
+    for r in range(flat.shape[0]):
+        for b in range(SCALE_BYTES):
+            codes[r, b], scales[r, b] = quantize_block(flat[r, b])
+    return codes.reshape(*lead, ROW_ELEMS), scales.reshape(*lead, SCALE_BYTES)
+
+
+def insert_rows(pool, rows, slots):
+    """Write float rows [n, heads, 128] into pool [pages, heads, 8704] through slots [n].
+
+    Returns the pool (a copy) and the list of token indices whose slot was
+    past the pool (those rows are not written).
+    """
+    pool = np.array(pool, dtype=np.uint8, copy=True)
+    rows = np.asarray(rows, dtype=np.float64)
+    n_pages = pool.shape[0]
+    codes, scales = quantize_rows(rows)
+    data, scale = page_views(pool)
+    skipped = []
+    for t, s in enumerate(np.asarray(slots, dtype=np.int64)):
+        if s < 0:
+            continue
+        page, row = divmod(int(s), PAGE_TOKENS)
+        if page >= n_pages:
+            skipped.append(t)
+            continue
+        for h in range(rows.shape[1]):
+            c = codes[t, h]
+            data[page, h, row] = (c[0::2] | (c[1::2] << 4)).astype(np.uint8)
+            scale[page, h, row] = scales[t, h]
+    return pool, skipped
