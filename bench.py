@@ -18,8 +18,10 @@ rows of every selected token once per request) and the step time, both from
 the timed region; the roofline entry of the step kernel, timed in a second
 pass of the same steps with HIP events recorded around each launch on its
 stream; the two-call form of the step (index call, then attention call)
-timed the same way, for reference; and the CPU oracle timed on a bounded
-sample of the same workload.
+timed the same way, for reference; the MXFP4 cache insert (the decoded
+tokens' K, V and index-key rows written through their slots, and a
+32768-token prefill-sized insert) by kernel time; and the CPU oracle timed on
+a bounded sample of the same workload.
 """
 
 import argparse
@@ -45,6 +47,7 @@ KERNEL_SOURCES = {
     "sparse_decode_kernel": _STEP_SOURCES,
     "index_topk_kernel": _STEP_SOURCES,
     "pa_decode_kernel": _STEP_SOURCES,
+    "insert_kernel": ["pages.hip", "device_common.h", "launch.h"],
 }
 
 
@@ -85,6 +88,7 @@ def parse():
     p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
     p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
     p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
+    p.add_argument("--skip-insert", action="store_true", help="do not time the cache insert")
     p.add_argument("--skip-two-call", action="store_true",
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -148,6 +152,48 @@ def cpu_baseline(w, n_sample):
         "sample": f"{n} of {w.N} query tokens of {w.name} (scores + top-k + attention per query token), "
         f"{dt:.1f} s; numpy float64, BLAS threads <= {threads}",
     }
+
+
+def insert_bytes(n, heads):
+    """Algorithmic HBM bytes of inserting n tokens into K, V (heads each) and the index key.
+
+    Per written row: 256 B of bf16 read, 64 B of e2m1 and 4 B of scales
+    written; per token: its 8-B slot.
+    """
+    rows = n * (2 * heads + 1)
+    return rows * (256 + 68) + 8 * n
+
+
+def time_insert(spd, torch, dev, w, kp, vp, ip, reps):
+    """Kernel time of the cache insert: the step's own decoded tokens and a 32768-token prefill."""
+    from workloads import decode_slots, new_rows
+
+    H = kp[0].shape[1]
+    res = {}
+    for name, n, slots in (("decode", w.N, decode_slots(w)), ("prefill_32768", 32768, np.arange(32768, dtype=np.int64))):
+        r = new_rows(77, n, H)
+        rows = {c: torch.from_numpy(r[c].view(np.int16)).view(torch.bfloat16).to(dev) for c in r}
+        sl = torch.from_numpy(slots).to(dev)
+        ws = spd.Workspace(dev)
+
+        def ins(c):
+            spd.mono_insert_mxfp4(sl, k_rows=rows["k"], v_rows=rows["v"], index_rows=rows["index"],
+                                  k_pages=kp[c], v_pages=vp[c], index_pages=ip[c], workspace=ws)
+
+        for s in range(5):
+            ins(s % len(kp))
+        torch.cuda.synchronize(dev)
+        with spd.KernelTimer(capacity=reps + 4) as kt:
+            for s in range(reps):
+                ins(s % len(kp))
+            torch.cuda.synchronize(dev)
+        assert spd.check_device_errors(ws) == 0
+        us = kt.mean_us["insert_kernel"]
+        nbytes = insert_bytes(n, H)
+        res[name] = {"tokens": n, "kernel_us_mean": round(us, 3), "algorithmic_bytes": nbytes,
+                     "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+                     "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
+    return res
 
 
 def main():
@@ -272,6 +318,10 @@ def main():
     dom_bytes = bytes_step
     dom_us = kt.mean_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    # The cache insert (run last: it rewrites the decoded tokens' rows).
+    ins = None
+    if w.sparse and not args.skip_insert:
+        ins = time_insert(spd, torch, dev, w, kp, vp, ip, min(K, 100))
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(w, args.cpu_sample)
@@ -317,6 +367,7 @@ def main():
             "kernel_us_mean": round(dom_us, 3),
             "source_digest": kernel_digest(dom),
         },
+        "insert": ins,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
         "device": torch.cuda.get_device_name(dev),

@@ -11,6 +11,8 @@
  *   2. mono_pa_decode_mxfp4: 16-query-head : 1-KV-head attention (head_dim
  *      128) over the selected tokens, or over every valid token when no
  *      selection is given.
+ * mono_sparse_decode_mxfp4 runs both in one launch; mono_insert_mxfp4
+ * writes new K, V and index-key rows into the pages.
  *
  * Sources.  Page "vllm.models.minimax_m3.amd.ops.mxfp4_pages" (module
  * docstring and mxfp4_page_views) fixes the page: 128 tokens x 64 B of e2m1
@@ -90,6 +92,7 @@ extern "C" {
 #define MONO_DEVERR_SEQ_LEN 2u     /* seq_lens[b] < T or > bt_stride*128 */
 #define MONO_DEVERR_SELECTION 4u   /* internal selection counts disagreed (a bug; output refused) */
 #define MONO_DEVERR_WAIT 8u        /* a bounded wait of one work item on another ran out (a bug) */
+#define MONO_DEVERR_SLOT 16u       /* an insert slot at or past num_pages*128 */
 
 /* Geometry of one MXFP4 page (mxfp4_pages page, module docstring). */
 #define MONO_PAGE_TOKENS 128
@@ -209,6 +212,43 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Cache insert: quantise bf16 rows to MXFP4 and write them into the pages
+ * through a slot mapping.  Page "vllm.models.minimax_m3.amd.mono.dispatch"
+ * (_slots_shared, _step_refusal): K/V and the index key are written through
+ * one int64 slot mapping with pages of 128 tokens, shared by both caches;
+ * the mxfp4_pages page names the writer and fixes the page.  Slot s is row
+ * s%128 of page s/128 of every written cache.
+ *
+ * Rounding (a reading: the pages print no rule) is the OCP Microscaling
+ * v1.0 conversion, per 32-element block: scale byte
+ * clamp(floor(log2 max|v|) - 2 + 127, 0, 254); element code = the e2m1
+ * value nearest v / 2^(byte-127), ties to the even code, magnitudes above 6
+ * saturating to 6, sign in bit 3 (-0.0 gives code 8); an all-zero block
+ * has byte 0; a block holding NaN or +-inf gets byte 0xFF and codes 0.
+ * The result is exact (integer arithmetic on the bf16 fields).
+ *
+ * k_rows_dev, v_rows_dev  bf16 [n, kv_heads, 128]; index_rows_dev bf16
+ *                  [n, 128].  Each may be NULL together with its pool, and
+ *                  that cache is not written.
+ * slots_dev        int64 [n]; a negative slot skips token t (padding).  A
+ *                  slot at or past num_pages*128 is not written and sets
+ *                  MONO_DEVERR_SLOT in *err_dev.  Non-negative slots must be
+ *                  distinct (else which row lands is unspecified).
+ * k_pages_dev, v_pages_dev  uint8 [num_pages, kv_heads, 8704];
+ * index_pages_dev  uint8 [num_pages, 8704].  Only the written rows' 64 data
+ *                  bytes and 4 scale bytes change.
+ * err_dev          uint32 device word; error bits are OR-ed into it.  The
+ *                  first word of any workspace above serves, so that
+ *                  mono_check_device_errors reads and clears it.
+ * n == 0 is a no-op.  Rows and pages need 16-byte alignment.
+ * ------------------------------------------------------------------------- */
+int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev,
+                      const uint16_t* index_rows_dev, const int64_t* slots_dev, int64_t n,
+                      int kv_heads, uint8_t* k_pages_dev, uint8_t* v_pages_dev,
+                      uint8_t* index_pages_dev, int64_t num_pages, uint32_t* err_dev,
+                      void* stream);
+
+/* ---------------------------------------------------------------------------
  * Per-kernel timing, for benchmarks and profiling only (not for graph capture).
  *
  * mono_profile_start(capacity): from now on every kernel the library launches
@@ -221,7 +261,7 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
  * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
  * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
  * ------------------------------------------------------------------------- */
-#define MONO_NUM_KERNELS 7
+#define MONO_NUM_KERNELS 8
 int mono_profile_start(int capacity);
 int mono_profile_stop(double* total_ms, int* launches, int n);
 const char* mono_kernel_name(int id);

@@ -15,11 +15,18 @@ or both in one launch:
 
     out, sel = mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages,
                                         block_table, seq_lens, k, scale, T=T)
+
+New tokens' K, V and index-key rows enter the pages through the int64 slot
+mapping (dispatch page, _slots_shared):
+
+    mono_insert_mxfp4(slots, k_rows=k, v_rows=v, index_rows=ik,
+                      k_pages=k_pages, v_pages=v_pages, index_pages=index_pages)
 """
 
 from ._binding import (  # noqa: F401
     DEVERR_PAGE_ID,
     DEVERR_SELECTION,
+    DEVERR_SLOT,
     DEVERR_SEQ_LEN,
     DEVERR_WAIT,
     EXPORTED_SYMBOLS,
@@ -34,6 +41,7 @@ from ._binding import (  # noqa: F401
     index_score_topk_workspace_bytes,
     load_library,
     mono_index_score_topk,
+    mono_insert_mxfp4,
     mono_pa_decode_mxfp4,
     mono_sparse_decode_mxfp4,
     mxfp4_page_views,

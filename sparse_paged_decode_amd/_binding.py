@@ -38,6 +38,7 @@ DEVERR_PAGE_ID = 1
 DEVERR_SEQ_LEN = 2
 DEVERR_SELECTION = 4
 DEVERR_WAIT = 8
+DEVERR_SLOT = 16
 
 EXPORTED_SYMBOLS = (
     "mono_abi_version",
@@ -52,6 +53,7 @@ EXPORTED_SYMBOLS = (
     "mono_pa_decode_mxfp4",
     "mono_sparse_decode_workspace",
     "mono_sparse_decode_mxfp4",
+    "mono_insert_mxfp4",
     "mono_check_device_errors",
     "mono_profile_start",
     "mono_profile_stop",
@@ -95,6 +97,7 @@ def load_library(path=LIB_PATH):
         "mono_pa_decode_mxfp4": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, P, P, SZ, P]),
         "mono_sparse_decode_workspace": (SZ, [I, I, I, I, I]),
         "mono_sparse_decode_mxfp4": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, SZ, P]),
+        "mono_insert_mxfp4": (I, [P, P, P, P, I64, I, P, P, P, I64, P, P]),
         "mono_check_device_errors": (I, [P, P]),
         "mono_profile_start": (I, [I]),
         "mono_profile_stop": (I, [P, P, I]),
@@ -421,6 +424,48 @@ def mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages, block_ta
         _ptr(block_table), bt_stride, _ptr(seq_lens), B, T, k, ctypes.c_float(float(scale)),
         _ptr(selected_idx), _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return out, selected_idx
+
+
+def mono_insert_mxfp4(slots, *, k_rows=None, v_rows=None, index_rows=None, k_pages=None, v_pages=None,
+                      index_pages=None, workspace=None):
+    """Quantise bf16 rows to MXFP4 and write them into the pages through ``slots``.
+
+    ``slots``: int64 ``[n]``, slot s = row s % 128 of page s // 128; negative
+    slots are skipped.  ``k_rows``/``v_rows``: bf16 ``[n, H, 128]`` into
+    ``k_pages``/``v_pages`` ``[pages, H, 8704]``; ``index_rows``: bf16
+    ``[n, 128]`` into ``index_pages`` ``[pages, 8704]``.  Any cache may be
+    left out (rows and pages both None).  A slot past the pools sets
+    ``DEVERR_SLOT`` in the workspace's error word; the workspace used is
+    returned, for :func:`check_device_errors`.
+    """
+    lib = load_library()
+    _need(slots.dtype == torch.int64 and slots.dim() == 1 and slots.is_contiguous(), "slots must be int64 [n]")
+    n = slots.shape[0]
+    pairs = ((k_rows, k_pages, "k", 3), (v_rows, v_pages, "v", 3), (index_rows, index_pages, "index", 2))
+    given = [(r, p) for r, p, _, _ in pairs if r is not None or p is not None]
+    _need(len(given) > 0, "no cache to write")
+    H = 0
+    num_pages = None
+    for rows, pages, name, ndim in pairs:
+        if rows is None and pages is None:
+            continue
+        _need(rows is not None and pages is not None, f"{name}_rows and {name}_pages go together")
+        _check_pages(pages, f"{name}_pages", ndim)
+        _need(rows.dtype == torch.bfloat16 and rows.is_contiguous(), f"{name}_rows must be contiguous bf16")
+        heads = pages.shape[1] if ndim == 3 else 1
+        want = (n, heads, HEAD_DIM) if ndim == 3 else (n, HEAD_DIM)
+        _need(tuple(rows.shape) == want, f"{name}_rows must be {want}, got {tuple(rows.shape)}")
+        if ndim == 3:
+            _need(H in (0, heads), "k_pages and v_pages must have the same number of heads")
+            H = heads
+        _need(num_pages in (None, pages.shape[0]), "every pool must have the same page count")
+        num_pages = pages.shape[0]
+    dev = _on_gpu(slots, *[t for pair in given for t in pair])
+    ws = _workspace(workspace, dev, 256, "insert")
+    _check(lib.mono_insert_mxfp4(
+        _ptr(k_rows), _ptr(v_rows), _ptr(index_rows), _ptr(slots), n, H, _ptr(k_pages), _ptr(v_pages),
+        _ptr(index_pages), num_pages, _ptr(ws.buf), _stream(dev)))
+    return ws
 
 
 # --- per-kernel timing ---------------------------------------------------------------

@@ -44,7 +44,7 @@ Profiler g_prof;
 // The step kernel is one kernel; it is timed under the name of the call.
 const char* const kKernelNames[kNumKernels] = {"pack_kernel",         "unpack_kernel",     "dequant_f32_kernel",
                                                "dequant_bf16_kernel", "index_topk_kernel", "pa_decode_kernel",
-                                               "sparse_decode_kernel"};
+                                               "sparse_decode_kernel", "insert_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -261,6 +261,35 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
   a.out = out_dev;
   a.ws = static_cast<uint8_t*>(ws_dev);
   return launch_step(a, lay, (hipStream_t)stream, "mono_sparse_decode_mxfp4");
+}
+
+int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev, const uint16_t* index_rows_dev,
+                      const int64_t* slots_dev, int64_t n, int kv_heads, uint8_t* k_pages_dev, uint8_t* v_pages_dev,
+                      uint8_t* index_pages_dev, int64_t num_pages, uint32_t* err_dev, void* stream) {
+  clear_error();
+  if (n < 0) return set_error(MONO_EINVAL, "mono_insert_mxfp4: n < 0");
+  if (num_pages < 1 || num_pages > ((int64_t)1 << 34))
+    return set_error(MONO_EINVAL, "mono_insert_mxfp4: num_pages out of range");
+  if ((k_rows_dev == nullptr) != (k_pages_dev == nullptr) || (v_rows_dev == nullptr) != (v_pages_dev == nullptr) ||
+      (index_rows_dev == nullptr) != (index_pages_dev == nullptr))
+    return set_error(MONO_EINVAL, "mono_insert_mxfp4: rows and pages of a cache must be both given or both NULL");
+  const bool kv = k_rows_dev || v_rows_dev;
+  if (kv && (kv_heads < 1 || kv_heads > kMaxHeads))
+    return set_error(MONO_ENOTSUP, "mono_insert_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads, kv_heads);
+  if (!slots_dev || !err_dev) return set_error(MONO_EINVAL, "mono_insert_mxfp4: NULL slots or err");
+  const void* bufs16[6] = {k_rows_dev, v_rows_dev, index_rows_dev, k_pages_dev, v_pages_dev, index_pages_dev};
+  for (const void* b : bufs16)
+    if (b && !aligned(b, 16)) return set_error(MONO_EINVAL, "mono_insert_mxfp4: rows and pages need 16-byte alignment");
+  if (!aligned(slots_dev, 8) || !aligned(err_dev, 4))
+    return set_error(MONO_EINVAL, "mono_insert_mxfp4: slots need 8-byte and err 4-byte alignment");
+  const int row_heads[3] = {k_rows_dev ? kv_heads : 0, v_rows_dev ? kv_heads : 0, index_rows_dev ? 1 : 0};
+  const int64_t rows_per_token = row_heads[0] + row_heads[1] + row_heads[2];
+  if (n * rows_per_token * 4 >= ((int64_t)1 << 31))
+    return set_error(MONO_EINVAL, "mono_insert_mxfp4: n x rows per token too large");
+  if (n == 0 || rows_per_token == 0) return MONO_OK;
+  const uint16_t* const rows[3] = {k_rows_dev, v_rows_dev, index_rows_dev};
+  uint8_t* const pools[3] = {k_pages_dev, v_pages_dev, index_pages_dev};
+  return launch_insert(rows, pools, row_heads, slots_dev, n, num_pages, err_dev, (hipStream_t)stream);
 }
 
 int mono_profile_start(int capacity) {

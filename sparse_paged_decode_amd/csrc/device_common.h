@@ -14,6 +14,7 @@ namespace mono {
 constexpr int kPageTokens = 128;
 constexpr int kHeadDim = 128;
 constexpr int kRowBytes = 64;        // packed e2m1 bytes per row
+constexpr int kScaleBlock = 32;      // elements per e8m0 scale
 constexpr int kScaleOffset = 8192;   // 128 rows x 64 B
 constexpr int kPageBytes = 8704;     // + 128 rows x 4 B
 constexpr int kQHeads = 16;          // query heads per KV head
@@ -23,6 +24,7 @@ constexpr uint32_t kErrPageId = 1u;
 constexpr uint32_t kErrSeqLen = 2u;
 constexpr uint32_t kErrSelection = 4u;  // selection counts inconsistent (never expected)
 constexpr uint32_t kErrWait = 8u;       // a bounded wait for another work item ran out
+constexpr uint32_t kErrSlot = 16u;      // an insert slot past the pool
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -14,7 +14,17 @@ namespace mono {
 int check_launch(const char* what);
 
 // Kernel ids of the optional per-kernel event timing (mono_profile_*).
-enum KernelId { kKPack = 0, kKUnpack, kKDequant, kKDequantBf16, kKIndexScan, kKPaDecode, kKStep, kNumKernels };
+enum KernelId {
+  kKPack = 0,
+  kKUnpack,
+  kKDequant,
+  kKDequantBf16,
+  kKIndexScan,
+  kKPaDecode,
+  kKStep,
+  kKInsert,
+  kNumKernels
+};
 // When timing is on, takes the next pair of timing events for kernel `id`
 // and returns true; the launch then records them as part of its dispatch.
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop);
@@ -39,6 +49,11 @@ int launch_unpack(const uint8_t* pages, uint8_t* codes, uint8_t* scales, int64_t
                   hipStream_t stream);
 int launch_dequant_f32(const uint8_t* pages, float* out, int64_t n_pages, hipStream_t stream);
 int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
+// Cache insert: caches c = 0 (K), 1 (V), 2 (index key) with row_heads[c]
+// rows per token (0 = not written); rows[c] bf16 [n, row_heads[c], 128],
+// pools[c] [num_pages, row_heads[c], 8704].
+int launch_insert(const uint16_t* const rows[3], uint8_t* const pools[3], const int row_heads[3],
+                  const int64_t* slots, int64_t n, int64_t num_pages, uint32_t* err, hipStream_t stream);
 
 // ---- the persistent step kernel (step.hip) -----------------------------------
 enum StepMode { kModeIndex = 1, kModeAttn = 2, kModeFused = 3 };

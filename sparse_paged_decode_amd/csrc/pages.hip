@@ -118,6 +118,104 @@ __global__ __launch_bounds__(256) void dequant_bf16_kernel(const uint8_t* __rest
   for (int w = 0; w < 4; ++w) dst[w] = dequant8_bf16(d[w], scale);
 }
 
+// ---- the cache insert ---------------------------------------------------------
+// Rounding rule (OCP Microscaling v1.0 conversion; the pages name the writer
+// but not its rule): per 32-element block the scale byte is
+// floor(log2 max|v|) - 2 + 127 clamped to [0, 254]; each element goes to the
+// nearest e2m1 magnitude of v / 2^(byte-127), ties to the even code, above
+// 6 saturating; NaN or +-inf anywhere gives byte 0xFF and codes 0; an
+// all-zero block gives byte 0.
+//
+// All of it is integer arithmetic on the bf16 fields, so it is exact and
+// independent of the denormal mode.  A bf16 magnitude with exponent field E
+// and mantissa M is mant * 2^ex with mant = 128 + M, ex = E - 134 (E > 0) or
+// mant = M, ex = -133 (E = 0).  With 4q = 4|v| / 2^(byte-127) = mant * 2^-n,
+// n = byte - 129 - ex, the rounding thresholds of q (0.25, 0.75, 1.25, 1.75,
+// 2.5, 3.5, 5; strict where the lower code is even so that ties go to it)
+// become mant against k << n for k = 1, 3, 5, 7, 10, 14, 20.  The largest
+// element of a block has n = 3 (n = 4 when the byte is clamped at 0), the
+// others larger n; n above 12 puts every threshold above any mant < 256.
+__device__ __forceinline__ uint32_t e2m1_code_of(uint32_t mag, int byte) {
+  const uint32_t E = mag >> 7;
+  const uint32_t mant = E ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
+  const int ex = E ? (int)E - 134 : -133;
+  const int n = min(byte - 129 - ex, 12);
+  return (uint32_t)(mant > (1u << n)) + (uint32_t)(mant >= (3u << n)) + (uint32_t)(mant > (5u << n)) +
+         (uint32_t)(mant >= (7u << n)) + (uint32_t)(mant > (10u << n)) + (uint32_t)(mant >= (14u << n)) +
+         (uint32_t)(mant > (20u << n));
+}
+
+struct InsertArgs {
+  const uint16_t* rows[3];  // K [n, heads, 128], V [n, heads, 128], index key [n, 128] (bf16 bits)
+  uint8_t* pools[3];        // [num_pages, heads, 8704] x 2, [num_pages, 8704]
+  int row_heads[3];         // rows per token of each cache (0: not written)
+  const int64_t* slots;     // [n]
+  int64_t n_threads;        // n * rows_per_token * 4
+  int rows_per_token;
+  int64_t num_pages;
+  uint32_t* err;
+};
+
+// One thread per (token, cache row, 32-element block): reads the block's
+// 64 B of bf16, writes its 16 B of packed e2m1 and its scale byte.  The four
+// threads of a row are adjacent lanes, so a row is one 256-B read and one
+// 64-B write.
+__global__ __launch_bounds__(256) void insert_kernel(InsertArgs a) {
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid >= a.n_threads) return;
+  const int blk = (int)(tid & 3);
+  const int64_t row = tid >> 2;
+  const int64_t t = row / a.rows_per_token;
+  int j = (int)(row % a.rows_per_token);
+  int c = 0;
+  while (j >= a.row_heads[c]) j -= a.row_heads[c++];  // cache c, head j
+  const int64_t slot = a.slots[t];
+  if (slot < 0) return;
+  const int64_t page = slot >> 7;
+  if (page >= a.num_pages) {
+    if (blk == 0) raise_error(a.err, kErrSlot);
+    return;
+  }
+  const int heads = a.row_heads[c];
+  const u32x4_t* src =
+      reinterpret_cast<const u32x4_t*>(a.rows[c] + (t * heads + j) * kHeadDim + blk * kScaleBlock);
+  u32x4_t in[4];
+#pragma unroll
+  for (int L = 0; L < 4; ++L) in[L] = src[L];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int L = 0; L < 4; ++L)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) amax = max(amax, max(in[L][d] & 0x7FFFu, (in[L][d] >> 16) & 0x7FFFu));
+  int byte;
+  if (amax >= 0x7F80u) {
+    byte = 0xFF;
+  } else if (amax == 0) {
+    byte = 0;
+  } else {
+    const uint32_t E = amax >> 7;
+    const int flog2 = E ? (int)E - 127 : -133 + (31 - (int)__builtin_clz(amax & 0x7Fu));
+    byte = min(max(flog2 - 2 + 127, 0), 254);
+  }
+  u32x4_t out;
+#pragma unroll
+  for (int L = 0; L < 4; ++L) {  // bf16 elements 8L..8L+7 -> codes in nibbles of word L
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (in[L][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+      uint32_t code = e2m1_code_of(h & 0x7FFFu, byte) | ((h >> 12) & 8u);
+      if (byte == 0xFF) code = 0;
+      w |= code << (4 * i);
+    }
+    out[L] = w;
+  }
+  const int r = (int)(slot & (kPageTokens - 1));
+  uint8_t* pg = a.pools[c] + (page * heads + j) * kPageBytes;
+  *reinterpret_cast<u32x4_t*>(pg + r * kRowBytes + 16 * blk) = out;
+  pg[kScaleOffset + r * 4 + blk] = (uint8_t)byte;
+}
+
 inline unsigned grid_for(int64_t n, int block) { return (unsigned)((n + block - 1) / block); }
 
 }  // namespace
@@ -150,6 +248,24 @@ int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hi
   MONO_LAUNCH(kKDequantBf16, dequant_bf16_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
                      out, n_blocks);
   return check_launch("mxfp4_pages_dequant_bf16");
+}
+
+int launch_insert(const uint16_t* const rows[3], uint8_t* const pools[3], const int row_heads[3],
+                  const int64_t* slots, int64_t n, int64_t num_pages, uint32_t* err, hipStream_t stream) {
+  InsertArgs a{};
+  a.rows_per_token = 0;
+  for (int c = 0; c < 3; ++c) {
+    a.rows[c] = rows[c];
+    a.pools[c] = pools[c];
+    a.row_heads[c] = row_heads[c];
+    a.rows_per_token += row_heads[c];
+  }
+  a.slots = slots;
+  a.n_threads = n * a.rows_per_token * 4;
+  a.num_pages = num_pages;
+  a.err = err;
+  MONO_LAUNCH(kKInsert, insert_kernel, dim3(grid_for(a.n_threads, 256)), dim3(256), 0, stream, a);
+  return check_launch("mono_insert_mxfp4");
 }
 
 }  // namespace mono

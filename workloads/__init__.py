@@ -149,3 +149,54 @@ def workload(number, seed=None, **overrides):
     name, kw = WORKLOADS[number]
     kw = {**kw, **overrides}
     return make_workload(name, seed=1000 + number if seed is None else seed, **kw)
+
+
+# --- new rows for the cache insert ------------------------------------------------
+#
+# Recipe (``numpy.random.default_rng(seed)``, in this order): for each of K
+# ([n, heads, 128]), V ([n, heads, 128]) and the index key ([n, 128]),
+# standard-normal float32 rows times 2**u with u uniform in [-6, 6] per row,
+# rounded to bfloat16.  With ``specials``, every 32-element block then has,
+# with probability 0.02 each, all its elements set to +0.0, all to -0.0, or
+# its elements scaled by 2**-130 (bfloat16 subnormals), and each element with
+# probability 0.002 is set to +-inf or NaN, and 0.002 to -0.0.
+def _special_blocks(rng, x):
+    blocks = x.reshape(-1, 32)
+    r = rng.random(blocks.shape[0])
+    blocks[r < 0.02] = 0.0
+    blocks[(r >= 0.02) & (r < 0.04)] = -0.0
+    tiny = (r >= 0.04) & (r < 0.06)
+    blocks[tiny] *= np.float32(2.0**-130)
+    e = rng.random(blocks.shape)
+    blocks[e < 0.001] = np.inf
+    blocks[(e >= 0.001) & (e < 0.0015)] = -np.inf
+    blocks[(e >= 0.0015) & (e < 0.002)] = np.nan
+    blocks[(e >= 0.002) & (e < 0.004)] = -0.0
+    return blocks.reshape(x.shape)
+
+
+def new_rows(seed, n, heads, *, specials=False):
+    """bf16 bit patterns of new K, V ([n, heads, 128]) and index-key ([n, 128]) rows."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for name, shape in (("k", (n, heads, HEAD_DIM)), ("v", (n, heads, HEAD_DIM)), ("index", (n, HEAD_DIM))):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        x *= np.exp2(rng.uniform(-6, 6, size=shape[:-1] + (1,))).astype(np.float32)
+        if specials:
+            x = _special_blocks(rng, x)
+        out[name] = _bf16_bits(x)
+    return out
+
+
+def decode_slots(w):
+    """int64 slots of the T tokens being decoded of each request (flat b*T + t).
+
+    Token j of request b is row j % 128 of page block_table[b, j // 128], so
+    its slot (page * 128 + row) is block_table[b, j // 128] * 128 + j % 128.
+    """
+    slots = np.empty(w.B * w.T, dtype=np.int64)
+    for b in range(w.B):
+        for t in range(w.T):
+            j = int(w.seq_lens[b]) - w.T + t
+            slots[b * w.T + t] = int(w.block_table[b, j // _TOKENS_PER_PAGE]) * _TOKENS_PER_PAGE + j % _TOKENS_PER_PAGE
+    return slots
