@@ -149,39 +149,41 @@ struct InsertArgs {
   const uint16_t* rows[3];  // K [n, heads, 128], V [n, heads, 128], index key [n, 128] (bf16 bits)
   uint8_t* pools[3];        // [num_pages, heads, 8704] x 2, [num_pages, 8704]
   int row_heads[3];         // rows per token of each cache (0: not written)
+  int64_t row_end[3];       // running sums of n * row_heads: cache c owns rows [row_end[c-1], row_end[c])
   const int64_t* slots;     // [n]
-  int64_t n_threads;        // n * rows_per_token * 4
-  int rows_per_token;
+  int64_t n_threads;        // 4 * row_end[2]
   int64_t num_pages;
   uint32_t* err;
 };
 
-// One thread per (token, cache row, 32-element block): reads the block's
-// 64 B of bf16, writes its 16 B of packed e2m1 and its scale byte.  The four
-// threads of a row are adjacent lanes, so a row is one 256-B read and one
-// 64-B write.
+// One thread per (cache row, 32-element block): reads the block's 64 B of
+// bf16, writes its 16 B of packed e2m1 and its scale byte.  Rows are ordered
+// cache-major, then token, then head, so the four threads of a row are
+// adjacent lanes and a wave covers consecutive rows of one cache: its reads,
+// its data writes and its scale writes are each contiguous runs when the
+// slots are consecutive.
 __global__ __launch_bounds__(256) void insert_kernel(InsertArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (tid >= a.n_threads) return;
   const int blk = (int)(tid & 3);
   const int64_t row = tid >> 2;
-  const int64_t t = row / a.rows_per_token;
-  int j = (int)(row % a.rows_per_token);
-  int c = 0;
-  while (j >= a.row_heads[c]) j -= a.row_heads[c++];  // cache c, head j
+  const int c = (row >= a.row_end[0]) + (row >= a.row_end[1]);
+  const int64_t local = row - (c ? a.row_end[c - 1] : 0);  // = t * heads + j
+  const int heads = a.row_heads[c];
+  const int64_t t = local / heads;
+  const int j = (int)(local - t * heads);
+  // The row is loaded before the slot is looked at, so the two loads overlap.
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.rows[c] + local * kHeadDim + blk * kScaleBlock);
+  u32x4_t in[4];
+#pragma unroll
+  for (int L = 0; L < 4; ++L) in[L] = src[L];
   const int64_t slot = a.slots[t];
   if (slot < 0) return;
   const int64_t page = slot >> 7;
   if (page >= a.num_pages) {
-    if (blk == 0) raise_error(a.err, kErrSlot);
+    if (blk == 0 && j == 0) raise_error(a.err, kErrSlot);
     return;
   }
-  const int heads = a.row_heads[c];
-  const u32x4_t* src =
-      reinterpret_cast<const u32x4_t*>(a.rows[c] + (t * heads + j) * kHeadDim + blk * kScaleBlock);
-  u32x4_t in[4];
-#pragma unroll
-  for (int L = 0; L < 4; ++L) in[L] = src[L];
   uint32_t amax = 0;
 #pragma unroll
   for (int L = 0; L < 4; ++L)
@@ -253,15 +255,16 @@ int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hi
 int launch_insert(const uint16_t* const rows[3], uint8_t* const pools[3], const int row_heads[3],
                   const int64_t* slots, int64_t n, int64_t num_pages, uint32_t* err, hipStream_t stream) {
   InsertArgs a{};
-  a.rows_per_token = 0;
+  int64_t end = 0;
   for (int c = 0; c < 3; ++c) {
     a.rows[c] = rows[c];
     a.pools[c] = pools[c];
     a.row_heads[c] = row_heads[c];
-    a.rows_per_token += row_heads[c];
+    end += n * row_heads[c];
+    a.row_end[c] = end;
   }
   a.slots = slots;
-  a.n_threads = n * a.rows_per_token * 4;
+  a.n_threads = 4 * end;
   a.num_pages = num_pages;
   a.err = err;
   MONO_LAUNCH(kKInsert, insert_kernel, dim3(grid_for(a.n_threads, 256)), dim3(256), 0, stream, a);
