@@ -23,6 +23,9 @@ Sources and readings (each function repeats the one it relies on):
 * Top-k.  Per query token, the k highest-scoring valid tokens; ties go to
   the lower token index; with fewer than k valid tokens, all of them.  A NaN
   score ranks below every number.
+* Cache formats.  MXFP4 pages (8704 B, ``oracle.mxfp4``) or the older
+  build's fp8 pages (16384 B, ``oracle.fp8``), told apart by the page size;
+  with fp8, K and V values carry the per-tensor ``k_scale`` / ``v_scale``.
 * Attention.  Per query token: ``z_hj = scale * q_h . k_j`` over the
   candidate tokens (the selected ones, or every valid one when there is no
   selection), ``p = softmax_j(z)`` and ``o_h = sum_j p_hj v_j``.  All 16
@@ -34,7 +37,7 @@ All arithmetic is float64.
 
 import numpy as np
 
-from . import mxfp4
+from . import fp8, mxfp4
 
 Q_HEADS = 16  # query heads per KV head
 HEAD_DIM = 128
@@ -54,16 +57,24 @@ def query_positions(seq_lens, T):
 def sequence_rows(pool, bt_row, n_tokens, head=None):
     """Exact dequantised rows ``[n_tokens, 128]`` of tokens 0..n_tokens-1.
 
-    ``pool`` is ``[P, 8704]`` (index key) or ``[P, H, 8704]`` with ``head``
-    picking the KV head.  Token j comes from page ``bt_row[j // 128]``, row
-    ``j % 128``.
+    ``pool`` is ``[P, page]`` (index key) or ``[P, H, page]`` with ``head``
+    picking the KV head; a page of 8704 bytes is MXFP4, of 16384 bytes fp8
+    (without its tensor scale).  Token j comes from page ``bt_row[j // 128]``,
+    row ``j % 128``.
     """
     if n_tokens <= 0:
         return np.zeros((0, HEAD_DIM))
+    page_bytes = pool.shape[-1]
+    if page_bytes == mxfp4.PAGE_BYTES:
+        dequant = mxfp4.dequant
+    elif page_bytes == fp8.PAGE_BYTES:
+        dequant = fp8.dequant
+    else:
+        raise ValueError(f"unknown page size {page_bytes}")
     n_pages = -(-n_tokens // mxfp4.PAGE_TOKENS)
     page_ids = np.asarray(bt_row[:n_pages], dtype=np.int64)
     pages = pool[page_ids] if head is None else pool[page_ids, head]
-    rows = mxfp4.dequant(pages).reshape(n_pages * mxfp4.PAGE_TOKENS, HEAD_DIM)
+    rows = dequant(pages).reshape(n_pages * mxfp4.PAGE_TOKENS, HEAD_DIM)
     return rows[:n_tokens]
 
 
@@ -129,20 +140,25 @@ def attend(q_bits, k_rows, v_rows, scale):
     return p @ v_rows
 
 
-def decode_one(q_bits, k_pool, v_pool, bt_row, pos, scale, selected_row=None, head=0):
-    """Attention output ``[16, 128]`` for one query token."""
+def decode_one(q_bits, k_pool, v_pool, bt_row, pos, scale, selected_row=None, head=0, k_scale=1.0, v_scale=1.0):
+    """Attention output ``[16, 128]`` for one query token.
+
+    ``k_scale`` / ``v_scale`` multiply every K / V value (the fp8 caches'
+    per-tensor scales; 1 for MXFP4).  The products are exact in float64.
+    """
     cand = candidates(pos, selected_row)
     n_seen = int(cand.max()) + 1 if cand.size else 0
-    k_all = sequence_rows(k_pool, bt_row, n_seen, head)
-    v_all = sequence_rows(v_pool, bt_row, n_seen, head)
+    k_all = sequence_rows(k_pool, bt_row, n_seen, head) * float(k_scale)
+    v_all = sequence_rows(v_pool, bt_row, n_seen, head) * float(v_scale)
     return attend(q_bits, k_all[cand], v_all[cand], scale)
 
 
-def pa_decode(q_bits, k_pool, v_pool, block_table, seq_lens, T, scale, selected=None, head=0):
+def pa_decode(q_bits, k_pool, v_pool, block_table, seq_lens, T, scale, selected=None, head=0, k_scale=1.0,
+              v_scale=1.0):
     """Attention for every query token: float64 ``[B*T, 16, 128]``."""
     pos = query_positions(seq_lens, T)
     out = np.zeros((pos.shape[0], q_bits.shape[1], HEAD_DIM))
     for i, p in enumerate(pos):
         row = None if selected is None else selected[i]
-        out[i] = decode_one(q_bits[i], k_pool, v_pool, block_table[i // T], p, scale, row, head)
+        out[i] = decode_one(q_bits[i], k_pool, v_pool, block_table[i // T], p, scale, row, head, k_scale, v_scale)
     return out
