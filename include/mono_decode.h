@@ -12,7 +12,8 @@
  *      128) over the selected tokens, or over every valid token when no
  *      selection is given.
  * mono_sparse_decode_mxfp4 runs both in one launch; mono_insert_mxfp4
- * writes new K, V and index-key rows into the pages.
+ * writes new K, V and index-key rows into the pages.  The *_fp8 calls run
+ * the same step over the older build's fp8 caches.
  *
  * Sources.  Page "vllm.models.minimax_m3.amd.ops.mxfp4_pages" (module
  * docstring and mxfp4_page_views) fixes the page: 128 tokens x 64 B of e2m1
@@ -212,6 +213,54 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * The same step over fp8 caches (the older build's format: page
+ * "vllm.models.minimax_m3.amd.mono.weights", SparseMoeLayer, names an fp8
+ * index cache [blocks, block, head_dim] with shared block ids and the KV
+ * cache scales the layer's attention holds; page
+ * "vllm.models.minimax_m3.amd.mono.dispatch", _config_refusal, requires fp8
+ * KV and index caches).
+ *
+ * Readings where the pages only say "fp8":
+ *   - elements are OCP FP8 E4M3 (e4m3fn): bias 7, no infinities, 0x7F and
+ *     0xFF are NaN, largest value 448;
+ *   - a page is 128 tokens x 128 elements, one byte each, row-major (element
+ *     i of token row r at byte 128*r + i): MONO_FP8_PAGE_BYTES = 16384;
+ *     K/V pools are [num_pages, kv_heads, 16384], the index pool
+ *     [num_pages, 16384];
+ *   - K and V each carry one fp32 tensor scale: a K element is
+ *     e4m3 * k_scale, a V element e4m3 * v_scale.  The index cache has no
+ *     scale (its scores are plain dot products with the e4m3 values).
+ *
+ * Every argument, rule and error is that of the MXFP4 call of the same name
+ * (the workspace functions above serve both), except that the pools are fp8
+ * and the attention calls take k_scale and v_scale (finite, > 0), which
+ * multiply the logits and the output.  fp8_pages_dequant_bf16 converts
+ * whole pages [n_pages, 16384] to bf16 [n_pages, 128, 128] through the
+ * kernels' own conversion (exact: every e4m3 value is a bf16 value).
+ * ------------------------------------------------------------------------- */
+#define MONO_FP8_PAGE_BYTES 16384
+int mono_index_score_topk_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                              int64_t num_pages, const int32_t* block_table_dev, int bt_stride,
+                              const int32_t* seq_lens_dev, int B, int T, int k,
+                              int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
+                              size_t ws_bytes, void* stream);
+int mono_pa_decode_fp8(const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                       const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                       const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
+                       int B, int T, const int32_t* selected_idx_dev, int k, float scale,
+                       float k_scale, float v_scale, uint16_t* out_dev, void* ws_dev,
+                       size_t ws_bytes, void* stream);
+int mono_sparse_decode_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                           const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                           const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                           const int32_t* block_table_dev, int bt_stride,
+                           const int32_t* seq_lens_dev, int B, int T, int k, float scale,
+                           float k_scale, float v_scale, int32_t* selected_idx_dev,
+                           uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream);
+int fp8_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
  * Cache insert: quantise bf16 rows to MXFP4 and write them into the pages
  * through a slot mapping.  Page "vllm.models.minimax_m3.amd.mono.dispatch"
  * (_slots_shared, _step_refusal): K/V and the index key are written through
@@ -261,7 +310,7 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev,
  * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
  * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
  * ------------------------------------------------------------------------- */
-#define MONO_NUM_KERNELS 8
+#define MONO_NUM_KERNELS 12
 int mono_profile_start(int capacity);
 int mono_profile_stop(double* total_ms, int* launches, int n);
 const char* mono_kernel_name(int id);

@@ -16,6 +16,9 @@ or both in one launch:
     out, sel = mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages,
                                         block_table, seq_lens, k, scale, T=T)
 
+The same step over the older build's fp8 (e4m3) caches, with per-tensor K/V
+scales: mono_index_score_topk_fp8, mono_pa_decode_fp8, mono_sparse_decode_fp8.
+
 New tokens' K, V and index-key rows enter the pages through the int64 slot
 mapping (dispatch page, _slots_shared):
 
@@ -30,6 +33,7 @@ from ._binding import (  # noqa: F401
     DEVERR_SEQ_LEN,
     DEVERR_WAIT,
     EXPORTED_SYMBOLS,
+    FP8_PAGE_BYTES,
     HEAD_DIM,
     KernelTimer,
     PAGE_BYTES,
@@ -38,11 +42,15 @@ from ._binding import (  # noqa: F401
     MonoError,
     Workspace,
     check_device_errors,
+    fp8_pages_dequant_bf16,
     index_score_topk_workspace_bytes,
     load_library,
     mono_index_score_topk,
+    mono_index_score_topk_fp8,
     mono_insert_mxfp4,
+    mono_pa_decode_fp8,
     mono_pa_decode_mxfp4,
+    mono_sparse_decode_fp8,
     mono_sparse_decode_mxfp4,
     mxfp4_page_views,
     mxfp4_pages_dequant,

@@ -26,6 +26,7 @@ HEAD_DIM = 128
 DATA_BYTES = 64
 SCALE_BYTES = 4
 PAGE_BYTES = PAGE_TOKENS * (DATA_BYTES + SCALE_BYTES)  # 8704
+FP8_PAGE_BYTES = PAGE_TOKENS * HEAD_DIM  # 16384: the older build's fp8 (e4m3) pages
 Q_HEADS_PER_KV = 16
 
 MONO_OK = 0
@@ -54,6 +55,10 @@ EXPORTED_SYMBOLS = (
     "mono_sparse_decode_workspace",
     "mono_sparse_decode_mxfp4",
     "mono_insert_mxfp4",
+    "mono_index_score_topk_fp8",
+    "mono_pa_decode_fp8",
+    "mono_sparse_decode_fp8",
+    "fp8_pages_dequant_bf16",
     "mono_check_device_errors",
     "mono_profile_start",
     "mono_profile_stop",
@@ -98,6 +103,10 @@ def load_library(path=LIB_PATH):
         "mono_sparse_decode_workspace": (SZ, [I, I, I, I, I]),
         "mono_sparse_decode_mxfp4": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, SZ, P]),
         "mono_insert_mxfp4": (I, [P, P, P, P, I64, I, P, P, P, I64, P, P]),
+        "mono_index_score_topk_fp8": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
+        "mono_pa_decode_fp8": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, F, F, P, P, SZ, P]),
+        "mono_sparse_decode_fp8": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, F, F, P, P, P, SZ, P]),
+        "fp8_pages_dequant_bf16": (I, [P, P, I64, P]),
         "mono_check_device_errors": (I, [P, P]),
         "mono_profile_start": (I, [I]),
         "mono_profile_stop": (I, [P, P, I]),
@@ -163,9 +172,10 @@ def mxfp4_page_views(pages):
     return data, scale
 
 
-def _check_pages(pages, name, ndim):
+def _check_pages(pages, name, ndim, page_bytes=None):
+    page_bytes = PAGE_BYTES if page_bytes is None else page_bytes
     _need(pages.dtype == torch.uint8, f"{name} must be uint8, got {pages.dtype}")
-    _need(pages.dim() == ndim and pages.shape[-1] == PAGE_BYTES, f"{name} must be [{'..., ' * (ndim - 1)}{PAGE_BYTES}]")
+    _need(pages.dim() == ndim and pages.shape[-1] == page_bytes, f"{name} must be [{'..., ' * (ndim - 1)}{page_bytes}]")
     _need(pages.is_contiguous(), f"{name} must be contiguous")
 
 
@@ -217,6 +227,16 @@ def mxfp4_pages_dequant_bf16(pages):
     dev = _on_gpu(pages)
     out = torch.empty((pages.shape[0], 128, 128), dtype=torch.bfloat16, device=dev)
     _check(_lib.mxfp4_pages_dequant_bf16(_ptr(pages), _ptr(out), pages.shape[0], _stream(dev)))
+    return out
+
+
+def fp8_pages_dequant_bf16(pages):
+    """fp8 pages ``[n, 16384]`` -> bf16 values ``[n, 128, 128]`` via the kernels' conversion."""
+    load_library()
+    _check_pages(pages, "pages", 2, FP8_PAGE_BYTES)
+    dev = _on_gpu(pages)
+    out = torch.empty((pages.shape[0], 128, 128), dtype=torch.bfloat16, device=dev)
+    _check(_lib.fp8_pages_dequant_bf16(_ptr(pages), _ptr(out), pages.shape[0], _stream(dev)))
     return out
 
 
@@ -307,11 +327,25 @@ def mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, *, T=1
     Returns int32 ``[B*T, k]`` (any order within a row, -1 padding), and the
     fp32 scores of the selected tokens too if ``return_scores``.
     """
+    return _index_topk("mxfp4", index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores,
+                       workspace)
+
+
+def mono_index_score_topk_fp8(index_q, index_pages, block_table, seq_lens, k, *, T=1, out=None,
+                              out_scores=None, return_scores=False, workspace=None):
+    """:func:`mono_index_score_topk` over an fp8 (e4m3) index pool ``[P, 16384]``."""
+    return _index_topk("fp8", index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores,
+                       workspace)
+
+
+def _index_topk(fmt, index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores, workspace):
     lib = load_library()
+    page_bytes, fn = (PAGE_BYTES, lib.mono_index_score_topk) if fmt == "mxfp4" else \
+        (FP8_PAGE_BYTES, lib.mono_index_score_topk_fp8)
     _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM,
           "index_q must be bf16 [B*T, 128]")
     _need(index_q.is_contiguous(), "index_q must be contiguous")
-    _check_pages(index_pages, "index_pages", 2)
+    _check_pages(index_pages, "index_pages", 2, page_bytes)
     N = index_q.shape[0]
     B = _check_tables(block_table, seq_lens, N, T)
     dev = _on_gpu(index_q, index_pages, block_table, seq_lens)
@@ -329,7 +363,7 @@ def mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, *, T=1
     nbytes = lib.mono_index_score_topk_workspace(B, T, bt_stride, k)
     _need(nbytes > 0, "invalid shape for mono_index_score_topk")
     ws = _workspace(workspace, dev, nbytes, "topk")
-    _check(lib.mono_index_score_topk(
+    _check(fn(
         _ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table), bt_stride,
         _ptr(seq_lens), B, T, k, _ptr(out), _ptr(out_scores), _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return (out, out_scores) if return_scores else out
@@ -344,11 +378,28 @@ def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_id
     int32 ``[B*T, k]`` (entries < 0 or past the position are skipped).
     Returns bf16 ``[B*T, 16*H, 128]``.
     """
+    return _pa_decode("mxfp4", q, k_pages, v_pages, block_table, seq_lens, selected_idx, scale, 1.0, 1.0, T, out,
+                      workspace)
+
+
+def mono_pa_decode_fp8(q, k_pages, v_pages, block_table, seq_lens, selected_idx=None,
+                       scale=1.0 / math.sqrt(HEAD_DIM), k_scale=1.0, v_scale=1.0, *, T=1, out=None, workspace=None):
+    """:func:`mono_pa_decode_mxfp4` over fp8 (e4m3) K/V pools ``[P, H, 16384]``.
+
+    K values are e4m3 * ``k_scale`` and V values e4m3 * ``v_scale``.
+    """
+    return _pa_decode("fp8", q, k_pages, v_pages, block_table, seq_lens, selected_idx, scale, k_scale, v_scale, T,
+                      out, workspace)
+
+
+def _pa_decode(fmt, q, k_pages, v_pages, block_table, seq_lens, selected_idx, scale, k_scale, v_scale, T, out,
+               workspace):
     lib = load_library()
+    page_bytes = PAGE_BYTES if fmt == "mxfp4" else FP8_PAGE_BYTES
     _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be bf16 [B*T, 16*H, 128]")
     _need(q.is_contiguous(), "q must be contiguous")
-    _check_pages(k_pages, "k_pages", 3)
-    _check_pages(v_pages, "v_pages", 3)
+    _check_pages(k_pages, "k_pages", 3, page_bytes)
+    _check_pages(v_pages, "v_pages", 3, page_bytes)
     _need(k_pages.shape == v_pages.shape, "k_pages and v_pages must have the same shape")
     H = k_pages.shape[1]
     _need(q.shape[1] == Q_HEADS_PER_KV * H, f"q has {q.shape[1]} heads; the pools have {H} KV heads x 16")
@@ -369,10 +420,13 @@ def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_id
     nbytes = lib.mono_pa_decode_workspace(B, T, H, bt_stride, k, int(selected_idx is not None))
     _need(nbytes > 0, "invalid shape for mono_pa_decode_mxfp4")
     ws = _workspace(workspace, dev, nbytes, "pa")
-    _check(lib.mono_pa_decode_mxfp4(
-        _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H, _ptr(block_table), bt_stride,
-        _ptr(seq_lens), B, T, _ptr(selected_idx), k, ctypes.c_float(float(scale)), _ptr(out),
-        _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    args = [_ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H, _ptr(block_table), bt_stride,
+            _ptr(seq_lens), B, T, _ptr(selected_idx), k, ctypes.c_float(float(scale))]
+    if fmt == "mxfp4":
+        _check(lib.mono_pa_decode_mxfp4(*args, _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    else:
+        _check(lib.mono_pa_decode_fp8(*args, ctypes.c_float(float(k_scale)), ctypes.c_float(float(v_scale)),
+                                      _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return out
 
 
@@ -388,15 +442,30 @@ def mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages, block_ta
     Arguments as for :func:`mono_index_score_topk` and :func:`mono_pa_decode_mxfp4`.
     Returns ``(out, selected_idx)``: bf16 ``[B*T, 16*H, 128]`` and int32 ``[B*T, k]``.
     """
+    return _sparse_decode("mxfp4", index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k, scale, 1.0,
+                          1.0, T, out, selected_idx, workspace)
+
+
+def mono_sparse_decode_fp8(index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k,
+                           scale=1.0 / math.sqrt(HEAD_DIM), k_scale=1.0, v_scale=1.0, *, T=1, out=None,
+                           selected_idx=None, workspace=None):
+    """:func:`mono_sparse_decode_mxfp4` over fp8 (e4m3) pools: index ``[P, 16384]``, K/V ``[P, H, 16384]``."""
+    return _sparse_decode("fp8", index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k, scale, k_scale,
+                          v_scale, T, out, selected_idx, workspace)
+
+
+def _sparse_decode(fmt, index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k, scale, k_scale, v_scale,
+                   T, out, selected_idx, workspace):
     lib = load_library()
+    page_bytes = PAGE_BYTES if fmt == "mxfp4" else FP8_PAGE_BYTES
     _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM,
           "index_q must be bf16 [B*T, 128]")
     _need(index_q.is_contiguous(), "index_q must be contiguous")
-    _check_pages(index_pages, "index_pages", 2)
+    _check_pages(index_pages, "index_pages", 2, page_bytes)
     _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be bf16 [B*T, 16*H, 128]")
     _need(q.is_contiguous(), "q must be contiguous")
-    _check_pages(k_pages, "k_pages", 3)
-    _check_pages(v_pages, "v_pages", 3)
+    _check_pages(k_pages, "k_pages", 3, page_bytes)
+    _check_pages(v_pages, "v_pages", 3, page_bytes)
     _need(k_pages.shape == v_pages.shape, "k_pages and v_pages must have the same shape")
     _need(index_pages.shape[0] == k_pages.shape[0], "the index pool and the K/V pools must have the same page count")
     H = k_pages.shape[1]
@@ -419,10 +488,14 @@ def mono_sparse_decode_mxfp4(index_q, index_pages, q, k_pages, v_pages, block_ta
     nbytes = lib.mono_sparse_decode_workspace(B, T, H, bt_stride, k)
     _need(nbytes > 0, "invalid shape for mono_sparse_decode_mxfp4")
     ws = _workspace(workspace, dev, nbytes, "step")
-    _check(lib.mono_sparse_decode_mxfp4(
-        _ptr(index_q), _ptr(index_pages), _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H,
-        _ptr(block_table), bt_stride, _ptr(seq_lens), B, T, k, ctypes.c_float(float(scale)),
-        _ptr(selected_idx), _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    args = [_ptr(index_q), _ptr(index_pages), _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H,
+            _ptr(block_table), bt_stride, _ptr(seq_lens), B, T, k, ctypes.c_float(float(scale))]
+    tail = [_ptr(selected_idx), _ptr(out), _ptr(ws.buf), ws.nbytes, _stream(dev)]
+    if fmt == "mxfp4":
+        _check(lib.mono_sparse_decode_mxfp4(*args, *tail))
+    else:
+        _check(lib.mono_sparse_decode_fp8(*args, ctypes.c_float(float(k_scale)), ctypes.c_float(float(v_scale)),
+                                          *tail))
     return out, selected_idx
 
 

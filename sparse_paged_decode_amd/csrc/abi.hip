@@ -42,9 +42,10 @@ struct Profiler {
 };
 Profiler g_prof;
 // The step kernel is one kernel; it is timed under the name of the call.
-const char* const kKernelNames[kNumKernels] = {"pack_kernel",         "unpack_kernel",     "dequant_f32_kernel",
-                                               "dequant_bf16_kernel", "index_topk_kernel", "pa_decode_kernel",
-                                               "sparse_decode_kernel", "insert_kernel"};
+const char* const kKernelNames[kNumKernels] = {
+    "pack_kernel",          "unpack_kernel",         "dequant_f32_kernel",  "dequant_bf16_kernel",
+    "index_topk_kernel",    "pa_decode_kernel",      "sparse_decode_kernel", "insert_kernel",
+    "index_topk_fp8_kernel", "pa_decode_fp8_kernel", "sparse_decode_fp8_kernel", "dequant_fp8_bf16_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -85,6 +86,123 @@ int check_pages_args(const void* a, const void* b, const void* c, int64_t n_page
   if (n_pages > 0 && (!a || !b || !c))
     return set_error(MONO_EINVAL, "%s: NULL buffer", what);
   return MONO_OK;
+}
+
+// fp8 tensor scales must be finite and positive.
+bool bad_tensor_scale(float x) { return !(x > 0.f) || x == __builtin_inff(); }
+
+// The step calls, for either cache format (MXFP4 or fp8).
+int index_topk_impl(int fmt, const char* what, const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                    int64_t num_pages, const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
+                    int B, int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
+                    size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (!index_q_dev || !index_pages_dev || !block_table_dev || !seq_lens_dev || !selected_idx_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
+  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(ws_dev, 256) ||
+      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4) ||
+      !aligned(selected_scores_dev, 4))
+    return set_error(MONO_EINVAL, "%s: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment", what);
+  const StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
+  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  StepArgs a{};
+  a.fmt = fmt;
+  a.index_q = index_q_dev;
+  a.index_pages = index_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = selected_idx_dev;
+  a.sel_scores = selected_scores_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, what);
+}
+
+int pa_decode_impl(int fmt, const char* what, const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                   const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads, const int32_t* block_table_dev,
+                   int bt_stride, const int32_t* seq_lens_dev, int B, int T, const int32_t* selected_idx_dev, int k,
+                   float scale, float k_scale, float v_scale, uint16_t* out_dev, void* ws_dev, size_t ws_bytes,
+                   void* stream) {
+  clear_error();
+  const bool sparse = selected_idx_dev != nullptr;
+  if (int rc = check_step_shape(B, T, bt_stride, k, sparse)) return rc;
+  if (kv_heads < 1 || kv_heads > kMaxHeads)
+    return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
+  if (!q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev || !seq_lens_dev || !out_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return set_error(MONO_EINVAL, "%s: scale must be finite", what);
+  if (bad_tensor_scale(k_scale) || bad_tensor_scale(v_scale))
+    return set_error(MONO_EINVAL, "%s: k_scale and v_scale must be finite and > 0", what);
+  if (!aligned(q_dev, 16) || !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) ||
+      !aligned(ws_dev, 256) || !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) ||
+      !aligned(selected_idx_dev, 4))
+    return set_error(MONO_EINVAL, "%s: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment", what);
+  const StepLayout lay = step_layout(kModeAttn, B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
+  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  StepArgs a{};
+  a.fmt = fmt;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.q = q_dev;
+  a.k_pages = k_pages_dev;
+  a.v_pages = v_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = const_cast<int32_t*>(selected_idx_dev);
+  a.scale = scale;
+  a.out = out_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, what);
+}
+
+int sparse_decode_impl(int fmt, const char* what, const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                       const uint16_t* q_dev, const uint8_t* k_pages_dev, const uint8_t* v_pages_dev,
+                       int64_t num_pages, int kv_heads, const int32_t* block_table_dev, int bt_stride,
+                       const int32_t* seq_lens_dev, int B, int T, int k, float scale, float k_scale, float v_scale,
+                       int32_t* selected_idx_dev, uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  clear_error();
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (kv_heads < 1 || kv_heads > kMaxHeads)
+    return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
+  if (!index_q_dev || !index_pages_dev || !q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev ||
+      !seq_lens_dev || !selected_idx_dev || !out_dev || !ws_dev)
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+    return set_error(MONO_EINVAL, "%s: scale must be finite", what);
+  if (bad_tensor_scale(k_scale) || bad_tensor_scale(v_scale))
+    return set_error(MONO_EINVAL, "%s: k_scale and v_scale must be finite and > 0", what);
+  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(q_dev, 16) ||
+      !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) || !aligned(ws_dev, 256) ||
+      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4))
+    return set_error(MONO_EINVAL, "%s: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment", what);
+  const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
+  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  StepArgs a{};
+  a.fmt = fmt;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.index_q = index_q_dev;
+  a.index_pages = index_pages_dev;
+  a.q = q_dev;
+  a.k_pages = k_pages_dev;
+  a.v_pages = v_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.sel = selected_idx_dev;
+  a.scale = scale;
+  a.out = out_dev;
+  a.ws = static_cast<uint8_t*>(ws_dev);
+  return launch_step(a, lay, (hipStream_t)stream, what);
 }
 
 }  // namespace
@@ -145,30 +263,18 @@ int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_page
                           const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
                           int B, int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev,
                           void* ws_dev, size_t ws_bytes, void* stream) {
-  clear_error();
-  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
-  if (!index_q_dev || !index_pages_dev || !block_table_dev || !seq_lens_dev || !selected_idx_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "mono_index_score_topk: NULL buffer");
-  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_index_score_topk: num_pages must be >= 1");
-  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(ws_dev, 256) ||
-      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4) ||
-      !aligned(selected_scores_dev, 4))
-    return set_error(MONO_EINVAL,
-                     "mono_index_score_topk: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment");
-  const StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
-  if (ws_bytes < lay.total)
-    return set_error(MONO_ENOSPC, "mono_index_score_topk: workspace %zu B < %zu B", ws_bytes, lay.total);
-  StepArgs a{};
-  a.index_q = index_q_dev;
-  a.index_pages = index_pages_dev;
-  a.num_pages = num_pages;
-  a.block_table = block_table_dev;
-  a.bt_stride = bt_stride;
-  a.seq_lens = seq_lens_dev;
-  a.sel = selected_idx_dev;
-  a.sel_scores = selected_scores_dev;
-  a.ws = static_cast<uint8_t*>(ws_dev);
-  return launch_step(a, lay, (hipStream_t)stream, "mono_index_score_topk");
+  return index_topk_impl(kFmtMxfp4, "mono_index_score_topk", index_q_dev, index_pages_dev, num_pages, block_table_dev,
+                         bt_stride, seq_lens_dev, B, T, k, selected_idx_dev, selected_scores_dev, ws_dev, ws_bytes,
+                         stream);
+}
+
+int mono_index_score_topk_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                              const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B,
+                              int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
+                              size_t ws_bytes, void* stream) {
+  return index_topk_impl(kFmtFp8, "mono_index_score_topk_fp8", index_q_dev, index_pages_dev, num_pages,
+                         block_table_dev, bt_stride, seq_lens_dev, B, T, k, selected_idx_dev, selected_scores_dev,
+                         ws_dev, ws_bytes, stream);
 }
 
 size_t mono_pa_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k, int sparse) {
@@ -181,38 +287,18 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev, cons
                          int64_t num_pages, int kv_heads, const int32_t* block_table_dev, int bt_stride,
                          const int32_t* seq_lens_dev, int B, int T, const int32_t* selected_idx_dev, int k,
                          float scale, uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
-  clear_error();
-  const bool sparse = selected_idx_dev != nullptr;
-  if (int rc = check_step_shape(B, T, bt_stride, k, sparse)) return rc;
-  if (kv_heads < 1 || kv_heads > kMaxHeads)
-    return set_error(MONO_ENOTSUP, "mono_pa_decode_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads,
-                     kv_heads);
-  if (!q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev || !seq_lens_dev || !out_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: NULL buffer");
-  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: num_pages must be >= 1");
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return set_error(MONO_EINVAL, "mono_pa_decode_mxfp4: scale must be finite");
-  if (!aligned(q_dev, 16) || !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) ||
-      !aligned(ws_dev, 256) || !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) ||
-      !aligned(selected_idx_dev, 4))
-    return set_error(MONO_EINVAL,
-                     "mono_pa_decode_mxfp4: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment");
-  const StepLayout lay = step_layout(kModeAttn, B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
-  if (ws_bytes < lay.total)
-    return set_error(MONO_ENOSPC, "mono_pa_decode_mxfp4: workspace %zu B < %zu B", ws_bytes, lay.total);
-  StepArgs a{};
-  a.q = q_dev;
-  a.k_pages = k_pages_dev;
-  a.v_pages = v_pages_dev;
-  a.num_pages = num_pages;
-  a.block_table = block_table_dev;
-  a.bt_stride = bt_stride;
-  a.seq_lens = seq_lens_dev;
-  a.sel = const_cast<int32_t*>(selected_idx_dev);
-  a.scale = scale;
-  a.out = out_dev;
-  a.ws = static_cast<uint8_t*>(ws_dev);
-  return launch_step(a, lay, (hipStream_t)stream, "mono_pa_decode_mxfp4");
+  return pa_decode_impl(kFmtMxfp4, "mono_pa_decode_mxfp4", q_dev, k_pages_dev, v_pages_dev, num_pages, kv_heads,
+                        block_table_dev, bt_stride, seq_lens_dev, B, T, selected_idx_dev, k, scale, 1.f, 1.f, out_dev,
+                        ws_dev, ws_bytes, stream);
+}
+
+int mono_pa_decode_fp8(const uint16_t* q_dev, const uint8_t* k_pages_dev, const uint8_t* v_pages_dev,
+                       int64_t num_pages, int kv_heads, const int32_t* block_table_dev, int bt_stride,
+                       const int32_t* seq_lens_dev, int B, int T, const int32_t* selected_idx_dev, int k, float scale,
+                       float k_scale, float v_scale, uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return pa_decode_impl(kFmtFp8, "mono_pa_decode_fp8", q_dev, k_pages_dev, v_pages_dev, num_pages, kv_heads,
+                        block_table_dev, bt_stride, seq_lens_dev, B, T, selected_idx_dev, k, scale, k_scale, v_scale,
+                        out_dev, ws_dev, ws_bytes, stream);
 }
 
 size_t mono_sparse_decode_workspace(int B, int T, int kv_heads, int bt_stride, int k) {
@@ -227,40 +313,28 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                              const int32_t* seq_lens_dev, int B, int T, int k, float scale,
                              int32_t* selected_idx_dev, uint16_t* out_dev, void* ws_dev, size_t ws_bytes,
                              void* stream) {
+  return sparse_decode_impl(kFmtMxfp4, "mono_sparse_decode_mxfp4", index_q_dev, index_pages_dev, q_dev, k_pages_dev,
+                            v_pages_dev, num_pages, kv_heads, block_table_dev, bt_stride, seq_lens_dev, B, T, k, scale,
+                            1.f, 1.f, selected_idx_dev, out_dev, ws_dev, ws_bytes, stream);
+}
+
+int mono_sparse_decode_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, const uint16_t* q_dev,
+                           const uint8_t* k_pages_dev, const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                           const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B, int T,
+                           int k, float scale, float k_scale, float v_scale, int32_t* selected_idx_dev,
+                           uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return sparse_decode_impl(kFmtFp8, "mono_sparse_decode_fp8", index_q_dev, index_pages_dev, q_dev, k_pages_dev,
+                            v_pages_dev, num_pages, kv_heads, block_table_dev, bt_stride, seq_lens_dev, B, T, k, scale,
+                            k_scale, v_scale, selected_idx_dev, out_dev, ws_dev, ws_bytes, stream);
+}
+
+int fp8_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
-  if (kv_heads < 1 || kv_heads > kMaxHeads)
-    return set_error(MONO_ENOTSUP, "mono_sparse_decode_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads,
-                     kv_heads);
-  if (!index_q_dev || !index_pages_dev || !q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev ||
-      !seq_lens_dev || !selected_idx_dev || !out_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: NULL buffer");
-  if (num_pages < 1) return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: num_pages must be >= 1");
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return set_error(MONO_EINVAL, "mono_sparse_decode_mxfp4: scale must be finite");
-  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(q_dev, 16) ||
-      !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) || !aligned(ws_dev, 256) ||
-      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4))
-    return set_error(MONO_EINVAL,
-                     "mono_sparse_decode_mxfp4: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment");
-  const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
-  if (ws_bytes < lay.total)
-    return set_error(MONO_ENOSPC, "mono_sparse_decode_mxfp4: workspace %zu B < %zu B", ws_bytes, lay.total);
-  StepArgs a{};
-  a.index_q = index_q_dev;
-  a.index_pages = index_pages_dev;
-  a.q = q_dev;
-  a.k_pages = k_pages_dev;
-  a.v_pages = v_pages_dev;
-  a.num_pages = num_pages;
-  a.block_table = block_table_dev;
-  a.bt_stride = bt_stride;
-  a.seq_lens = seq_lens_dev;
-  a.sel = selected_idx_dev;
-  a.scale = scale;
-  a.out = out_dev;
-  a.ws = static_cast<uint8_t*>(ws_dev);
-  return launch_step(a, lay, (hipStream_t)stream, "mono_sparse_decode_mxfp4");
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "fp8_pages_dequant_bf16")) return rc;
+  if (n_pages == 0) return MONO_OK;
+  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
+    return set_error(MONO_EINVAL, "fp8_pages_dequant_bf16: pages and out need 16-byte alignment");
+  return launch_dequant_fp8_bf16(pages_dev, out_dev, n_pages, (hipStream_t)stream);
 }
 
 int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev, const uint16_t* index_rows_dev,

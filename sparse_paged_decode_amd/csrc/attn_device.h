@@ -1,4 +1,5 @@
-// Paged GQA decode attention over MXFP4 K/V pages: one split of one query
+// Paged GQA decode attention over MXFP4 K/V pages (or the older build's fp8
+// pages, through the format policy of page_format.h): one split of one query
 // token and KV head (gfx950).
 //
 // The pa_decode the mxfp4_pages page names reads [pages, heads, 8704] K and V
@@ -29,6 +30,7 @@
 
 #include "block_ops.h"
 #include "launch.h"
+#include "page_format.h"
 
 namespace mono {
 
@@ -50,7 +52,7 @@ struct AttnLds {
 
 struct AttnArgs {
   const uint16_t* q;        // this query token's 16 heads of KV head h: [16, 128]
-  const uint8_t* k_pages;   // [num_pages, H, 8704]
+  const uint8_t* k_pages;   // [num_pages, H, page bytes of the format]
   const uint8_t* v_pages;
   int64_t num_pages;
   int H, h;
@@ -59,7 +61,8 @@ struct AttnArgs {
   int pos;                  // position of the query token
   int e0, e1;               // candidates of this split
   int split, n_splits;
-  float scale;
+  float scale;              // logit scale (times the K tensor scale for fp8)
+  float v_scale;            // V tensor scale (1 for MXFP4)
   uint16_t* out;            // [16, 128] bf16 output of (query token, KV head)
   float* pm;                // [n_splits, 16] partial maxima of (query token, KV head)
   float* pl;                // [n_splits, 16] partial sums
@@ -78,14 +81,14 @@ __device__ __forceinline__ void store_bf16x8(uint16_t* dst, const float* o, floa
 }
 
 // The K and V data of one group as one lane needs them.
+template <class Fmt>
 struct AttnGroup {
-  u32x4_t kd;      // K chunk g of token m
-  uint32_t ke;     // its e8m0 scale
-  uint32_t vd[4];  // V bytes 4m..4m+3 of tokens 4g..4g+3
-  uint32_t ve[4];  // their e8m0 scales (block m/4)
-  uint32_t valid;  // token m is a candidate
+  typename Fmt::Chunk k;     // K chunk g (elements 32g..32g+31) of token m
+  typename Fmt::Slice v[4];  // V elements 8m..8m+7 of tokens 4g..4g+3
+  uint32_t valid;            // token m is a candidate
 };
 
+template <class Fmt>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
@@ -126,9 +129,9 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const size_t kv_stride = (size_t)H * kPageBytes;
-  const uint8_t* kbase = a.k_pages + (size_t)h * kPageBytes;
-  const uint8_t* vbase = a.v_pages + (size_t)h * kPageBytes;
+  const size_t kv_stride = (size_t)H * Fmt::kPageBytes;
+  const uint8_t* kbase = a.k_pages + (size_t)h * Fmt::kPageBytes;
+  const uint8_t* vbase = a.v_pages + (size_t)h * Fmt::kPageBytes;
 
   // Token j of lane (g, m) -> its pool row, packed as page << 7 | row, or
   // ~0u when it is not a candidate.
@@ -143,41 +146,30 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   };
   // Loads are unconditional (a non-candidate reads page 0, row 0, and is
   // zeroed afterwards) so the compiler can count outstanding loads exactly.
-  auto load_group = [&](uint32_t ref) -> AttnGroup {
-    AttnGroup t;
+  auto load_group = [&](uint32_t ref) -> AttnGroup<Fmt> {
+    AttnGroup<Fmt> t;
     t.valid = ref != ~0u;
     const uint32_t r0 = t.valid ? ref : 0u;
     {
-      const uint8_t* row = kbase + (size_t)(r0 >> 7) * kv_stride;
-      const uint32_t rr = r0 & 127u;
-      t.kd = *reinterpret_cast<const u32x4_t*>(row + rr * kRowBytes + 16 * g);
-      t.ke = row[kScaleOffset + rr * 4 + g];
+      const uint8_t* page = kbase + (size_t)(r0 >> 7) * kv_stride;
+      t.k = Fmt::load_chunk(page, Fmt::chunk_addr((int)(r0 & 127u), g));
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t ri = __shfl(ref, 4 * g + i);
       const uint32_t r1 = ri != ~0u ? ri : 0u;
-      const uint8_t* row = vbase + (size_t)(r1 >> 7) * kv_stride;
-      const uint32_t rr = r1 & 127u;
-      t.vd[i] = *reinterpret_cast<const uint32_t*>(row + rr * kRowBytes + 4 * m);
-      t.ve[i] = row[kScaleOffset + rr * 4 + (m >> 2)];
-      if (ri == ~0u) {
-        t.vd[i] = 0u;
-        t.ve[i] = 127u;
-      }
+      const uint8_t* page = vbase + (size_t)(r1 >> 7) * kv_stride;
+      t.v[i] = Fmt::load_slice(page, r1 & 127u, m);
+      if (ri == ~0u) t.v[i] = Fmt::zero_slice();
     }
-    if (!t.valid) {
-      t.kd = u32x4_t{0u, 0u, 0u, 0u};
-      t.ke = 127u;
-    }
+    if (!t.valid) t.k = Fmt::zero_chunk();
     return t;
   };
   // S^T tile of a group: lane (g, n) gets tokens 4g + i (i = 0..3) of head n.
-  auto qk_group = [&](const AttnGroup& t) -> f32x4_t {
-    const float sc = e8m0_scale_operand(t.ke);
+  auto qk_group = [&](const AttnGroup<Fmt>& t) -> f32x4_t {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dequant8_bf16(t.kd[s], sc), qb[s], c, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::chunk_bf16(t.k, s), qb[s], c, 0, 0, 0);
     // Validity of token r sits in bit r of this ballot (lanes 0..15).
     const uint32_t vm = (uint32_t)__ballot(t.valid);
 #pragma unroll
@@ -186,11 +178,11 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   };
   // acc += P V of a group; pa is the A operand (row n = head n, k-slot (g, i)
   // = token 4g + i).
-  auto pv_group = [&](const AttnGroup& t, s16x4_t pa) {
+  auto pv_group = [&](const AttnGroup<Fmt>& t, s16x4_t pa) {
     // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1).
     u32x4_t vv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = __builtin_bit_cast(u32x4_t, dequant8_bf16(t.vd[i], e8m0_scale_operand(t.ve[i])));
+    for (int i = 0; i < 4; ++i) vv[i] = Fmt::slice_bf16(t.v[i]);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int p = x >> 1;
@@ -207,7 +199,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   // loads of all of them at once, QK^T of all, one online-softmax update,
   // then P V of all.  The first pass's entries were requested at the start.
   for (int gb = wave; gb < n_groups; gb += kWaves * kPassGroups) {
-    AttnGroup grp[kPassGroups];
+    AttnGroup<Fmt> grp[kPassGroups];
 #pragma unroll
     for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(jv[x]));
     // The next pass's entries load while this pass computes.
@@ -285,7 +277,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 
   uint16_t* orow = a.out + (size_t)hd * kHeadDim + d0;
   if (n_splits == 1) {
-    store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
+    store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
     return;
   }
 
@@ -354,7 +346,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     }
     M = Mb;
   }
-  store_bf16x8(orow, o, lsum > 0.f ? 1.f / lsum : 0.f);
+  store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
 }
 
 }  // namespace mono

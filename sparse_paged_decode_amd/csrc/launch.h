@@ -23,6 +23,10 @@ enum KernelId {
   kKPaDecode,
   kKStep,
   kKInsert,
+  kKIndexScanFp8,
+  kKPaDecodeFp8,
+  kKStepFp8,
+  kKDequantFp8Bf16,
   kNumKernels
 };
 // When timing is on, takes the next pair of timing events for kernel `id`
@@ -49,6 +53,8 @@ int launch_unpack(const uint8_t* pages, uint8_t* codes, uint8_t* scales, int64_t
                   hipStream_t stream);
 int launch_dequant_f32(const uint8_t* pages, float* out, int64_t n_pages, hipStream_t stream);
 int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
+// fp8 pages [n_pages, 16384] -> bf16 [n_pages, 128, 128] through the step kernel's conversion.
+int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
 // Cache insert: caches c = 0 (K), 1 (V), 2 (index key) with row_heads[c]
 // rows per token (0 = not written); rows[c] bf16 [n, row_heads[c], 128],
 // pools[c] [num_pages, row_heads[c], 8704].
@@ -91,7 +97,13 @@ struct StepLayout {
 };
 StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
 
+// Cache page formats (page_format.h).
+enum CacheFormat { kFmtMxfp4 = 0, kFmtFp8 = 1 };
+
 struct StepArgs {
+  int fmt = kFmtMxfp4;  // CacheFormat of the index, K and V pools
+  float k_scale = 1.f;  // fp8 K tensor scale (1 for MXFP4)
+  float v_scale = 1.f;  // fp8 V tensor scale (1 for MXFP4)
   const uint16_t* index_q;
   const uint8_t* index_pages;
   const uint16_t* q;

@@ -5,6 +5,7 @@
 // rows of 4 e8m0 scale bytes (one per 32 elements), 8704 B per page.
 #include "device_common.h"
 #include "launch.h"
+#include "page_format.h"
 
 namespace mono {
 namespace {
@@ -116,6 +117,21 @@ __global__ __launch_bounds__(256) void dequant_bf16_kernel(const uint8_t* __rest
   bf16x8_t* dst = reinterpret_cast<bf16x8_t*>(out + row * kHeadDim + 32 * g);
 #pragma unroll
   for (int w = 0; w < 4; ++w) dst[w] = dequant8_bf16(d[w], scale);
+}
+
+// fp8 pages: one thread per (page, row, 32-element chunk), converted by the
+// step kernel's own chunk conversion.
+__global__ __launch_bounds__(256) void dequant_fp8_bf16_kernel(const uint8_t* __restrict__ pages,
+                                                               uint16_t* __restrict__ out, int64_t n_chunks) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n_chunks) return;
+  const int64_t row = c >> 2;
+  const int g = (int)(c & 3);
+  const uint8_t* p = pages + (row / kPageTokens) * Fp8Format::kPageBytes;
+  const Fp8Format::Chunk ch = Fp8Format::load_chunk(p, Fp8Format::chunk_addr((int)(row % kPageTokens), g));
+  bf16x8_t* dst = reinterpret_cast<bf16x8_t*>(out + row * kHeadDim + 32 * g);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) dst[s] = Fp8Format::chunk_bf16(ch, s);
 }
 
 // ---- the cache insert ---------------------------------------------------------
@@ -250,6 +266,13 @@ int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hi
   MONO_LAUNCH(kKDequantBf16, dequant_bf16_kernel, dim3(grid_for(n_blocks, 256)), dim3(256), 0, stream, pages,
                      out, n_blocks);
   return check_launch("mxfp4_pages_dequant_bf16");
+}
+
+int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream) {
+  const int64_t n_chunks = n_pages * kPageTokens * 4;
+  MONO_LAUNCH(kKDequantFp8Bf16, dequant_fp8_bf16_kernel, dim3(grid_for(n_chunks, 256)), dim3(256), 0, stream, pages,
+              out, n_chunks);
+  return check_launch("fp8_pages_dequant_bf16");
 }
 
 int launch_insert(const uint16_t* const rows[3], uint8_t* const pools[3], const int row_heads[3],

@@ -236,7 +236,7 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
     publish(lay, ctrl, kItemAttn, i * (uint32_t)(lay.H * lay.n_splits), (uint32_t)(lay.H * lay.n_splits), err, s_pub);
 }
 
-template <int TQ>
+template <int TQ, class Fmt>
 __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& lay, uint32_t t, StepLds<TQ>& slds,
                                           uint32_t* ctrl, uint32_t* err, uint32_t& s_flag, uint32_t& s_pub) {
   ScanLds<TQ>& lds = slds.scan;
@@ -269,7 +269,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
       sa.tq = tq;
       sa.p_begin = c * lay.chunk_pages;
       sa.p_end = min(sa.p_begin + lay.chunk_pages, n_pages);
-      scan_chunk<TQ>(sa, lds);
+      scan_chunk<TQ, Fmt>(sa, lds);
       wait_vmem();  // scores and histogram updates are complete before the arrival
     }
   }
@@ -321,7 +321,7 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
             err, s_pub);
 }
 
-template <int TQ>
+template <int TQ, class Fmt>
 __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& lay, uint32_t v, StepLds<TQ>& lds,
                                           uint32_t* ctrl, uint32_t* err) {
   const int H = lay.H, S = lay.n_splits;
@@ -354,17 +354,18 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   aa.e1 = min(aa.e0 + lay.split_tokens, list_len);
   aa.split = split;
   aa.n_splits = n_splits;
-  aa.scale = a.scale;
+  aa.scale = a.scale * a.k_scale;
+  aa.v_scale = a.v_scale;
   aa.out = a.out + qh * kQHeads * kHeadDim;
   aa.pm = reinterpret_cast<float*>(a.ws + lay.pm) + qh * S * kQHeads;
   aa.pl = reinterpret_cast<float*>(a.ws + lay.pl) + qh * S * kQHeads;
   aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
   aa.split_cnt = ctrl + lay.attn_cnt + qh;
   aa.err = err;
-  attn_split(aa, lds.attn);
+  attn_split<Fmt>(aa, lds.attn);
 }
 
-template <int TQ>
+template <int TQ, class Fmt>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
   __shared__ StepLds<TQ> lds;
   __shared__ uint32_t s_item, s_flag, s_clear, s_desc, s_pub;
@@ -398,13 +399,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
           u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, s_desc);
       const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
       if (kind == kItemScan) {
-        scan_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
+        scan_item<TQ, Fmt>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
       } else if (kind == kItemSelect) {
         select_item<TQ>(a, lay, idx, lds, ctrl, err, s_pub);
       } else if (kind == kItemFilter) {
         filter_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
       } else if (kind == kItemAttn) {
-        attn_item<TQ>(a, lay, idx, lds, ctrl, err);
+        attn_item<TQ, Fmt>(a, lay, idx, lds, ctrl, err);
       }
     }
     __syncthreads();  // the next item reuses the LDS
@@ -444,8 +445,12 @@ int resident_workgroups(const void* kernel, int variant) {
 
 int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream, const char* what) {
   const bool tq4 = lay_in.T > 1 && (lay_in.mode & kModeIndex);
-  const void* kern = tq4 ? reinterpret_cast<const void*>(&step_kernel<4>) : reinterpret_cast<const void*>(&step_kernel<1>);
-  const int cap = resident_workgroups(kern, tq4 ? 1 : 0);
+  const bool f8 = a.fmt == kFmtFp8;
+  const void* const kernels[4] = {
+      reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format>), reinterpret_cast<const void*>(&step_kernel<4, Mxfp4Format>),
+      reinterpret_cast<const void*>(&step_kernel<1, Fp8Format>), reinterpret_cast<const void*>(&step_kernel<4, Fp8Format>)};
+  const int variant = (tq4 ? 1 : 0) + (f8 ? 2 : 0);
+  const int cap = resident_workgroups(kernels[variant], variant);
   StepLayout lay = lay_in;
   if (lay.mode & kModeIndex) {
     // Scan chunks sized so the scan items make about one round of the
@@ -491,11 +496,14 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
   if (lay.zero_units > 0xFFFFFFFFull || lay.ctrl_base != 256)
     return set_error(MONO_ENOTSUP, "%s: workspace layout too large", what);
   const unsigned grid = (unsigned)std::min<uint64_t>(n_items, (uint64_t)cap);
-  const int kid = lay.mode == kModeIndex ? kKIndexScan : (lay.mode == kModeAttn ? kKPaDecode : kKStep);
-  if (tq4) {
-    MONO_LAUNCH(kid, step_kernel<4>, dim3(grid), dim3(kBlock), 0, stream, a, lay);
-  } else {
-    MONO_LAUNCH(kid, step_kernel<1>, dim3(grid), dim3(kBlock), 0, stream, a, lay);
+  const int kid = lay.mode == kModeIndex ? (f8 ? kKIndexScanFp8 : kKIndexScan)
+                  : lay.mode == kModeAttn  ? (f8 ? kKPaDecodeFp8 : kKPaDecode)
+                                           : (f8 ? kKStepFp8 : kKStep);
+  switch (variant) {
+    case 0: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 1: MONO_LAUNCH(kid, (step_kernel<4, Mxfp4Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    default: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
   }
   return check_launch(what);
 }

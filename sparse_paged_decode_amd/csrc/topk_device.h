@@ -21,11 +21,14 @@
 //                    ties at the threshold go to the lowest token indices.
 //
 // Scores, histograms and selections cross workgroups, so they are written
-// and read with coherent (agent-scope) operations.
+// and read with coherent (agent-scope) operations.  The scan is written over
+// a page-format policy (page_format.h): MXFP4 pages, or the fp8 pages of
+// the older build.
 #pragma once
 
 #include "block_ops.h"
 #include "launch.h"
+#include "page_format.h"
 
 #include <type_traits>
 
@@ -33,7 +36,6 @@ namespace mono {
 
 constexpr int kScanChunkPages = 16;  // index pages per scan work item (default)
 constexpr int kMaxChunkPages = 64;   // one page id per lane of a wave
-constexpr int kBatch = 4;            // pages per prefetch batch
 constexpr int kHistBins = 2048;      // top 11 bits of the score key
 constexpr int kHistShift = 21;
 
@@ -45,15 +47,15 @@ struct ScanLds {
 // ---------------------------------------------------------------------------
 // scan_chunk: pages [p_begin, p_end) of request b for query tokens t0..t0+tq-1.
 // Wave w scores rows 32w..32w+31 of every page as two 16-row MFMA tiles; lane
-// (g = lane/16, m = lane%16) loads the 16-byte chunk g (elements 32g..32g+31,
-// one e8m0 block) of row m of a tile, which is that row's B-operand slot for
-// the four k-steps.  Scores: C = Q K^T with the query tokens as M and the 16
+// (g = lane/16, m = lane%16) loads chunk g (elements 32g..32g+31: one e8m0
+// block of 16 bytes, or 32 fp8 bytes) of row m of a tile, which is that
+// row's B-operand slot for the four k-steps.  Scores: C = Q K^T with the query tokens as M and the 16
 // rows of a tile as N, so lane (0, n) ends with row n's scores for query
 // tokens 0..3 (acc[i]).
 // ---------------------------------------------------------------------------
 struct ScanArgs {
   const uint16_t* index_q;  // bf16 [B*T, 128]
-  const uint8_t* pages;     // [num_pages, 8704]
+  const uint8_t* pages;     // [num_pages, page bytes of the format]
   int64_t num_pages;
   const int32_t* bt_row;    // block-table row of request b
   float* q_scores;          // scores of query token t0, rows lcap apart
@@ -66,8 +68,9 @@ struct ScanArgs {
   int p_begin, p_end;       // pages of the chunk
 };
 
-template <int TQ>
+template <int TQ, class Fmt>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) {
+  constexpr int kBatch = Fmt::kScanBatch;  // pages per prefetch batch
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
 
@@ -92,10 +95,8 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
   const int row0 = 32 * wave + m;  // tile 0 row; tile 1 is row0 + 16
   // 32-bit lane offsets inside a page, so each load is (page base in SGPRs) +
   // (fixed lane offset) with no per-load address arithmetic.
-  const uint32_t off_d0 = (uint32_t)(row0 * kRowBytes + 16 * g);
-  const uint32_t off_d1 = off_d0 + 16u * kRowBytes;
-  const uint32_t off_e0 = (uint32_t)(kScaleOffset + row0 * 4 + g);
-  const uint32_t off_e1 = off_e0 + 16u * 4u;
+  const typename Fmt::ChunkAddr off0 = Fmt::chunk_addr(row0, g);
+  const typename Fmt::ChunkAddr off1 = Fmt::chunk_addr(row0 + 16, g);
 
   // The chunk's physical page ids, one per lane (lanes past the chunk repeat
   // its last page); each page's id is then taken with readlane, so no load
@@ -114,29 +115,24 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
   // count the outstanding loads exactly and wait only for the batch being
   // scored.
   struct Rows {
-    u32x4_t d[2];
-    uint32_t e[2];
+    typename Fmt::Chunk c[2];  // tiles 0 and 1
   };
   auto load_batch = [&](Rows* r, int p0) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int cp = min(p0 + u - p_begin, n_cp - 1);
-      const uint8_t* pg = a.pages + (size_t)__builtin_amdgcn_readlane(lane_pid, cp) * kPageBytes;
-      r[u].d[0] = *reinterpret_cast<const u32x4_t*>(pg + off_d0);
-      r[u].d[1] = *reinterpret_cast<const u32x4_t*>(pg + off_d1);
-      r[u].e[0] = pg[off_e0];
-      r[u].e[1] = pg[off_e1];
+      const uint8_t* pg = a.pages + (size_t)__builtin_amdgcn_readlane(lane_pid, cp) * Fmt::kPageBytes;
+      r[u].c[0] = Fmt::load_chunk(pg, off0);
+      r[u].c[1] = Fmt::load_chunk(pg, off1);
     }
   };
   auto score_page = [&](const Rows& r, int p) {
     if (p >= p_end) return;  // past the chunk: the registers hold a repeat of its last page
-    const float sc0 = e8m0_scale_operand(r.e[0]);
-    const float sc1 = e8m0_scale_operand(r.e[1]);
     f32x4_t c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[0][s], sc0), c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], dequant8_bf16(r.d[1][s], sc1), c1, 0, 0, 0);
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], Fmt::chunk_bf16(r.c[0], s), c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[s], Fmt::chunk_bf16(r.c[1], s), c1, 0, 0, 0);
     }
     if (g == 0) {
 #pragma unroll

@@ -21,6 +21,12 @@ this order):
 4. ``q`` (``[B*T, 16, 128]``) and, for sparse workloads, ``index_q``
    (``[B*T, 128]``): standard normal float32 rounded to bfloat16
    (round-to-nearest-even), stored as uint16 bit patterns.
+
+With ``cache="fp8"`` step 3 draws fp8 (e4m3) pages instead (``[P, 1, 16384]``
+and ``[P, 16384]``): every byte has a uniform sign bit, an exponent field
+uniform in ``fp8_exp_range`` (at most 14, so no NaN code) and a uniform
+3-bit mantissa; the workload also carries the K and V tensor scales
+``k_scale`` / ``v_scale`` it was built with.
 """
 
 from dataclasses import dataclass
@@ -48,6 +54,9 @@ class Workload:
     q: np.ndarray  # uint16 bf16 bits [B*T, 16, 128]
     index_pool: np.ndarray | None = None  # uint8 [P, 8704]
     index_q: np.ndarray | None = None  # uint16 bf16 bits [B*T, 128]
+    cache: str = "mxfp4"  # or "fp8": pools of [.., 16384] e4m3 pages
+    k_scale: float = 1.0  # fp8 K tensor scale
+    v_scale: float = 1.0  # fp8 V tensor scale
 
     @property
     def N(self):
@@ -76,6 +85,18 @@ def _pages(rng, shape, exp_range):
     return np.concatenate([data, scales], axis=-1)
 
 
+def _fp8_pages(rng, shape, exp_range):
+    lo, hi = exp_range
+    assert 0 <= lo <= hi <= 14
+    n = (*shape, _TOKENS_PER_PAGE * HEAD_DIM)
+    bits = rng.integers(0, 256, size=n, dtype=np.uint8)  # its sign bit and low 3 bits are used
+    exp = rng.integers(lo, hi + 1, size=n, dtype=np.uint8)
+    bits &= 0x87
+    exp <<= 3
+    bits |= exp
+    return bits
+
+
 def make_workload(
     name,
     *,
@@ -89,6 +110,10 @@ def make_workload(
     scale=1.0 / np.sqrt(128.0),
     identity_table=False,
     extra_pages=0,
+    cache="mxfp4",
+    fp8_exp_range=(4, 10),
+    k_scale=0.5,
+    v_scale=0.25,
 ):
     """Build one workload; ``seq_lens`` is an int, a list, or a ``(lo, hi)`` range tuple."""
     rng = np.random.default_rng(seed)
@@ -106,9 +131,15 @@ def make_workload(
     for b in range(B):
         bt[b, : n_pages[b]] = perm[off : off + n_pages[b]]
         off += int(n_pages[b])
-    k_pool = _pages(rng, (P, 1), exp_range)
-    v_pool = _pages(rng, (P, 1), exp_range)
-    index_pool = _pages(rng, (P,), exp_range) if k > 0 else None
+    if cache == "fp8":
+        k_pool = _fp8_pages(rng, (P, 1), fp8_exp_range)
+        v_pool = _fp8_pages(rng, (P, 1), fp8_exp_range)
+        index_pool = _fp8_pages(rng, (P,), fp8_exp_range) if k > 0 else None
+    else:
+        assert cache == "mxfp4"
+        k_pool = _pages(rng, (P, 1), exp_range)
+        v_pool = _pages(rng, (P, 1), exp_range)
+        index_pool = _pages(rng, (P,), exp_range) if k > 0 else None
     N = B * T
     q = _bf16_bits(rng.standard_normal((N, Q_HEADS, HEAD_DIM), dtype=np.float32))
     index_q = _bf16_bits(rng.standard_normal((N, HEAD_DIM), dtype=np.float32)) if k > 0 else None
@@ -125,6 +156,9 @@ def make_workload(
         q=q,
         index_pool=index_pool,
         index_q=index_q,
+        cache=cache,
+        k_scale=float(k_scale) if cache == "fp8" else 1.0,
+        v_scale=float(v_scale) if cache == "fp8" else 1.0,
     )
 
 
