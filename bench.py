@@ -1,12 +1,13 @@
 """Decode-step benchmark of the sparse paged MXFP4 decode path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3] [--cache mxfp4|fp8]
 
 A step is one pass of the whole path over one batch: on sparse workloads one
 mono_sparse_decode_mxfp4 call (index scores, top-k and attention over the
 selected tokens, in one launch); dense workloads run mono_pa_decode_mxfp4
 alone.  The default workload is batch 64, context 32768 (256 pages per
-request), top-2048.
+request), top-2048.  ``--cache fp8`` runs the same shapes over the older
+build's fp8 (e4m3) pages with the *_fp8 calls.
 
 Inputs are resident in HBM before timing starts.  The K, V and index-key
 pools are replicated ``--copies`` times and the steps rotate through the
@@ -37,16 +38,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E peak, GB/s
-ROW_BYTES = 68  # 64 B e2m1 data + 4 B e8m0 scales per token row
+ROW_BYTES = {"mxfp4": 68, "fp8": 128}  # per token row: 64 B e2m1 + 4 B e8m0; or 128 B of e4m3
 METRIC = "decode-step µs + achieved HBM GB/s (% of peak), B=64 ctx=32k top-2048"
 CSRC = os.path.join(ROOT, "sparse_paged_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # Source files that define each kernel; their digest keys the stored counter data.
-_STEP_SOURCES = ["step.hip", "topk_device.h", "attn_device.h", "device_common.h", "block_ops.h", "launch.h"]
+_STEP_SOURCES = ["step.hip", "topk_device.h", "attn_device.h", "device_common.h", "block_ops.h", "launch.h",
+                 "page_format.h"]
 KERNEL_SOURCES = {
     "sparse_decode_kernel": _STEP_SOURCES,
     "index_topk_kernel": _STEP_SOURCES,
     "pa_decode_kernel": _STEP_SOURCES,
+    "sparse_decode_fp8_kernel": _STEP_SOURCES,
+    "pa_decode_fp8_kernel": _STEP_SOURCES,
     "insert_kernel": ["pages.hip", "device_common.h", "launch.h"],
 }
 
@@ -85,6 +89,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    p.add_argument("--cache", default="mxfp4", choices=["mxfp4", "fp8"],
+                   help="cache page format (fp8: the older build's e4m3 pages, same shapes)")
     p.add_argument("--copies", type=int, default=4, help="pool replicas rotated over (1 = warm cache)")
     p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
     p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
@@ -110,10 +116,12 @@ def copy_calibration():
 
 
 def algorithmic_bytes(w, sel):
-    """(index bytes, K+V bytes) the step must read: 68 B per index row of every
-    valid token once per request, 2 x 68 B per selected (or, dense, valid)
-    token once per request (union over the request's query tokens)."""
-    idx_bytes = int(np.sum(w.seq_lens.astype(np.int64))) * ROW_BYTES if w.sparse else 0
+    """(index bytes, K+V bytes) the step must read: one row (68 B MXFP4, 128 B
+    fp8) per index row of every valid token once per request, 2 rows per
+    selected (or, dense, valid) token once per request (union over the
+    request's query tokens)."""
+    row = ROW_BYTES[w.cache]
+    idx_bytes = int(np.sum(w.seq_lens.astype(np.int64))) * row if w.sparse else 0
     kv_tokens = 0
     for b in range(w.B):
         if sel is None:
@@ -121,7 +129,7 @@ def algorithmic_bytes(w, sel):
         else:
             rows = sel[b * w.T : (b + 1) * w.T]
             kv_tokens += int(np.unique(rows[rows >= 0]).size)
-    return idx_bytes, 2 * ROW_BYTES * kv_tokens
+    return idx_bytes, 2 * row * kv_tokens
 
 
 def cpu_baseline(w, n_sample):
@@ -130,6 +138,7 @@ def cpu_baseline(w, n_sample):
 
     threads = len(os.sched_getaffinity(0))
     pos = decode.query_positions(w.seq_lens, w.T)
+    row = ROW_BYTES[w.cache]
     n = min(n_sample, w.N)
     t0 = time.perf_counter()
     done_bytes = 0
@@ -140,9 +149,9 @@ def cpu_baseline(w, n_sample):
         if w.sparse:
             s = decode.index_scores(w.index_q[i], w.index_pool, bt, pos[i])
             sel = decode.topk(s, w.k)
-            done_bytes += (pos[i] + 1) * ROW_BYTES
-        decode.decode_one(w.q[i], w.k_pool, w.v_pool, bt, pos[i], w.scale, sel)
-        done_bytes += 2 * ROW_BYTES * (len(sel) if sel is not None else pos[i] + 1)
+            done_bytes += (pos[i] + 1) * row
+        decode.decode_one(w.q[i], w.k_pool, w.v_pool, bt, pos[i], w.scale, sel, k_scale=w.k_scale, v_scale=w.v_scale)
+        done_bytes += 2 * row * (len(sel) if sel is not None else pos[i] + 1)
     dt = time.perf_counter() - t0
     return {
         "value": round(done_bytes / dt / 1e9, 4),
@@ -212,7 +221,8 @@ def main():
 
     spd.load_library()
     dev = torch.device("cuda:0")
-    w = workload(args.workload)
+    w = workload(args.workload, cache=args.cache)
+    f8 = args.cache == "fp8"
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -237,15 +247,26 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step(c):
-        if w.sparse:
+        if w.sparse and f8:
+            spd.mono_sparse_decode_fp8(iq, ip[c], q, kp[c], vp[c], bt, sl, w.k, w.scale, w.k_scale, w.v_scale, T=w.T,
+                                       out=out, selected_idx=sel, workspace=ws)
+        elif w.sparse:
             spd.mono_sparse_decode_mxfp4(iq, ip[c], q, kp[c], vp[c], bt, sl, w.k, w.scale, T=w.T, out=out,
                                          selected_idx=sel, workspace=ws)
+        elif f8:
+            spd.mono_pa_decode_fp8(q, kp[c], vp[c], bt, sl, None, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
+                                   workspace=ws_pa)
         else:
             spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, None, w.scale, T=w.T, out=out, workspace=ws_pa)
 
     def two_calls(c):
-        spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
-        spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, sel, w.scale, T=w.T, out=out, workspace=ws_pa)
+        if f8:
+            spd.mono_index_score_topk_fp8(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
+            spd.mono_pa_decode_fp8(q, kp[c], vp[c], bt, sl, sel, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
+                                   workspace=ws_pa)
+        else:
+            spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
+            spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, sel, w.scale, T=w.T, out=out, workspace=ws_pa)
 
     for s in range(args.warmup):
         step(s % copies)
@@ -314,13 +335,13 @@ def main():
 
     # Roofline entry of the step kernel (on dense workloads the attention
     # kernel is the step).
-    dom = "sparse_decode_kernel" if w.sparse else "pa_decode_kernel"
+    dom = ("sparse_decode_kernel" if w.sparse else "pa_decode_kernel").replace("_kernel", "_fp8_kernel" if f8 else "_kernel")
     dom_bytes = bytes_step
     dom_us = kt.mean_us[dom]
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     # The cache insert (run last: it rewrites the decoded tokens' rows).
     ins = None
-    if w.sparse and not args.skip_insert:
+    if w.sparse and not f8 and not args.skip_insert:
         ins = time_insert(spd, torch, dev, w, kp, vp, ip, min(K, 100))
     cpu = None
     if args.cpu_sample > 0:
@@ -345,6 +366,7 @@ def main():
             "T": w.T,
             "context": int(w.seq_lens.max()) if w.T == 1 else [int(w.seq_lens.min()), int(w.seq_lens.max())],
             "k": w.k,
+            "cache": w.cache,
             "pool_copies_rotated": copies,
         },
         "step_us": round(ms_per_step * 1e3, 2),
