@@ -213,6 +213,41 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Indexer context parallelism, emulated on one GPU.  Page
+ * "vllm.models.minimax_m3.amd.mono.weights", _build_cp_qkv: every rank keeps
+ * all ranks' index-q heads, so rank r can score its share of every
+ * sequence's index pages for all heads; each head's candidates then go to
+ * the head's owner, which keeps its top-k.  Readings: shard r of G owns
+ * block-table columns [r*c, min(W, (r+1)*c)), c = ceil(W/G); a shard emits
+ * per query token the top-k (position, score) pairs among its tokens that
+ * the query sees, by the index call's rule; the owner merges the G lists by
+ * the same rule.  The merged selection equals the index call's.
+ *
+ * mono_index_score_topk_window: mono_index_score_topk (same arguments and
+ * workspace) restricted to the tokens of block-table columns
+ * [page_lo, page_hi) (0 <= page_lo < page_hi <= bt_stride).
+ * selected_idx_dev receives absolute token positions; a query that sees no
+ * token of the window gets a row of -1.  selected_scores_dev should be given
+ * (the merge needs the scores).
+ *
+ * mono_topk_merge: cand_idx_dev int32 [G, N, k_in] (positions, < 0 = empty
+ * slot) and cand_scores_dev fp32 [G, N, k_in] -> out_idx_dev int32
+ * [N, k_out] (sorted by rank: highest score first, ties to the lower
+ * position, NaN last; -1 padding) and out_scores_dev (NULL or fp32
+ * [N, k_out], NaN padding).  A position must not appear in two lists.
+ * G * k_in <= 8192 (else MONO_ENOTSUP).  No workspace.
+ * ------------------------------------------------------------------------- */
+int mono_index_score_topk_window(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                                 int64_t num_pages, const int32_t* block_table_dev, int bt_stride,
+                                 const int32_t* seq_lens_dev, int B, int T, int k, int page_lo,
+                                 int page_hi, int32_t* selected_idx_dev,
+                                 float* selected_scores_dev, void* ws_dev, size_t ws_bytes,
+                                 void* stream);
+int mono_topk_merge(const int32_t* cand_idx_dev, const float* cand_scores_dev, int G, int64_t N,
+                    int k_in, int k_out, int32_t* out_idx_dev, float* out_scores_dev,
+                    void* stream);
+
+/* ---------------------------------------------------------------------------
  * The same step over fp8 caches (the older build's format: page
  * "vllm.models.minimax_m3.amd.mono.weights", SparseMoeLayer, names an fp8
  * index cache [blocks, block, head_dim] with shared block ids and the KV
@@ -310,7 +345,7 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev,
  * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
  * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
  * ------------------------------------------------------------------------- */
-#define MONO_NUM_KERNELS 12
+#define MONO_NUM_KERNELS 13
 int mono_profile_start(int capacity);
 int mono_profile_stop(double* total_ms, int* launches, int n);
 const char* mono_kernel_name(int id);

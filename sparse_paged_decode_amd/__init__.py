@@ -19,6 +19,11 @@ or both in one launch:
 The same step over the older build's fp8 (e4m3) caches, with per-tensor K/V
 scales: mono_index_score_topk_fp8, mono_pa_decode_fp8, mono_sparse_decode_fp8.
 
+Indexer context parallelism, emulated on one GPU (G page-window shard scans
+of all index heads, then a merge of each head's candidates):
+indexer_cp_topk, built on mono_index_score_topk(page_window=...) and
+mono_topk_merge.
+
 New tokens' K, V and index-key rows enter the pages through the int64 slot
 mapping (dispatch page, _slots_shared):
 
@@ -42,8 +47,10 @@ from ._binding import (  # noqa: F401
     MonoError,
     Workspace,
     check_device_errors,
+    cp_shard_windows,
     fp8_pages_dequant_bf16,
     index_score_topk_workspace_bytes,
+    indexer_cp_topk,
     load_library,
     mono_index_score_topk,
     mono_index_score_topk_fp8,
@@ -52,6 +59,7 @@ from ._binding import (  # noqa: F401
     mono_pa_decode_mxfp4,
     mono_sparse_decode_fp8,
     mono_sparse_decode_mxfp4,
+    mono_topk_merge,
     mxfp4_page_views,
     mxfp4_pages_dequant,
     mxfp4_pages_dequant_bf16,

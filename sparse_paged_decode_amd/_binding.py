@@ -56,6 +56,8 @@ EXPORTED_SYMBOLS = (
     "mono_sparse_decode_mxfp4",
     "mono_insert_mxfp4",
     "mono_index_score_topk_fp8",
+    "mono_index_score_topk_window",
+    "mono_topk_merge",
     "mono_pa_decode_fp8",
     "mono_sparse_decode_fp8",
     "fp8_pages_dequant_bf16",
@@ -104,6 +106,8 @@ def load_library(path=LIB_PATH):
         "mono_sparse_decode_mxfp4": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, SZ, P]),
         "mono_insert_mxfp4": (I, [P, P, P, P, I64, I, P, P, P, I64, P, P]),
         "mono_index_score_topk_fp8": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
+        "mono_index_score_topk_window": (I, [P, P, I64, P, I, P, I, I, I, I, I, P, P, P, SZ, P]),
+        "mono_topk_merge": (I, [P, P, I, I64, I, I, P, P, P]),
         "mono_pa_decode_fp8": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, F, F, P, P, SZ, P]),
         "mono_sparse_decode_fp8": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, F, F, P, P, P, SZ, P]),
         "fp8_pages_dequant_bf16": (I, [P, P, I64, P]),
@@ -319,16 +323,18 @@ def pa_decode_workspace_bytes(B, T, kv_heads, bt_stride, k, sparse):
 
 
 def mono_index_score_topk(index_q, index_pages, block_table, seq_lens, k, *, T=1, out=None,
-                          out_scores=None, return_scores=False, workspace=None):
+                          out_scores=None, return_scores=False, workspace=None, page_window=None):
     """Top-k token positions per query token by fp32 index score.
 
     index_q: bf16 ``[B*T, 128]``; index_pages: uint8 ``[P, 8704]``;
     block_table: int32 ``[>=B, W]`` row-contiguous; seq_lens: int32 ``[>=B]``.
     Returns int32 ``[B*T, k]`` (any order within a row, -1 padding), and the
     fp32 scores of the selected tokens too if ``return_scores``.
+    ``page_window=(lo, hi)`` restricts the tokens to block-table columns
+    ``[lo, hi)`` (one shard of the indexer's context parallelism).
     """
     return _index_topk("mxfp4", index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores,
-                       workspace)
+                       workspace, page_window)
 
 
 def mono_index_score_topk_fp8(index_q, index_pages, block_table, seq_lens, k, *, T=1, out=None,
@@ -338,7 +344,8 @@ def mono_index_score_topk_fp8(index_q, index_pages, block_table, seq_lens, k, *,
                        workspace)
 
 
-def _index_topk(fmt, index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores, workspace):
+def _index_topk(fmt, index_q, index_pages, block_table, seq_lens, k, T, out, out_scores, return_scores, workspace,
+                page_window=None):
     lib = load_library()
     page_bytes, fn = (PAGE_BYTES, lib.mono_index_score_topk) if fmt == "mxfp4" else \
         (FP8_PAGE_BYTES, lib.mono_index_score_topk_fp8)
@@ -363,10 +370,84 @@ def _index_topk(fmt, index_q, index_pages, block_table, seq_lens, k, T, out, out
     nbytes = lib.mono_index_score_topk_workspace(B, T, bt_stride, k)
     _need(nbytes > 0, "invalid shape for mono_index_score_topk")
     ws = _workspace(workspace, dev, nbytes, "topk")
-    _check(fn(
-        _ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table), bt_stride,
-        _ptr(seq_lens), B, T, k, _ptr(out), _ptr(out_scores), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    if page_window is None:
+        _check(fn(
+            _ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table), bt_stride,
+            _ptr(seq_lens), B, T, k, _ptr(out), _ptr(out_scores), _ptr(ws.buf), ws.nbytes, _stream(dev)))
+    else:
+        _need(fmt == "mxfp4", "page windows are for MXFP4 index pools")
+        lo, hi = (int(x) for x in page_window)
+        _check(lib.mono_index_score_topk_window(
+            _ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table), bt_stride,
+            _ptr(seq_lens), B, T, k, lo, hi, _ptr(out), _ptr(out_scores), _ptr(ws.buf), ws.nbytes, _stream(dev)))
     return (out, out_scores) if return_scores else out
+
+
+def mono_topk_merge(cand_idx, cand_scores, k, *, out=None, out_scores=None):
+    """Merge G top-k lists per query token: int32/fp32 ``[G, N, k_in]`` -> (int32 ``[N, k]``, fp32 ``[N, k]``).
+
+    Rows come out in rank order (highest score first, ties to the lower
+    position, NaN last), padded with -1 / NaN.
+    """
+    lib = load_library()
+    _need(cand_idx.dtype == torch.int32 and cand_scores.dtype == torch.float32, "candidates must be int32 / fp32")
+    _need(cand_idx.dim() == 3 and cand_idx.shape == cand_scores.shape, "candidates must be [G, N, k_in], alike")
+    _need(cand_idx.is_contiguous() and cand_scores.is_contiguous(), "candidates must be contiguous")
+    G, N, k_in = cand_idx.shape
+    dev = _on_gpu(cand_idx, cand_scores)
+    k = int(k)
+    if out is None:
+        out = torch.empty((N, k), dtype=torch.int32, device=dev)
+    if out_scores is None:
+        out_scores = torch.empty((N, k), dtype=torch.float32, device=dev)
+    _need(tuple(out.shape) == (N, k) and out.dtype == torch.int32 and out.is_contiguous(), "out must be int32 [N, k]")
+    _need(tuple(out_scores.shape) == (N, k) and out_scores.dtype == torch.float32 and out_scores.is_contiguous(),
+          "out_scores must be fp32 [N, k]")
+    _check(lib.mono_topk_merge(_ptr(cand_idx), _ptr(cand_scores), G, N, k_in, k, _ptr(out), _ptr(out_scores),
+                               _stream(dev)))
+    return out, out_scores
+
+
+def cp_shard_windows(bt_width, shards):
+    """Page windows ``[(lo, hi), ...]``: shard r owns columns [r*c, min(W, (r+1)*c)), c = ceil(W / shards)."""
+    c = -(-int(bt_width) // int(shards))
+    return [(min(r * c, bt_width), min((r + 1) * c, bt_width)) for r in range(shards)]
+
+
+def indexer_cp_topk(index_q_heads, index_pages, block_table, seq_lens, k, *, T=1, shards=None, workspace=None):
+    """Indexer context parallelism on one GPU: G shard scans, then one merge per head.
+
+    index_q_heads: bf16 ``[H, B*T, 128]`` (every rank's index-q head).  Shard
+    r scores block-table columns ``cp_shard_windows(W, G)[r]`` of every
+    request for all H heads (one window launch, the heads stacked as
+    requests) and emits its top-k (position, score) pairs; the merge keeps
+    each head's top-k over the G lists.  ``shards`` defaults to H.
+    Returns int32 ``[H, B*T, k]`` in rank order, -1 padded.
+    """
+    _need(index_q_heads.dim() == 3 and index_q_heads.shape[2] == HEAD_DIM and index_q_heads.dtype == torch.bfloat16,
+          "index_q_heads must be bf16 [H, B*T, 128]")
+    H, N = index_q_heads.shape[0], index_q_heads.shape[1]
+    G = H if shards is None else int(shards)
+    _need(G >= 1, "shards must be >= 1")
+    B = _check_tables(block_table, seq_lens, N, T)
+    dev = _on_gpu(index_q_heads, index_pages, block_table, seq_lens)
+    W = block_table.shape[1]
+    # The heads become H copies of the batch, one after another.
+    iq = index_q_heads.reshape(H * N, HEAD_DIM).contiguous()
+    bt = block_table[:B].repeat(H, 1).contiguous()
+    sl = seq_lens[:B].repeat(H).contiguous()
+    k = int(k)
+    cand = torch.empty((G, H * N, k), dtype=torch.int32, device=dev)
+    cand_s = torch.empty((G, H * N, k), dtype=torch.float32, device=dev)
+    for r, (lo, hi) in enumerate(cp_shard_windows(W, G)):
+        if lo >= hi:  # more shards than table columns: an empty shard
+            cand[r].fill_(-1)
+            cand_s[r].fill_(float("nan"))
+            continue
+        mono_index_score_topk(iq, index_pages, bt, sl, k, T=T, out=cand[r], out_scores=cand_s[r],
+                              workspace=workspace, page_window=(lo, hi))
+    out, _ = mono_topk_merge(cand, cand_s, k)
+    return out.view(H, N, k)
 
 
 def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_idx=None,

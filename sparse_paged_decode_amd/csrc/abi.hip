@@ -21,6 +21,7 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 constexpr int kMaxBtStride = 1 << 20;  // 2^27 tokens per request
 constexpr int kMaxHeads = 64;
+constexpr int kMergeMaxCandidates = 8192;  // 64 KiB of LDS keys per workgroup
 }  // namespace
 
 int set_error(int code, const char* fmt, ...) {
@@ -45,7 +46,8 @@ Profiler g_prof;
 const char* const kKernelNames[kNumKernels] = {
     "pack_kernel",          "unpack_kernel",         "dequant_f32_kernel",  "dequant_bf16_kernel",
     "index_topk_kernel",    "pa_decode_kernel",      "sparse_decode_kernel", "insert_kernel",
-    "index_topk_fp8_kernel", "pa_decode_fp8_kernel", "sparse_decode_fp8_kernel", "dequant_fp8_bf16_kernel"};
+    "index_topk_fp8_kernel", "pa_decode_fp8_kernel", "sparse_decode_fp8_kernel", "dequant_fp8_bf16_kernel",
+    "topk_merge_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -95,9 +97,12 @@ bool bad_tensor_scale(float x) { return !(x > 0.f) || x == __builtin_inff(); }
 int index_topk_impl(int fmt, const char* what, const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
                     int64_t num_pages, const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
                     int B, int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, void* stream, int page_lo = 0, int page_hi = -1) {
   clear_error();
   if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (page_hi < 0) page_hi = bt_stride;
+  if (page_lo < 0 || page_lo >= page_hi || page_hi > bt_stride)
+    return set_error(MONO_EINVAL, "%s: page window [%d, %d) not inside [0, %d)", what, page_lo, page_hi, bt_stride);
   if (!index_q_dev || !index_pages_dev || !block_table_dev || !seq_lens_dev || !selected_idx_dev || !ws_dev)
     return set_error(MONO_EINVAL, "%s: NULL buffer", what);
   if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
@@ -105,8 +110,10 @@ int index_topk_impl(int fmt, const char* what, const uint16_t* index_q_dev, cons
       !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4) ||
       !aligned(selected_scores_dev, 4))
     return set_error(MONO_EINVAL, "%s: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment", what);
-  const StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
+  StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
   if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  lay.win_lo = page_lo;
+  lay.win_hi = page_hi;
   StepArgs a{};
   a.fmt = fmt;
   a.index_q = index_q_dev;
@@ -266,6 +273,32 @@ int mono_index_score_topk(const uint16_t* index_q_dev, const uint8_t* index_page
   return index_topk_impl(kFmtMxfp4, "mono_index_score_topk", index_q_dev, index_pages_dev, num_pages, block_table_dev,
                          bt_stride, seq_lens_dev, B, T, k, selected_idx_dev, selected_scores_dev, ws_dev, ws_bytes,
                          stream);
+}
+
+int mono_index_score_topk_window(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                                 const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B,
+                                 int T, int k, int page_lo, int page_hi, int32_t* selected_idx_dev,
+                                 float* selected_scores_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  return index_topk_impl(kFmtMxfp4, "mono_index_score_topk_window", index_q_dev, index_pages_dev, num_pages,
+                         block_table_dev, bt_stride, seq_lens_dev, B, T, k, selected_idx_dev, selected_scores_dev,
+                         ws_dev, ws_bytes, stream, page_lo, page_hi);
+}
+
+int mono_topk_merge(const int32_t* cand_idx_dev, const float* cand_scores_dev, int G, int64_t N, int k_in, int k_out,
+                    int32_t* out_idx_dev, float* out_scores_dev, void* stream) {
+  clear_error();
+  if (G < 1 || k_in < 1 || k_out < 1 || N < 0 || N > 0x7fffffff)
+    return set_error(MONO_EINVAL, "mono_topk_merge: need G, k_in, k_out >= 1 and 0 <= N < 2^31");
+  if ((int64_t)G * k_in > kMergeMaxCandidates)
+    return set_error(MONO_ENOTSUP, "mono_topk_merge: G * k_in = %lld exceeds %d candidates", (long long)G * k_in,
+                     kMergeMaxCandidates);
+  if (N == 0) return MONO_OK;
+  if (!cand_idx_dev || !cand_scores_dev || !out_idx_dev) return set_error(MONO_EINVAL, "mono_topk_merge: NULL buffer");
+  if (!aligned(cand_idx_dev, 4) || !aligned(cand_scores_dev, 4) || !aligned(out_idx_dev, 4) ||
+      !aligned(out_scores_dev, 4))
+    return set_error(MONO_EINVAL, "mono_topk_merge: buffers need 4-byte alignment");
+  return launch_topk_merge(cand_idx_dev, cand_scores_dev, G, (int)N, k_in, k_out, out_idx_dev, out_scores_dev,
+                           (hipStream_t)stream);
 }
 
 int mono_index_score_topk_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,

@@ -27,6 +27,7 @@ enum KernelId {
   kKPaDecodeFp8,
   kKStepFp8,
   kKDequantFp8Bf16,
+  kKTopkMerge,
   kNumKernels
 };
 // When timing is on, takes the next pair of timing events for kernel `id`
@@ -53,6 +54,10 @@ int launch_unpack(const uint8_t* pages, uint8_t* codes, uint8_t* scales, int64_t
                   hipStream_t stream);
 int launch_dequant_f32(const uint8_t* pages, float* out, int64_t n_pages, hipStream_t stream);
 int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
+// Merge of G per-shard top-k lists per query token (merge.hip): candidates
+// [G, N, k_in] (positions, -1 = empty; fp32 scores) -> [N, k_out].
+int launch_topk_merge(const int32_t* cand_idx, const float* cand_scores, int G, int N, int k_in, int k_out,
+                      int32_t* out_idx, float* out_scores, hipStream_t stream);
 // fp8 pages [n_pages, 16384] -> bf16 [n_pages, 128, 128] through the step kernel's conversion.
 int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
 // Cache insert: caches c = 0 (K), 1 (V), 2 (index key) with row_heads[c]
@@ -78,7 +83,8 @@ struct StepLayout {
   int mode, B, T, H, k, sparse;
   int q_groups;      // ceil(T / 4) query-token groups per request
   int chunk_pages;   // index pages per scan chunk
-  int chunks;        // scan chunks per query group (bt_stride / chunk_pages, rounded up)
+  int chunks;        // scan chunks per query group (window pages / chunk_pages, rounded up)
+  int win_lo, win_hi;  // page window [win_lo, win_hi) of every request the index items score
   int lcap;          // bt_stride * 128: capacity of a score row
   int slices;        // filter slices per query token (lcap / 4096, rounded up)
   int split_tokens;  // attention candidates per split

@@ -48,6 +48,8 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.chunk_pages = kScanChunkPages;  // launch_step re-balances this to the resident workgroups
   l.chunks = (bt_stride + l.chunk_pages - 1) / l.chunk_pages;
   l.lcap = bt_stride * kPageTokens;
+  l.win_lo = 0;  // the index call over a page window narrows these
+  l.win_hi = bt_stride;
   l.slices = (l.lcap + kSlice - 1) / kSlice;
   const bool index = (mode & kModeIndex) != 0, attn = (mode & kModeAttn) != 0;
   // Attention splits: 256 candidates per workgroup unless that makes more
@@ -194,6 +196,12 @@ __device__ __forceinline__ int group_chunks(int L, int T, int qg, int chunk_page
   return (n_pages + chunk_pages - 1) / chunk_pages;
 }
 
+// Tokens query position pos sees inside the layout's page window (all of
+// 0..pos unless the index call was given a window).
+__device__ __forceinline__ int window_valid(const StepLayout& lay, int pos) {
+  return max(0, min(pos + 1, lay.win_hi * kPageTokens) - lay.win_lo * kPageTokens);
+}
+
 template <int TQ>
 union StepLds {
   ScanLds<TQ> scan;
@@ -216,6 +224,7 @@ __device__ __forceinline__ SelectArgs select_args(const StepArgs& a, const StepL
   sa.cand_cnt = ctrl + lay.cand_cnt + i;
   sa.err = err;
   sa.n_valid = n_valid;
+  sa.j_base = lay.win_lo * kPageTokens;
   sa.k = lay.k;
   return sa;
 }
@@ -228,7 +237,7 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
   const int T = lay.T, b = (int)i / T, t = (int)i % T;
   const int L = a.seq_lens[b];
   if (L >= T && L <= lay.lcap) {  // an invalid length was reported by the scan items
-    select_query(select_args(a, lay, (int)i, L - T + t + 1, ctrl, err), lds.resolve);
+    select_query(select_args(a, lay, (int)i, window_valid(lay, L - T + t), ctrl, err), lds.resolve);
     wait_vmem();
   }
   __syncthreads();
@@ -252,23 +261,26 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
     if (c == 0 && qg == 0 && thread_index() == 0) raise_error(err, kErrSeqLen);
   } else {
     int tq, n_pages;
-    const int nchunks = group_chunks(L, T, qg, lay.chunk_pages, tq, n_pages);
+    group_chunks(L, T, qg, lay.chunk_pages, tq, n_pages);
+    // The group's pages inside the window, relative to its first page.
+    const int n_rel = max(0, min(n_pages, lay.win_hi) - lay.win_lo);
+    const int nchunks = (n_rel + lay.chunk_pages - 1) / lay.chunk_pages;
     if (c < nchunks) {
       const int q0 = b * T + t0;
       ScanArgs sa;
       sa.index_q = a.index_q;
       sa.pages = a.index_pages;
       sa.num_pages = a.num_pages;
-      sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
+      sa.bt_row = a.block_table + (size_t)b * a.bt_stride + lay.win_lo;
       sa.q_scores = reinterpret_cast<float*>(a.ws + lay.scores) + (size_t)q0 * lay.lcap;
       sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)q0 * kHistBins;
       sa.err = err;
       sa.lcap = lay.lcap;
       sa.q0 = q0;
-      sa.pos0 = L - T + t0;
+      sa.pos0 = L - T + t0 - lay.win_lo * kPageTokens;  // scores are indexed from the window's first token
       sa.tq = tq;
       sa.p_begin = c * lay.chunk_pages;
-      sa.p_end = min(sa.p_begin + lay.chunk_pages, n_pages);
+      sa.p_end = min(sa.p_begin + lay.chunk_pages, n_rel);
       scan_chunk<TQ, Fmt>(sa, lds);
       wait_vmem();  // scores and histogram updates are complete before the arrival
     }
@@ -297,8 +309,10 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   const int T = lay.T, b = i / T, t = i % T;
   const int L = a.seq_lens[b];
   const bool valid = L >= T && L <= lay.lcap;  // an invalid length was reported by the scan items
-  const int n_valid = L - T + t + 1;
-  const int n_slices = valid ? (n_valid + kSlice - 1) / kSlice : 0;
+  const int n_valid = window_valid(lay, L - T + t);
+  // A query that sees no token of the window still runs slice 0, which
+  // writes its -1 padding.
+  const int n_slices = valid ? max(1, (n_valid + kSlice - 1) / kSlice) : 0;
 
   const SelectArgs sa = select_args(a, lay, i, n_valid, ctrl, err);
   if (s < n_slices) {
@@ -456,10 +470,10 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
     // Scan chunks sized so the scan items make about one round of the
     // resident workgroups (all of them start together and end together).
     const int groups = lay.B * lay.q_groups;
-    const int bt_stride = lay.lcap / kPageTokens;
+    const int span = lay.win_hi - lay.win_lo;  // pages of the window (the whole table by default)
     const int per_group = std::max(1, cap / std::max(1, groups));
-    lay.chunk_pages = std::min(kMaxChunkPages, std::max(1, (bt_stride + per_group - 1) / per_group));
-    lay.chunks = (bt_stride + lay.chunk_pages - 1) / lay.chunk_pages;
+    lay.chunk_pages = std::min(kMaxChunkPages, std::max(1, (span + per_group - 1) / per_group));
+    lay.chunks = (span + lay.chunk_pages - 1) / lay.chunk_pages;
     lay.n_scan = (uint32_t)((size_t)groups * lay.chunks);
     lay.n_ready0 = lay.n_scan;
     // Rows of at most kSelectMax scores are selected by one workgroup each
@@ -468,7 +482,7 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
     // workgroups; with fewer query tokens, slices spread each selection
     // over more compute units and finish sooner.
     const size_t N = (size_t)lay.B * lay.T;
-    if (lay.lcap <= kSelectMax && N * (size_t)lay.slices > 2 * (size_t)cap) {
+    if ((size_t)span * kPageTokens <= kSelectMax && N * (size_t)lay.slices > 2 * (size_t)cap) {
       lay.select_mode = 1;
       lay.n_filter = 0u;
       lay.n_select = lay.T > 1 ? (uint32_t)N : 0u;

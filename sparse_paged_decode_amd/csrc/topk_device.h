@@ -209,6 +209,7 @@ struct SelectArgs {
   uint32_t* err;
   int n_valid;
   int k;
+  int j_base;           // position of score 0 (the first token of the page window)
 };
 
 // Slots past k would mean inconsistent counts; they are refused and flagged.
@@ -217,7 +218,7 @@ __device__ __forceinline__ void put_selection(const SelectArgs& a, uint32_t slot
     raise_error(a.err, kErrSelection);
     return;
   }
-  store_coherent(reinterpret_cast<uint32_t*>(a.out + slot), (uint32_t)j);
+  store_coherent(reinterpret_cast<uint32_t*>(a.out + slot), (uint32_t)(j + a.j_base));
   if (a.out_scores) store_coherent(a.out_scores + slot, score);
 }
 
