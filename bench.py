@@ -21,8 +21,10 @@ pass of the same steps with HIP events recorded around each launch on its
 stream; the two-call form of the step (index call, then attention call)
 timed the same way, for reference; the MXFP4 cache insert (the decoded
 tokens' K, V and index-key rows written through their slots, and a
-32768-token prefill-sized insert) by kernel time; and the CPU oracle timed on
-a bounded sample of the same workload.
+32768-token prefill-sized insert) by kernel time; the indexer's
+context-parallel emulation (4 index heads over 4 page-window shards, then the
+merge) by kernel time; and the CPU oracle timed on a bounded sample of the
+same workload.
 """
 
 import argparse
@@ -95,6 +97,7 @@ def parse():
     p.add_argument("--cpu-sample", type=int, default=64, help="query tokens timed on the CPU oracle (0 = skip)")
     p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
     p.add_argument("--skip-insert", action="store_true", help="do not time the cache insert")
+    p.add_argument("--skip-cp", action="store_true", help="do not time the indexer context-parallel emulation")
     p.add_argument("--skip-two-call", action="store_true",
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -203,6 +206,44 @@ def time_insert(spd, torch, dev, w, kp, vp, ip, reps):
                      "achieved_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
                      "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)}
     return res
+
+
+def time_cp(spd, torch, dev, w, iq, ip, bt, sl, reps, heads=4):
+    """Kernel times of the indexer context-parallel emulation: `heads` index heads over `heads` shards.
+
+    One shard launch scores its page window of every request for all heads
+    (the work one rank of the context-parallel indexer does); the merge keeps
+    each head's top-k.  For reference, the one-head index call over whole
+    sequences (the work without context parallelism, per head).
+    """
+    rng = np.random.default_rng(90)
+    extra = torch.from_numpy(rng.standard_normal((heads - 1, w.N, 128), dtype=np.float32)).to(dev).to(torch.bfloat16)
+    q_heads = torch.cat([iq[None], extra]).contiguous()
+    ws = spd.Workspace(dev)
+    for _ in range(3):
+        spd.indexer_cp_topk(q_heads, ip, bt, sl, w.k, T=w.T, shards=heads, workspace=ws)
+    torch.cuda.synchronize(dev)
+    with spd.KernelTimer(capacity=(heads + 1) * reps + 8) as kt:
+        for _ in range(reps):
+            spd.indexer_cp_topk(q_heads, ip, bt, sl, w.k, T=w.T, shards=heads, workspace=ws)
+        torch.cuda.synchronize(dev)
+    W = bt.shape[1]
+    lens = w.seq_lens.astype(np.int64)
+    win_bytes = []
+    for lo, hi in spd.cp_shard_windows(W, heads):
+        toks = np.clip(lens, lo * 128, hi * 128) - lo * 128
+        win_bytes.append(int(toks.sum()) * ROW_BYTES["mxfp4"])
+    shard_us = kt.mean_us["index_topk_kernel"]
+    return {
+        "heads": heads,
+        "shards": heads,
+        "shard_kernel_us_mean": round(shard_us, 2),
+        "merge_kernel_us_mean": round(kt.mean_us["topk_merge_kernel"], 2),
+        "shard_index_bytes_one_rank": max(win_bytes),
+        "shard_index_bytes_read_here": heads * max(win_bytes),
+        "note": "each shard launch re-reads its window once per head (heads stacked as requests); a rank of the "
+                "context-parallel indexer would read it once for all heads",
+    }
 
 
 def main():
@@ -343,6 +384,9 @@ def main():
     ins = None
     if w.sparse and not f8 and not args.skip_insert:
         ins = time_insert(spd, torch, dev, w, kp, vp, ip, min(K, 100))
+    cp = None
+    if w.sparse and not f8 and not args.skip_cp:
+        cp = time_cp(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(w, args.cpu_sample)
@@ -390,6 +434,7 @@ def main():
             "source_digest": kernel_digest(dom),
         },
         "insert": ins,
+        "cp_emulation": cp,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
         "device": torch.cuda.get_device_name(dev),

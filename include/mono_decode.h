@@ -232,10 +232,11 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
  *
  * mono_topk_merge: cand_idx_dev int32 [G, N, k_in] (positions, < 0 = empty
  * slot) and cand_scores_dev fp32 [G, N, k_in] -> out_idx_dev int32
- * [N, k_out] (sorted by rank: highest score first, ties to the lower
- * position, NaN last; -1 padding) and out_scores_dev (NULL or fp32
- * [N, k_out], NaN padding).  A position must not appear in two lists.
- * G * k_in <= 8192 (else MONO_ENOTSUP).  No workspace.
+ * [N, k_out]: the min(k_out, candidates) best by the index call's rule
+ * (higher score, ties to the lower position, NaN last), in any order, then
+ * -1 padding; out_scores_dev (NULL or fp32 [N, k_out]) their scores, NaN
+ * padding.  A position must not appear in two lists.  G * k_in <= 8192
+ * (else MONO_ENOTSUP).  No workspace.
  * ------------------------------------------------------------------------- */
 int mono_index_score_topk_window(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
                                  int64_t num_pages, const int32_t* block_table_dev, int bt_stride,

@@ -386,8 +386,9 @@ def _index_topk(fmt, index_q, index_pages, block_table, seq_lens, k, T, out, out
 def mono_topk_merge(cand_idx, cand_scores, k, *, out=None, out_scores=None):
     """Merge G top-k lists per query token: int32/fp32 ``[G, N, k_in]`` -> (int32 ``[N, k]``, fp32 ``[N, k]``).
 
-    Rows come out in rank order (highest score first, ties to the lower
-    position, NaN last), padded with -1 / NaN.
+    Each row holds the best min(k, candidates) by the index call's rule
+    (higher score, ties to the lower position, NaN last) in any order, then
+    -1 / NaN padding.
     """
     lib = load_library()
     _need(cand_idx.dtype == torch.int32 and cand_scores.dtype == torch.float32, "candidates must be int32 / fp32")
@@ -422,7 +423,7 @@ def indexer_cp_topk(index_q_heads, index_pages, block_table, seq_lens, k, *, T=1
     request for all H heads (one window launch, the heads stacked as
     requests) and emits its top-k (position, score) pairs; the merge keeps
     each head's top-k over the G lists.  ``shards`` defaults to H.
-    Returns int32 ``[H, B*T, k]`` in rank order, -1 padded.
+    Returns int32 ``[H, B*T, k]`` (any order within a row, -1 padding).
     """
     _need(index_q_heads.dim() == 3 and index_q_heads.shape[2] == HEAD_DIM and index_q_heads.dtype == torch.bfloat16,
           "index_q_heads must be bf16 [H, B*T, 128]")
