@@ -315,8 +315,10 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   const int n_slices = valid ? max(1, (n_valid + kSlice - 1) / kSlice) : 0;
 
   const SelectArgs sa = select_args(a, lay, i, n_valid, ctrl, err);
-  if (s < n_slices) {
-    filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
+  BinSplit split{0, 0u, 0u};
+  const bool sliced = s < n_slices;
+  if (sliced) {
+    split = filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
     wait_vmem();
   }
   // Every slice slot arrives; the last one resolves the selection and
@@ -325,14 +327,24 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   if (thread_index() == 0) s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(lay.slices - 1);
   __syncthreads();
   if (!s_flag) return;
+  // Attention items of token i are numbered split-major (split * H + h), so
+  // the splits whose candidates are final can be published as one range:
+  // the tokens above the threshold bin fill the first output slots before
+  // the rest are picked, and their splits run while this workgroup picks.
+  const uint32_t H = (uint32_t)lay.H, S = (uint32_t)lay.n_splits;
+  const uint32_t first = (uint32_t)i * H * S;
+  uint32_t n_early = 0;
   if (valid) {
-    resolve_query(sa, lds.resolve);
+    resolve_query(sa, lds.resolve, sliced, split, [&](uint32_t n_final) {
+      if (lay.mode != kModeFused) return;
+      n_early = n_final >= (uint32_t)lay.k ? S : min(S, n_final / (uint32_t)lay.split_tokens);
+      if (n_early) publish(lay, ctrl, kItemAttn, first, n_early * H, err, s_pub);
+    });
     wait_vmem();
     __syncthreads();
   }
-  if (lay.mode == kModeFused)
-    publish(lay, ctrl, kItemAttn, (uint32_t)i * (uint32_t)(lay.H * lay.n_splits), (uint32_t)(lay.H * lay.n_splits),
-            err, s_pub);
+  if (lay.mode == kModeFused && n_early < S)
+    publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
 }
 
 template <int TQ, class Fmt>
@@ -341,7 +353,7 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   const int H = lay.H, S = lay.n_splits;
   const int i = (int)(v / (uint32_t)(H * S));
   const int rem = (int)(v % (uint32_t)(H * S));
-  const int h = rem / S, split = rem % S;
+  const int split = rem / H, h = rem % H;  // split-major (filter_item publishes final splits first)
   const int T = lay.T, b = i / T, t = i % T;
   const int L = a.seq_lens[b];
   if (L < T || L > lay.lcap) {

@@ -234,8 +234,10 @@ __device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* hist,
   return find_bin_of_rank(hist, kHistBins, (uint32_t)a.k, scratch);
 }
 
-// Slice [j0, j1) of the scores.
-__device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds) {
+// Slice [j0, j1) of the scores.  Returns the histogram split it used (the
+// bin of the k-th largest score), which the resolve can reuse; count = 0 and
+// above = k when every valid token is selected.
+__device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds) {
   const int tid = thread_index();
   if (a.n_valid <= a.k) {  // at most k valid tokens: all of them, then -1 padding
     for (int j = j0 + tid; j < j1; j += kBlock) put_selection(a, (uint32_t)j, j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
@@ -245,7 +247,7 @@ __device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1
         if (a.out_scores) store_coherent(a.out_scores + s, __uint_as_float(0x7fc00000u));
       }
     }
-    return;
+    return BinSplit{0, (uint32_t)a.k, 0u};
   }
   // The slice's scores are loaded unconditionally (indices clamped inside the
   // row's capacity, masked below) so the loads overlap the histogram's.
@@ -285,6 +287,7 @@ __device__ __forceinline__ void filter_slice(const SelectArgs& a, int j0, int j1
       ++cs;
     }
   }
+  return sp;
 }
 
 // Where pick_in_bin reads the tokens of the threshold bin from.
@@ -386,20 +389,33 @@ __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds
 }
 
 // The remaining tokens of bin B1, once every slice is done.  Leaves the
-// histogram row zero.
-__device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& lds) {
+// histogram row zero.  With `have_known`, `known` is the histogram split a
+// slice of this workgroup already found (the histogram is final before any
+// slice runs); otherwise the histogram is read again.  on_final(n) is called by every
+// thread as soon as the output slots 0..n-1 are final (the tokens above bin
+// B1, which the slices wrote, or all k slots when every valid token is
+// selected), while the candidates are still loading.
+template <class OnFinal>
+__device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& lds, bool have_known, BinSplit known,
+                                              OnFinal on_final) {
   const int tid = thread_index();
-  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  // The first kLdsCand candidates are requested first (entries past the
+  // list's count are never used).
+  constexpr int kPer = kLdsCand / kBlock;
+  uint64_t c[kPer];
+  const bool resolve = a.n_valid > a.k;
+  if (resolve) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
+  }
+  const BinSplit sp = have_known ? known : kth_bin(a, lds.hist, lds.scratch);
+  on_final(resolve ? sp.above : (uint32_t)a.k);
   for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
-  if (a.n_valid <= a.k) return;  // the filter items wrote everything
+  if (!resolve) return;  // the filter items wrote everything
   const uint32_t in_bin = sp.count;
   const bool use_cand = in_bin <= (uint32_t)kCandCap;
   const bool in_lds = in_bin <= (uint32_t)kLdsCand;
   if (in_lds) {
-    constexpr int kPer = kLdsCand / kBlock;
-    uint64_t c[kPer];
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) lds.cand[u * kBlock + tid] = make_uint2((uint32_t)c[u], (uint32_t)(c[u] >> 32));
   }
