@@ -194,3 +194,35 @@ def test_step_many_query_tokens(spd):
             _check_token(w, i, sel_np[i], out_bits)
         for i in range(w.N):
             check_topk_row(sel_np[i], w, i, w.k)
+
+
+def test_step_multiple_kv_heads(spd):
+    """Three KV heads (48 query heads), several attention splits per head and
+    two query tokens per request: every head against the oracle with the
+    selection the call returned (the heads share it)."""
+    w = make_workload("h3step", B=3, T=2, seq_lens=[900, 3000, 5000], bt_width=40, k=700, seed=33,
+                      exp_range=(124, 127))
+    H = 3
+    rng = np.random.default_rng(34)
+    kh = rng.integers(0, 256, size=(w.num_pages, H, 8704), dtype=np.uint8)
+    vh = rng.integers(0, 256, size=(w.num_pages, H, 8704), dtype=np.uint8)
+    kh[..., 8192:] = rng.integers(124, 128, size=(w.num_pages, H, 512))
+    vh[..., 8192:] = rng.integers(124, 128, size=(w.num_pages, H, 512))
+    w.k_pool, w.v_pool = kh, vh
+    w.q = mxfp4.round_to_bf16_bits(rng.standard_normal((w.N, 16 * H, 128)))
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(w.N):
+        check_topk_row(sel_np[i], w, i, w.k)
+        b = i // w.T
+        pos = int(w.seq_lens[b]) - w.T + i % w.T
+        for h in range(H):
+            ref = decode.decode_one(w.q[i, 16 * h : 16 * h + 16], kh, vh, w.block_table[b], pos, w.scale, sel_np[i],
+                                    head=h)
+            vmax = float(np.abs(decode.sequence_rows(vh, w.block_table[b], pos + 1, h)).max())
+            o = mxfp4.bf16_bits_to_f64(out_bits[i, 16 * h : 16 * h + 16])
+            rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+            assert rel <= 5e-3 and np.max(np.abs(o - ref)) <= 1e-2 * vmax, (i, h, rel)

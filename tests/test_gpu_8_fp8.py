@@ -153,3 +153,26 @@ def test_fp8_step_full_size_sampled(spd, number, samples):
         assert np.all(row[n:] == -1) and np.all((row[:n] >= 0) & (row[:n] <= pos[i]))
         assert np.unique(row[:n]).size == n
     assert torch.isfinite(out.float()).all()
+
+
+def test_fp8_step_two_kv_heads(spd):
+    w = make_workload("h2fp8", B=2, T=1, seq_lens=[2000, 4100], bt_width=40, k=600, seed=55, cache="fp8")
+    H = 2
+    rng = np.random.default_rng(56)
+    def pool():
+        bits = rng.integers(0, 256, size=(w.num_pages, H, fp8.PAGE_BYTES), dtype=np.uint8)
+        exp = rng.integers(4, 11, size=bits.shape, dtype=np.uint8)
+        return (bits & 0x87) | (exp << 3)
+    w.k_pool, w.v_pool = pool(), pool()
+    w.q = mxfp4.round_to_bf16_bits(rng.standard_normal((w.N, 16 * H, 128)))
+    d = to_device(w)
+    out, sel = _step(spd, w, d)
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(w.N):
+        check_topk_row(sel_np[i], w, i, w.k)
+        pos = int(w.seq_lens[i]) - 1
+        for h in range(H):
+            ref = decode.decode_one(w.q[i, 16 * h : 16 * h + 16], w.k_pool, w.v_pool, w.block_table[i], pos, w.scale,
+                                    sel_np[i], head=h, k_scale=w.k_scale, v_scale=w.v_scale)
+            o = mxfp4.bf16_bits_to_f64(out_bits[i, 16 * h : 16 * h + 16])
+            assert np.linalg.norm(o - ref) <= 5e-3 * np.linalg.norm(ref), (i, h)
