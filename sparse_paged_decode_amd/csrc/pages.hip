@@ -142,23 +142,22 @@ __global__ __launch_bounds__(256) void dequant_fp8_bf16_kernel(const uint8_t* __
 // 6 saturating; NaN or +-inf anywhere gives byte 0xFF and codes 0; an
 // all-zero block gives byte 0.
 //
-// All of it is integer arithmetic on the bf16 fields, so it is exact and
-// independent of the denormal mode.  A bf16 magnitude with exponent field E
-// and mantissa M is mant * 2^ex with mant = 128 + M, ex = E - 134 (E > 0) or
-// mant = M, ex = -133 (E = 0).  With 4q = 4|v| / 2^(byte-127) = mant * 2^-n,
-// n = byte - 129 - ex, the rounding thresholds of q (0.25, 0.75, 1.25, 1.75,
-// 2.5, 3.5, 5; strict where the lower code is even so that ties go to it)
-// become mant against k << n for k = 1, 3, 5, 7, 10, 14, 20.  The largest
-// element of a block has n = 3 (n = 4 when the byte is clamped at 0), the
-// others larger n; n above 12 puts every threshold above any mant < 256.
-__device__ __forceinline__ uint32_t e2m1_code_of(uint32_t mag, int byte) {
-  const uint32_t E = mag >> 7;
-  const uint32_t mant = E ? (0x80u | (mag & 0x7Fu)) : (mag & 0x7Fu);
-  const int ex = E ? (int)E - 134 : -133;
-  const int n = min(byte - 129 - ex, 12);
-  return (uint32_t)(mant > (1u << n)) + (uint32_t)(mant >= (3u << n)) + (uint32_t)(mant > (5u << n)) +
-         (uint32_t)(mant >= (7u << n)) + (uint32_t)(mant > (10u << n)) + (uint32_t)(mant >= (14u << n)) +
-         (uint32_t)(mant > (20u << n));
+// The element codes are decided in fp32, exactly: a bf16 value converts to
+// fp32 exactly, and q = |v| * 2^(127-byte) (< 8) only changes the exponent
+// (byte <= 252 for any finite bf16 block, so the factor is a normal fp32;
+// the kernel keeps fp32 subnormals, so blocks of bf16 subnormals, whose byte
+// clamps to 0, scale exactly too).  e2m1 is a float format with one mantissa
+// bit whose grid step is 2^(k-1) on [2^k, 2^(k+1)) for k = 1, 2 and 0.5
+// below 2, so with k = floor(log2 q) clamped to [0, 2] the code is
+// 2k + rint(q * 2^(1-k)): rint rounds to nearest with ties to even, which
+// sends every tie to the even code (0.25 -> 0, 0.75 -> 2, 1.25 -> 2,
+// 1.75 -> 4, 2.5 -> 4, 3.5 -> 6, 5 -> 6), and codes above 7 (q >= 7)
+// saturate to 7 (6.0).
+__device__ __forceinline__ uint32_t e2m1_code_of(float v, float scale) {
+  const float q = fabsf(v) * scale;
+  const int k = min(max((int)((__float_as_uint(q) >> 23) & 0xFFu) - 127, 0), 2);
+  const float r = __builtin_rintf(__builtin_amdgcn_ldexpf(q, 1 - k));
+  return min((uint32_t)(2 * k) + (uint32_t)r, 7u);
 }
 
 struct InsertArgs {
@@ -215,18 +214,18 @@ __global__ __launch_bounds__(256) void insert_kernel(InsertArgs a) {
     const int flog2 = E ? (int)E - 127 : -133 + (31 - (int)__builtin_clz(amax & 0x7Fu));
     byte = min(max(flog2 - 2 + 127, 0), 254);
   }
+  const float scale = __uint_as_float((uint32_t)(254 - min(byte, 252)) << 23);  // 2^(127 - byte)
   u32x4_t out;
 #pragma unroll
   for (int L = 0; L < 4; ++L) {  // bf16 elements 8L..8L+7 -> codes in nibbles of word L
     uint32_t w = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t h = (in[L][i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-      uint32_t code = e2m1_code_of(h & 0x7FFFu, byte) | ((h >> 12) & 8u);
-      if (byte == 0xFF) code = 0;
-      w |= code << (4 * i);
+      const uint32_t d = in[L][i >> 1];
+      const uint32_t f = (i & 1) ? (d & 0xFFFF0000u) : (d << 16);  // the bf16 as fp32 bits
+      w |= (e2m1_code_of(__uint_as_float(f), scale) | ((f >> 28) & 8u)) << (4 * i);
     }
-    out[L] = w;
+    out[L] = byte == 0xFF ? 0u : w;
   }
   const int r = (int)(slot & (kPageTokens - 1));
   uint8_t* pg = a.pools[c] + (page * heads + j) * kPageBytes;
