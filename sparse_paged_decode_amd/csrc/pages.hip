@@ -142,24 +142,14 @@ __global__ __launch_bounds__(256) void dequant_fp8_bf16_kernel(const uint8_t* __
 // 6 saturating; NaN or +-inf anywhere gives byte 0xFF and codes 0; an
 // all-zero block gives byte 0.
 //
-// The element codes are decided in fp32, exactly: a bf16 value converts to
-// fp32 exactly, and q = |v| * 2^(127-byte) (< 8) only changes the exponent
-// (byte <= 252 for any finite bf16 block, so the factor is a normal fp32;
-// the kernel keeps fp32 subnormals, so blocks of bf16 subnormals, whose byte
-// clamps to 0, scale exactly too).  e2m1 is a float format with one mantissa
-// bit whose grid step is 2^(k-1) on [2^k, 2^(k+1)) for k = 1, 2 and 0.5
-// below 2, so with k = floor(log2 q) clamped to [0, 2] the code is
-// 2k + rint(q * 2^(1-k)): rint rounds to nearest with ties to even, which
-// sends every tie to the even code (0.25 -> 0, 0.75 -> 2, 1.25 -> 2,
-// 1.75 -> 4, 2.5 -> 4, 3.5 -> 6, 5 -> 6), and codes above 7 (q >= 7)
-// saturate to 7 (6.0).
-__device__ __forceinline__ uint32_t e2m1_code_of(float v, float scale) {
-  const float q = fabsf(v) * scale;
-  const int k = min(max((int)((__float_as_uint(q) >> 23) & 0xFFu) - 127, 0), 2);
-  const float r = __builtin_rintf(__builtin_amdgcn_ldexpf(q, 1 - k));
-  return min((uint32_t)(2 * k) + (uint32_t)r, 7u);
-}
-
+// The element codes come from v_cvt_scalef32_pk_fp4_f32 with the block's
+// e8m0 scale 2^(byte-127): it converts two fp32 values (each bf16 exactly)
+// to e2m1 codes of value / scale, nearest with ties to the even code,
+// saturating at 6, keeping the sign (-0.0 gives code 8), and packs them
+// into one byte, the first in the low nibble.  That is the conversion
+// above; it was checked for every positive finite bf16 value at every scale
+// byte that keeps the quotient below 8, both signs, against the
+// nearest-with-ties-to-even rule.
 struct InsertArgs {
   const uint16_t* rows[3];  // K [n, heads, 128], V [n, heads, 128], index key [n, 128] (bf16 bits)
   uint8_t* pools[3];        // [num_pages, heads, 8704] x 2, [num_pages, 8704]
@@ -214,17 +204,17 @@ __global__ __launch_bounds__(256) void insert_kernel(InsertArgs a) {
     const int flog2 = E ? (int)E - 127 : -133 + (31 - (int)__builtin_clz(amax & 0x7Fu));
     byte = min(max(flog2 - 2 + 127, 0), 254);
   }
-  const float scale = __uint_as_float((uint32_t)(254 - min(byte, 252)) << 23);  // 2^(127 - byte)
+  const float scale = e8m0_scale_operand((uint32_t)byte);  // 2^(byte - 127)
   u32x4_t out;
 #pragma unroll
   for (int L = 0; L < 4; ++L) {  // bf16 elements 8L..8L+7 -> codes in nibbles of word L
-    uint32_t w = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t d = in[L][i >> 1];
-      const uint32_t f = (i & 1) ? (d & 0xFFFF0000u) : (d << 16);  // the bf16 as fp32 bits
-      w |= (e2m1_code_of(__uint_as_float(f), scale) | ((f >> 28) & 8u)) << (4 * i);
-    }
+    // byte p of the word takes elements 8L+2p (low nibble) and 8L+2p+1
+    auto lo = [&](int p) { return __uint_as_float(in[L][p] << 16); };
+    auto hi = [&](int p) { return __uint_as_float(in[L][p] & 0xFFFF0000u); };
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, lo(0), hi(0), scale, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(1), hi(1), scale, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(2), hi(2), scale, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, lo(3), hi(3), scale, 3);
     out[L] = byte == 0xFF ? 0u : w;
   }
   const int r = (int)(slot & (kPageTokens - 1));

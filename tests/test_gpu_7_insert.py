@@ -178,3 +178,43 @@ def test_full_size_decode_insert(spd):
     np.testing.assert_array_equal(got["k_pages"], k_new)
     np.testing.assert_array_equal(got["v_pages"], v_new)
     np.testing.assert_array_equal(got["index_pages"], i_new)
+
+
+def test_insert_ties_and_edges_from_golden_blocks(spd):
+    """The hand-worked blocks (every e2m1 tie, saturation, signed zeros,
+    NaN/inf, subnormals, the largest bf16 exponents), rounded to bf16 and
+    shifted by powers of two, so ties occur at many scale bytes."""
+    import os
+
+    blocks = []
+    with open(os.path.join(os.path.dirname(__file__), "golden", "mxfp4_quantize_blocks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            vals = [float.fromhex(t) if "p" in t else float(t) for t in line.split()[3:]]
+            v = np.zeros(32)
+            v[: len(vals)] = vals
+            blocks.append(v)
+    rows = []
+    for v in blocks:
+        with np.errstate(over="ignore", invalid="ignore"):
+            for j in (-120, -40, -3, 0, 5, 60):
+                rows.append(v * 2.0**j)
+    rows = np.array(rows)
+    n_rows = -(-rows.shape[0] // 4)
+    flat = np.zeros((n_rows * 4, 32))
+    flat[: rows.shape[0]] = rows
+    bits = mxfp4.round_to_bf16_bits(flat.reshape(n_rows, 128))  # out-of-range values become inf blocks
+    rng = np.random.default_rng(29)
+    pages = -(-n_rows // 128)
+    k_pool, v_pool, index_pool = _pools(rng, pages, 1)
+    rows_d = {"k": bits[:, None, :], "v": bits[::-1, None, :].copy(), "index": bits}
+    slots = rng.permutation(pages * 128)[:n_rows].astype(np.int64)
+    ws = spd.Workspace("cuda")
+    got = _gpu_insert(spd, k_pool, v_pool, index_pool, rows_d, slots, ws)
+    assert spd.check_device_errors(ws) == 0
+    k_new, v_new, i_new, _ = _oracle_insert(k_pool, v_pool, index_pool, rows_d, slots)
+    np.testing.assert_array_equal(got["k_pages"], k_new)
+    np.testing.assert_array_equal(got["v_pages"], v_new)
+    np.testing.assert_array_equal(got["index_pages"], i_new)
