@@ -16,9 +16,10 @@ copies, so each step reads pages that are not in the 256 MB Infinity Cache.
 Printed (one JSON line): achieved HBM GB/s over the KV+index bytes the method
 must read (the index rows of every valid token once per request, the K and V
 rows of every selected token once per request) and the step time, both from
-the timed region; the roofline entry of the step kernel, timed in a second
-pass of the same steps with HIP events recorded around each launch on its
-stream; the two-call form of the step (index call, then attention call)
+the timed region (K steps back to back between two events); the spread of
+single steps from a second pass with an event pair around each step; the
+roofline entry of the step kernel, timed in a further pass of the same steps
+with HIP events recorded around each launch on its stream; the two-call form of the step (index call, then attention call)
 timed the same way, for reference; the MXFP4 cache insert (the decoded
 tokens' K, V and index-key rows written through their slots, and a
 32768-token prefill-sized insert) by kernel time; the indexer's
@@ -316,22 +317,32 @@ def main():
     idx_bytes, kv_bytes = algorithmic_bytes(w, sel_np)
     bytes_step = idx_bytes + kv_bytes
 
-    # Timed region: exactly K steps, an event pair around each step.
+    # Timed region: exactly K steps back to back, one event before the first
+    # and one after the last, between synchronisations.
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
+    ev0.record(stream)
+    for s in range(K):
+        step(s % copies)
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    total_ms = ev0.elapsed_time(ev1)
+    ms_per_step = total_ms / K
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    # The spread of single steps: the same K steps again with an event pair
+    # around each (the events add a little time between steps).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(K)]
+    torch.cuda.synchronize(dev)
     for s in range(K):
         evs[s][0].record(stream)
         step(s % copies)
         evs[s][1].record(stream)
     torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-
     step_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
-    total_ms = evs[0][0].elapsed_time(evs[-1][1])
-    ms_per_step = total_ms / K
-    value = bytes_step / (ms_per_step * 1e-3) / 1e9
 
     # Kernel-timing pass: the same K steps again, every kernel the library
     # launches bracketed by HIP events on its stream (the events add launch
