@@ -226,3 +226,57 @@ def test_step_multiple_kv_heads(spd):
             o = mxfp4.bf16_bits_to_f64(out_bits[i, 16 * h : 16 * h + 16])
             rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
             assert rel <= 5e-3 and np.max(np.abs(o - ref)) <= 1e-2 * vmax, (i, h, rel)
+
+
+def test_one_workspace_across_formats_windows_and_inserts(spd):
+    """One buffer for MXFP4 and fp8 steps, window scans, dense attention and
+    inserts, in a mixed order: each result equals the same call on a fresh
+    workspace."""
+    ws = spd.Workspace("cuda", 64 << 20)
+    w4 = make_workload("mix4", B=3, T=2, seq_lens=[700, 3000, 5000], bt_width=40, k=300, seed=81,
+                       exp_range=(124, 127))
+    w8 = make_workload("mix8", B=2, T=1, seq_lens=[9000, 130], bt_width=71, k=500, seed=82, cache="fp8")
+    d4, d8 = to_device(w4), to_device(w8)
+
+    def step4(ws_):
+        return spd.mono_sparse_decode_mxfp4(d4["index_q"], d4["index_pool"], d4["q"], d4["k_pool"], d4["v_pool"],
+                                            d4["block_table"], d4["seq_lens"], w4.k, w4.scale, T=w4.T, workspace=ws_)
+
+    def step8(ws_):
+        return spd.mono_sparse_decode_fp8(d8["index_q"], d8["index_pool"], d8["q"], d8["k_pool"], d8["v_pool"],
+                                          d8["block_table"], d8["seq_lens"], w8.k, w8.scale, w8.k_scale, w8.v_scale,
+                                          workspace=ws_)
+
+    def window(ws_):
+        return spd.mono_index_score_topk(d4["index_q"], d4["index_pool"], d4["block_table"], d4["seq_lens"], w4.k,
+                                         T=w4.T, page_window=(10, 30), workspace=ws_)
+
+    def dense(ws_):
+        return spd.mono_pa_decode_mxfp4(d4["q"], d4["k_pool"], d4["v_pool"], d4["block_table"], d4["seq_lens"], None,
+                                        w4.scale, T=w4.T, workspace=ws_)
+
+    def norm(r):
+        if isinstance(r, tuple):
+            out, sel = r
+            return bf16_bits(out), np.sort(sel.cpu().numpy(), axis=1)
+        return (np.sort(r.cpu().numpy(), axis=1),) if r.dtype == torch.int32 else (bf16_bits(r),)
+
+    calls = [step8, window, step4, dense, step8, step4, window]
+    want = {f.__name__: norm(f(spd.Workspace("cuda"))) for f in set(calls)}
+    torch.cuda.synchronize()
+    for n, f in enumerate(calls):
+        got = norm(f(ws))
+        torch.cuda.synchronize()
+        for a, b in zip(got, want[f.__name__]):
+            if a.dtype == np.uint16:  # outputs: equal up to fp32 summation order
+                fa, fb = mxfp4.bf16_bits_to_f64(a), mxfp4.bf16_bits_to_f64(b)
+                assert np.max(np.abs(fa - fb)) <= 1e-2 * np.max(np.abs(fb)), (n, f.__name__)
+            else:
+                np.testing.assert_array_equal(a, b, err_msg=f"call {n} ({f.__name__})")
+        # an insert into a copy of the pools reports its errors through the same workspace
+        if n == 3:
+            slots = torch.tensor([5, 3 * 10**9], dtype=torch.int64, device="cuda")
+            rows = torch.zeros((2, 128), dtype=torch.bfloat16, device="cuda")
+            spd.mono_insert_mxfp4(slots, index_rows=rows, index_pages=d4["index_pool"].clone(), workspace=ws)
+            assert spd.check_device_errors(ws) == spd.DEVERR_SLOT
+    assert spd.check_device_errors(ws) == 0
