@@ -119,6 +119,22 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
 
 
+def gpu_clocks():
+    """Current clocks of GPU 0 from rocm-smi (a child process, run before this
+    process touches the GPU), or None when rocm-smi is unavailable."""
+    import subprocess
+
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        data = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next((v for k, v in sorted(data.items()) if k.startswith("card")), None)
+    if not isinstance(card, dict):
+        return None
+    return {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk"))}
+
+
 def algorithmic_bytes(w, sel):
     """(index bytes, K+V bytes) the step must read: one row (68 B MXFP4, 128 B
     fp8) per index row of every valid token once per request, 2 rows per
@@ -255,6 +271,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    clocks = gpu_clocks()
 
     import torch
 
@@ -450,6 +467,7 @@ def main():
         "wall_s": round(wall, 3),
         "device": torch.cuda.get_device_name(dev),
         "arch": torch.cuda.get_device_properties(dev).gcnArchName,
+        "clocks": clocks,
         "hip": torch.version.hip,
     }
     print(json.dumps(line))
