@@ -32,6 +32,8 @@
 #include "launch.h"
 #include "page_format.h"
 
+#include <type_traits>
+
 namespace mono {
 
 constexpr int kGroupTokens = 16;
@@ -97,20 +99,27 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
 
   // The first pass's selection entries are requested first; the block-table
   // row (into LDS) and the q operand (into registers) load meanwhile.
-  // The entry load is unconditional (clamped inside the split, masked
-  // after) so the compiler can count outstanding loads exactly.
-  auto entry_of = [&](int grp) -> int {
+  // Loaded values are never rewritten before use (a rewrite makes the
+  // compiler wait for that load before issuing the next ones): entry loads
+  // are unconditional, clamped inside the split, and whether an entry
+  // counts is decided where it is used (token_of).
+  auto entry_load = [&](int grp) -> int {
+    if (!a.sel_row) return 0;
+    const int entry = e0 + kGroupTokens * grp + m;
+    return (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + min(entry, e1 - 1)));
+  };
+  auto token_of = [&](int grp, int raw) -> int {
     const int entry = e0 + kGroupTokens * grp + m;
     const bool in = grp < n_groups && entry < e1;
-    if (!a.sel_row) return in ? entry : -1;
-    const int j = (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + min(entry, e1 - 1)));
-    return in ? j : -1;
+    return in ? (a.sel_row ? raw : entry) : -1;
   };
   int jv[kPassGroups];
 #pragma unroll
-  for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(wave + kWaves * x);
+  for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
   const int bt_len = (pos >> 7) + 1;
   const bool bt_lds = bt_len <= kBtCache;
+  typedef __attribute__((address_space(3))) const int32_t lds_i32;
+  lds_i32* const bt_local = (lds_i32*)(lds.bt);
   if (bt_lds)
     for (int x = tid; x < bt_len; x += kBlock) lds.bt[x] = a.bt_row[x];
   // B operand of QK^T: column n = m is query head m; k-slot (g, e) of k-step
@@ -134,18 +143,30 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   const uint8_t* vbase = a.v_pages + (size_t)h * Fmt::kPageBytes;
 
   // Token j of lane (g, m) -> its pool row, packed as page << 7 | row, or
-  // ~0u when it is not a candidate.
-  auto token_ref = [&](int j) -> uint32_t {
+  // ~0u when it is not a candidate.  The page id comes from the LDS copy of
+  // the block-table row through an LDS-qualified pointer, or, in the
+  // long-table instance of the pass loop, from the row in global memory.
+  // (A run-time choice between the two becomes one generic-address load,
+  // whose wait covers both memory counters and so every K/V load in flight.)
+  auto token_ref = [&](int j, auto long_table) -> uint32_t {
     if (j < 0 || j > pos) return ~0u;
-    const int pid = bt_lds ? lds.bt[j >> 7] : a.bt_row[j >> 7];
+    const int idx = j >> 7;
+    int pid;
+    if constexpr (decltype(long_table)::value) {
+      pid = a.bt_row[idx];
+    } else {
+      pid = bt_local[idx];
+    }
     if (pid < 0 || pid >= a.num_pages) {
       raise_error(a.err, kErrPageId);
       return ~0u;
     }
     return ((uint32_t)pid << 7) | (uint32_t)(j & (kPageTokens - 1));
   };
-  // Loads are unconditional (a non-candidate reads page 0, row 0, and is
-  // zeroed afterwards) so the compiler can count outstanding loads exactly.
+  // Loads are unconditional (a non-candidate reads page 0, row 0) and their
+  // values are not touched here: a non-candidate's logits become -inf in
+  // qk_group (each logit depends on its own token's K row only) and its V
+  // values become zero in pv_group, so a NaN in such a row cannot leak.
   auto load_group = [&](uint32_t ref) -> AttnGroup<Fmt> {
     AttnGroup<Fmt> t;
     t.valid = ref != ~0u;
@@ -160,9 +181,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
       const uint32_t r1 = ri != ~0u ? ri : 0u;
       const uint8_t* page = vbase + (size_t)(r1 >> 7) * kv_stride;
       t.v[i] = Fmt::load_slice(page, r1 & 127u, m);
-      if (ri == ~0u) t.v[i] = Fmt::zero_slice();
     }
-    if (!t.valid) t.k = Fmt::zero_chunk();
     return t;
   };
   // S^T tile of a group: lane (g, n) gets tokens 4g + i (i = 0..3) of head n.
@@ -179,10 +198,16 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   // acc += P V of a group; pa is the A operand (row n = head n, k-slot (g, i)
   // = token 4g + i).
   auto pv_group = [&](const AttnGroup<Fmt>& t, s16x4_t pa) {
-    // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1).
+    // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1);
+    // exact zeros for tokens that are not candidates.
+    const uint32_t vm = (uint32_t)__ballot(t.valid);
     u32x4_t vv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vv[i] = Fmt::slice_bf16(t.v[i]);
+    for (int i = 0; i < 4; ++i) {
+      const u32x4_t c = Fmt::slice_bf16(t.v[i]);
+      const bool ok = (vm >> (4 * g + i)) & 1u;
+      vv[i] = u32x4_t{ok ? c[0] : 0u, ok ? c[1] : 0u, ok ? c[2] : 0u, ok ? c[3] : 0u};
+    }
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int p = x >> 1;
@@ -198,13 +223,14 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   // A pass covers kPassGroups groups of this wave: page lookups, the K/V
   // loads of all of them at once, QK^T of all, one online-softmax update,
   // then P V of all.  The first pass's entries were requested at the start.
+  auto passes = [&](auto long_table) {
   for (int gb = wave; gb < n_groups; gb += kWaves * kPassGroups) {
     AttnGroup<Fmt> grp[kPassGroups];
 #pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(jv[x]));
+    for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(token_of(gb + kWaves * x, jv[x]), long_table));
     // The next pass's entries load while this pass computes.
 #pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_of(gb + kWaves * kPassGroups + kWaves * x);
+    for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_load(gb + kWaves * kPassGroups + kWaves * x);
     f32x4_t z[kPassGroups];
     float mx = -INFINITY;
 #pragma unroll
@@ -235,6 +261,12 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
       pv_group(grp[x], __builtin_bit_cast(s16x4_t, (uint64_t)p01 | ((uint64_t)p23 << 32)));
     }
     l_run = l_run * alpha + psum;
+  }
+  };
+  if (bt_lds) {
+    passes(std::false_type{});
+  } else {
+    passes(std::true_type{});
   }
 
   // ---- combine the four waves -------------------------------------------
@@ -315,20 +347,21 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
     float mv[kMergeBatch], lv[kMergeBatch];
     f32x4_t av[kMergeBatch][2];
+    // Loaded values are not rewritten before all loads of the batch are
+    // issued (a rewrite makes the compiler wait load by load); splits past
+    // the last are masked where the values are used.
 #pragma unroll
     for (int y = 0; y < kMergeBatch; ++y) {
-      const bool in = s0 + y < n_splits;
-      const size_t sl = (size_t)(in ? s0 + y : s0);
+      const size_t sl = (size_t)min(s0 + y, n_splits - 1);
       mv[y] = load_coherent(pm + sl * kQHeads + hd);
       lv[y] = load_coherent(pl + sl * kQHeads + hd);
       const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + (sl * kQHeads + hd) * kHeadDim + d0);
       av[y][0] = src[0];
       av[y][1] = src[1];
-      if (!in) mv[y] = -INFINITY;
     }
     float Mb = M;
 #pragma unroll
-    for (int y = 0; y < kMergeBatch; ++y) Mb = fmaxf(Mb, mv[y]);
+    for (int y = 0; y < kMergeBatch; ++y) Mb = fmaxf(Mb, s0 + y < n_splits ? mv[y] : -INFINITY);
     const float Mu_b = (Mb == -INFINITY) ? 0.f : Mb;
     const float fo = __builtin_amdgcn_exp2f(M - Mu_b);  // rescale what was merged so far
     lsum *= fo;
@@ -336,7 +369,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     for (int x = 0; x < 8; ++x) o[x] *= fo;
 #pragma unroll
     for (int y = 0; y < kMergeBatch; ++y) {
-      const float f = __builtin_amdgcn_exp2f(mv[y] - Mu_b);
+      const float f = s0 + y < n_splits ? __builtin_amdgcn_exp2f(mv[y] - Mu_b) : 0.f;
       lsum += lv[y] * f;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
