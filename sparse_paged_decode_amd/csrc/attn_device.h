@@ -71,6 +71,11 @@ struct AttnArgs {
   float* pacc;              // [n_splits, 16, 128] partial accumulators
   uint32_t* split_cnt;      // arrivals of (query token, KV head)
   uint32_t* err;
+  // Chunk-local attention only: the candidates are LDS entries (token
+  // tok0 + llist[e]) whose pages are lptab[(j >> 7) - page0].
+  const __attribute__((address_space(3))) uint16_t* llist;
+  const __attribute__((address_space(3))) int32_t* lptab;
+  int tok0, page0;
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -90,7 +95,7 @@ struct AttnGroup {
   uint32_t valid;            // token m is a candidate
 };
 
-template <class Fmt>
+template <class Fmt, bool kLocal = false>
 __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
@@ -104,14 +109,18 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   // are unconditional, clamped inside the split, and whether an entry
   // counts is decided where it is used (token_of).
   auto entry_load = [&](int grp) -> int {
-    if (!a.sel_row) return 0;
     const int entry = e0 + kGroupTokens * grp + m;
-    return (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + min(entry, e1 - 1)));
+    if constexpr (kLocal) {
+      return a.tok0 + (int)a.llist[max(0, min(entry, e1 - 1))];
+    } else {
+      if (!a.sel_row) return 0;
+      return (int)load_coherent(reinterpret_cast<const uint32_t*>(a.sel_row + min(entry, e1 - 1)));
+    }
   };
   auto token_of = [&](int grp, int raw) -> int {
     const int entry = e0 + kGroupTokens * grp + m;
     const bool in = grp < n_groups && entry < e1;
-    return in ? (a.sel_row ? raw : entry) : -1;
+    return in ? ((kLocal || a.sel_row) ? raw : entry) : -1;
   };
   int jv[kPassGroups];
 #pragma unroll
@@ -120,7 +129,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   const bool bt_lds = bt_len <= kBtCache;
   typedef __attribute__((address_space(3))) const int32_t lds_i32;
   lds_i32* const bt_local = (lds_i32*)(lds.bt);
-  if (bt_lds)
+  if (!kLocal && bt_lds)
     for (int x = tid; x < bt_len; x += kBlock) lds.bt[x] = a.bt_row[x];
   // B operand of QK^T: column n = m is query head m; k-slot (g, e) of k-step
   // s holds q element 32g + 8s + e.
@@ -152,7 +161,9 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     if (j < 0 || j > pos) return ~0u;
     const int idx = j >> 7;
     int pid;
-    if constexpr (decltype(long_table)::value) {
+    if constexpr (kLocal) {
+      pid = a.lptab[idx - a.page0];
+    } else if constexpr (decltype(long_table)::value) {
       pid = a.bt_row[idx];
     } else {
       pid = bt_local[idx];
@@ -263,7 +274,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     l_run = l_run * alpha + psum;
   }
   };
-  if (bt_lds) {
+  if (kLocal || bt_lds) {
     passes(std::false_type{});
   } else {
     passes(std::true_type{});

@@ -90,6 +90,8 @@ struct StepLayout {
   int split_tokens;  // attention candidates per split
   int n_splits;      // attention splits per (query token, KV head)
   int select_mode;   // 1: one workgroup selects each query token's top k
+  int local;         // 1: chunk-local step (one query token per request; see step.hip)
+  int part_splits;   // splits the partial buffers hold per (query token, KV head)
   uint32_t n_clear, n_scan, n_select, n_filter, n_attn;  // work items of each kind (clear: when needed)
   uint32_t n_ready0;    // items ready at the start (the first tickets after the clear items)
   uint32_t ready_kind;  // their kind
@@ -97,9 +99,9 @@ struct StepLayout {
   size_t zero_end;      // [ctrl_base + header, zero_end) must be zero when items start
   uint64_t zero_units;  // zero_end / 256
   // control block (u32 words from ctrl_base): word offsets
-  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, pub, queue, ctrl_words;
-  // byte offsets in the workspace
-  size_t err, ctrl_base, hist, scores, cand, pm, pl, pacc, total;
+  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, lvl_cnt, pub, queue, ctrl_words;
+  // byte offsets in the workspace (hist2, hist3, ties, xcand, xcnt: chunk-local step only)
+  size_t err, ctrl_base, hist, hist2, hist3, ties, scores, xcand, xcnt, cand, pm, pl, pacc, total;
 };
 StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
 

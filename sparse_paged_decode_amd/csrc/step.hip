@@ -34,6 +34,12 @@ constexpr uint32_t kMaxSpins = 1u << 21;  // bound of one wait (seconds, far abo
 constexpr size_t kClearBytes = 32768;     // bytes zeroed by one clear item
 constexpr int kMinSplitTokens = 256;      // attention candidates per split: one pass of 4 waves x 4 groups of 16
 constexpr int kMaxSplitTokens = 8192;
+// Chunk-local step: scores a scan item keeps in LDS (32 pages), and chunks
+// per request (its attention splits).
+constexpr int kLocalTokens = 4096;
+constexpr int kLocalMaxChunks = 16;
+constexpr int kLvlWords = 5;  // per query token: arrivals of the four levels, then the finished count
+constexpr int kExchCap = 2048;  // threshold-bin tokens a request's chunks exchange (more: radix levels)
 
 StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse) {
   StepLayout l{};
@@ -66,6 +72,10 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   // workgroup per query token instead (the queue is sized for slices, the
   // larger of the two).
   l.select_mode = 0;
+  l.local = 0;  // launch_step decides
+  // The one-launch step with one query token per request may run chunk-local
+  // (launch_step decides); it needs room for up to kLocalMaxChunks splits.
+  const bool local_ok = mode == kModeFused && T == 1;
   l.n_scan = index ? (uint32_t)(B * l.q_groups * l.chunks) : 0u;
   l.n_select = 0u;
   l.n_filter = index ? (uint32_t)(N * l.slices) : 0u;
@@ -97,6 +107,8 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   w += index ? N : 0;
   l.attn_cnt = w;
   w += attn ? NH : 0;
+  l.lvl_cnt = w;
+  w += local_ok ? N * kLvlWords : 0;
   l.pub = w;
   w += 1;
   l.queue = w;
@@ -104,6 +116,9 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.ctrl_words = w;
   l.ctrl_base = take(w * 4);
   l.hist = take(index ? N * kHistBins * 4 : 0);
+  l.hist2 = take(local_ok ? N * kHistBins * 4 : 0);
+  l.hist3 = take(local_ok ? N * 1024 * 4 : 0);
+  l.ties = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
   // Everything from the end of the header to here must be zero when the
   // items start; the rest is scratch that each call overwrites.
   l.zero_end = off;
@@ -111,8 +126,11 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   const size_t zero_bytes = off - (l.ctrl_base + kHdrWords * 4);
   l.n_clear = (uint32_t)((zero_bytes + kClearBytes - 1) / kClearBytes);
   l.scores = take(index ? N * (size_t)l.lcap * 4 : 0);
+  l.xcand = take(local_ok ? N * kLocalMaxChunks * (size_t)kExchCap * 8 : 0);
+  l.xcnt = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
   l.cand = take(index ? N * (size_t)kCandCap * 8 : 0);
-  const size_t S = (size_t)l.n_splits;
+  l.part_splits = local_ok ? std::max(l.n_splits, kLocalMaxChunks) : l.n_splits;
+  const size_t S = (size_t)l.part_splits;
   l.pm = take(attn ? NH * S * kQHeads * 4 : 0);
   l.pl = take(attn ? NH * S * kQHeads * 4 : 0);
   l.pacc = take(attn ? NH * S * kQHeads * kHeadDim * 4 : 0);
@@ -202,6 +220,35 @@ __device__ __forceinline__ int window_valid(const StepLayout& lay, int pos) {
   return max(0, min(pos + 1, lay.win_hi * kPageTokens) - lay.win_lo * kPageTokens);
 }
 
+// ---------------------------------------------------------------------------
+// Chunk-local step (the one-launch call with one query token per request).
+// The scan item of chunk c keeps its scores in LDS.  The chunks of a request
+// are all resident at once, so they can agree on the threshold of the k-th
+// largest score through global histograms, one radix level at a time (key
+// bits 31..21, 20..10, 9..0; a level runs only while the threshold bin
+// holds more tokens than places left): each chunk adds its counts, arrives,
+// waits for the others and reads the sums.  More exact ties at the final key
+// than places go to the lowest positions, chunk by chunk, through per-chunk
+// tie counts.  Every chunk then attends over its own selected tokens as one
+// split of the token's attention; the last split to arrive merges them.
+// Scores, candidates and the selection never travel through global memory
+// between items, and no item is queued.
+// ---------------------------------------------------------------------------
+struct LocalLds {
+  union {
+    struct {
+      float scores[kLocalTokens];  // token e of the chunk (position 128 * first page + e)
+      ScanLds<1> scan;             // the scan's histogram, then each level's
+    } sel;
+    AttnLds attn;  // the attention's combine area (its block-table part is unused)
+  } u;
+  uint16_t list[kLocalTokens];  // the chunk's selected tokens e
+  int32_t ptab[kLocalTokens / kPageTokens];
+  uint32_t scratch[kWaves + 4];
+  uint32_t xc[kLocalMaxChunks], xpre[kLocalMaxChunks + 1];  // exchanged counts per chunk, their prefix sums
+};
+static_assert(sizeof(float) * kLocalTokens >= sizeof(uint2) * kExchCap, "exchanged candidates reuse the score area");
+
 template <int TQ>
 union StepLds {
   ScanLds<TQ> scan;
@@ -243,6 +290,360 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
   __syncthreads();
   if (lay.mode == kModeFused)
     publish(lay, ctrl, kItemAttn, i * (uint32_t)(lay.H * lay.n_splits), (uint32_t)(lay.H * lay.n_splits), err, s_pub);
+}
+
+// Every thread's memory updates are complete, then this workgroup arrives at
+// *cnt and waits until `target` workgroups have.
+__device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint32_t* err) {
+  wait_vmem();
+  __syncthreads();
+  if (thread_index() == 0) {
+    atomicAdd(cnt, 1u);
+    uint32_t spins = 0;
+    while (load_coherent(cnt) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kMaxSpins) {
+        raise_error(err, kErrWait);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// The bin of the R-th largest key in a global histogram row of nbins (<= 2048) bins.
+__device__ __forceinline__ BinSplit global_rank_bin(const uint32_t* g, int nbins, uint32_t R, uint32_t* hist,
+                                                    uint32_t* scratch) {
+  const int tid = thread_index();
+  uint32_t h[kHistBins / kBlock];
+#pragma unroll
+  for (int u = 0; u < kHistBins / kBlock; ++u) h[u] = u * kBlock < nbins ? load_coherent(g + u * kBlock + tid) : 0u;
+#pragma unroll
+  for (int u = 0; u < kHistBins / kBlock; ++u)
+    if (u * kBlock < nbins) hist[u * kBlock + tid] = h[u];
+  __syncthreads();
+  return find_bin_of_rank(hist, nbins, R, scratch);
+}
+
+// Adds the digits (key >> shift) & (nbins - 1) of this thread's keys marked
+// in `mask` to global histogram row g, through an LDS histogram.
+__device__ __forceinline__ void level_counts(const uint32_t* key, uint32_t mask, int shift, int nbins, uint32_t* hist,
+                                             uint32_t* g) {
+  const int tid = thread_index();
+  for (int x = tid; x < nbins; x += kBlock) hist[x] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    if ((mask >> u) & 1u) atomicAdd(&hist[(key[u] >> shift) & (uint32_t)(nbins - 1)], 1u);
+  __syncthreads();
+  for (int x = tid; x < nbins; x += kBlock) {
+    const uint32_t v = hist[x];
+    if (v) atomicAdd(g + x, v);
+  }
+}
+
+template <class Fmt>
+__device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& lay, uint32_t t, LocalLds& lds,
+                                           uint32_t* ctrl, uint32_t* err) {
+  const int tid = thread_index();
+  const int b = (int)(t / (uint32_t)lay.chunks), c = (int)(t % (uint32_t)lay.chunks);
+  const int L = a.seq_lens[b];
+  if (L < 1 || L > lay.lcap) {
+    if (c == 0 && tid == 0) raise_error(err, kErrSeqLen);
+    return;
+  }
+  const int n_pages = (L + kPageTokens - 1) / kPageTokens;
+  const int nch = (n_pages + lay.chunk_pages - 1) / lay.chunk_pages;
+  if (c >= nch) return;  // every chunk of the request agrees on nch
+  const int i = b;       // one query token per request, at position L - 1; tokens 0..L-1 are valid
+  const int p_begin = c * lay.chunk_pages, p_end = min(p_begin + lay.chunk_pages, n_pages);
+  const int tok0 = p_begin * kPageTokens;
+  const int n_mine = min(L, p_end * kPageTokens) - tok0;  // valid tokens of the chunk (>= 1)
+  const int k = lay.k;
+  uint32_t* g1 = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)i * kHistBins;
+  uint32_t* g2 = reinterpret_cast<uint32_t*>(a.ws + lay.hist2) + (size_t)i * kHistBins;
+  uint32_t* g3 = reinterpret_cast<uint32_t*>(a.ws + lay.hist3) + (size_t)i * 1024;
+  uint32_t* gt = reinterpret_cast<uint32_t*>(a.ws + lay.ties) + (size_t)i * kLocalMaxChunks;
+  uint32_t* lvl = ctrl + lay.lvl_cnt + (size_t)i * kLvlWords;
+  uint32_t* hist = lds.u.sel.scan.hist;
+
+  {
+    ScanArgs sa;
+    sa.index_q = a.index_q;
+    sa.pages = a.index_pages;
+    sa.num_pages = a.num_pages;
+    sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
+    sa.q_scores = nullptr;
+    sa.ghist = g1;
+    sa.err = err;
+    sa.lcap = lay.lcap;
+    sa.q0 = i;
+    sa.pos0 = L - 1;
+    sa.tq = 1;
+    sa.p_begin = p_begin;
+    sa.p_end = p_end;
+    scan_chunk<1, Fmt, true>(sa, lds.u.sel.scan, (lds_f32*)lds.u.sel.scores, (lds_i32w*)lds.ptab);
+  }
+  __syncthreads();
+
+  // Thread t holds the keys of tokens 16t..16t+15 of the chunk.
+  uint32_t key[16];
+  {
+    const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(lds.u.sel.scores + 16 * tid);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4_t v = sp[q4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) key[4 * q4 + x] = score_key(v[x]);
+    }
+  }
+  const int n_here = max(0, min(16, n_mine - 16 * tid));
+  const uint32_t valid = n_here >= 16 ? 0xFFFFu : ((1u << n_here) - 1u);
+
+  // Threshold: every token with key > thr is selected, and of those with
+  // key == thr the first `take` in position order (all of them unless ties).
+  const bool all = L <= k;
+  uint32_t thr = 0u, take = 0xFFFFFFFFu;
+  bool ties = false;
+  if (!all) {
+    arrive_wait(lvl + 0, (uint32_t)nch, err);
+    const BinSplit s1 = global_rank_bin(g1, kHistBins, (uint32_t)k, hist, lds.scratch);
+    uint32_t R = (uint32_t)k - s1.above;
+    const uint32_t B1 = (uint32_t)s1.bin;
+    thr = B1 << kHistShift;
+    if (s1.count != R && s1.count <= (uint32_t)kExchCap) {
+      // Few enough tokens in bin B1: every chunk publishes its own (key,
+      // position) pairs of that bin, then each chunk reads all of them and
+      // takes the rest of the selection from them in LDS.
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m2 |= ((key[u] >> kHistShift) == B1) ? (1u << u) : 0u;
+      m2 &= valid;
+      uint32_t my_cnt;
+      const uint32_t my_off = block_exclusive_scan((uint32_t)__popc(m2), lds.scratch, my_cnt);
+      uint64_t* xc_all = reinterpret_cast<uint64_t*>(a.ws + lay.xcand) + (size_t)i * kLocalMaxChunks * kExchCap;
+      uint32_t* xn_all = reinterpret_cast<uint32_t*>(a.ws + lay.xcnt) + (size_t)i * kLocalMaxChunks;
+      {
+        uint64_t* mine = xc_all + (size_t)c * kExchCap;
+        uint32_t bits = m2, o = my_off;
+        while (bits) {
+          const int u = __builtin_ctz(bits);
+          bits &= bits - 1u;
+          store_coherent(mine + o++, (uint64_t)key[u] | ((uint64_t)(uint32_t)(tok0 + 16 * tid + u) << 32));
+        }
+      }
+      if (tid == 0) store_coherent(xn_all + c, my_cnt);
+      arrive_wait(lvl + 1, (uint32_t)nch, err);
+      // Counts and the first `win` entries of every chunk are requested at
+      // once; chunks with more follow in a second round.
+      const int win = kExchCap / nch;
+      constexpr int kPer = kExchCap / kBlock;
+      uint64_t v[kPer];
+      const uint32_t cnt_ld = tid < nch ? load_coherent(xn_all + tid) : 0u;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int e = q * kBlock + tid, cc = e / win, r = e % win;
+        v[q] = cc < nch ? load_coherent(xc_all + (size_t)cc * kExchCap + r) : 0ull;
+      }
+      if (tid < nch) lds.xc[tid] = cnt_ld;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t acc = 0;
+        for (int cc = 0; cc < nch; ++cc) {
+          lds.xpre[cc] = acc;
+          acc += min(lds.xc[cc], (uint32_t)kExchCap);
+        }
+        lds.xpre[nch] = acc;
+      }
+      __syncthreads();
+      uint2* cand = reinterpret_cast<uint2*>(lds.u.sel.scores);
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) {
+        const int e = q * kBlock + tid, cc = e / win, r = e % win;
+        if (cc < nch && (uint32_t)r < lds.xc[cc]) {
+          const uint32_t at = lds.xpre[cc] + (uint32_t)r;
+          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)v[q], (uint32_t)(v[q] >> 32));
+        }
+      }
+      for (int cc = 0; cc < nch; ++cc) {
+        const uint32_t n_cc = min(lds.xc[cc], (uint32_t)kExchCap);
+        for (uint32_t r = (uint32_t)win + tid; r < n_cc; r += kBlock) {
+          const uint32_t at = lds.xpre[cc] + r;
+          const uint64_t x = load_coherent(xc_all + (size_t)cc * kExchCap + r);
+          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+        }
+      }
+      const int n_c = (int)min(lds.xpre[nch], (uint32_t)kExchCap);
+      if (lds.xpre[nch] != s1.count && tid == 0) raise_error(err, kErrSelection);  // never expected
+      // Radix passes over key bits 20..10, then 9..0, among the candidates.
+      for (int x = tid; x < kHistBins; x += kBlock) hist[x] = 0u;
+      __syncthreads();
+      for (int e = tid; e < n_c; e += kBlock) atomicAdd(&hist[(cand[e].x >> 10) & 0x7FFu], 1u);
+      __syncthreads();
+      const BinSplit s2 = find_bin_of_rank(hist, kHistBins, R, lds.scratch);
+      R -= s2.above;
+      const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;
+      thr = pre2 << 10;
+      if (s2.count != R) {
+        for (int x = tid; x < 1024; x += kBlock) hist[x] = 0u;
+        __syncthreads();
+        for (int e = tid; e < n_c; e += kBlock)
+          if ((cand[e].x >> 10) == pre2) atomicAdd(&hist[cand[e].x & 0x3FFu], 1u);
+        __syncthreads();
+        const BinSplit s3 = find_bin_of_rank(hist, 1024, R, lds.scratch);
+        R -= s3.above;
+        thr = (pre2 << 10) | (uint32_t)s3.bin;
+        if (s3.count != R) {
+          // More tokens with key thr than places: the lowest positions
+          // first; `before` counts those of the chunks ahead of this one.
+          uint32_t mine = 0;
+          for (int e = tid; e < n_c; e += kBlock) mine += (cand[e].x == thr && (int)cand[e].y < tok0) ? 1u : 0u;
+          uint32_t before;
+          block_exclusive_scan(mine, lds.scratch, before);
+          take = R > before ? R - before : 0u;
+          ties = true;
+        }
+      }
+    } else if (s1.count != R) {
+      uint32_t m2 = 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m2 |= ((key[u] >> kHistShift) == B1) ? (1u << u) : 0u;
+      level_counts(key, m2 & valid, 10, kHistBins, hist, g2);
+      arrive_wait(lvl + 1, (uint32_t)nch, err);
+      const BinSplit s2 = global_rank_bin(g2, kHistBins, R, hist, lds.scratch);
+      R -= s2.above;
+      const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;
+      thr = pre2 << 10;
+      if (s2.count != R) {
+        uint32_t m3 = 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) m3 |= ((key[u] >> 10) == pre2) ? (1u << u) : 0u;
+        level_counts(key, m3 & valid, 0, 1024, hist, g3);
+        arrive_wait(lvl + 2, (uint32_t)nch, err);
+        const BinSplit s3 = global_rank_bin(g3, 1024, R, hist, lds.scratch);
+        R -= s3.above;
+        thr = (pre2 << 10) | (uint32_t)s3.bin;
+        if (s3.count != R) {
+          // More tokens with key thr than places: the lowest positions first.
+          uint32_t mine = 0;
+#pragma unroll
+          for (int u = 0; u < 16; ++u) mine += (((valid >> u) & 1u) && key[u] == thr) ? 1u : 0u;
+          uint32_t tot;
+          block_exclusive_scan(mine, lds.scratch, tot);
+          if (tid == 0) store_coherent(gt + c, tot);
+          arrive_wait(lvl + 3, (uint32_t)nch, err);
+          uint32_t before = 0;
+          for (int x = 0; x < c; ++x) before += load_coherent(gt + x);
+          take = R > before ? R - before : 0u;
+          ties = true;
+        }
+      }
+    }
+  }
+  uint32_t selm = 0, tie_rank = 0;
+  if (ties) {
+    uint32_t mine = 0;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mine += (((valid >> u) & 1u) && key[u] == thr) ? 1u : 0u;
+    uint32_t tot;
+    tie_rank = block_exclusive_scan(mine, lds.scratch, tot);
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const bool eq = key[u] == thr;
+    const bool in = all || key[u] > thr || (eq && tie_rank < take);
+    if (((valid >> u) & 1u) && in) selm |= 1u << u;
+    if (ties && ((valid >> u) & 1u) && eq) ++tie_rank;
+  }
+  uint32_t n_sel;
+  const uint32_t off = block_exclusive_scan((uint32_t)__popc(selm), lds.scratch, n_sel);
+  {
+    uint32_t bits = selm, o = off;
+    while (bits) {
+      const int u = __builtin_ctz(bits);
+      bits &= bits - 1u;
+      lds.list[o++] = (uint16_t)(16 * tid + u);
+    }
+  }
+  // Output slots: a block of n_sel taken from the token's counter (its value
+  // is needed only after the attention), or position j itself when every
+  // valid token is selected.  Then this chunk has read every global row it
+  // needs; the last chunk to get here clears them after its attention.
+  uint32_t base = 0, done_prev = 0;
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    if (!all && n_sel) base = atomicAdd(ctrl + lay.out_cnt + i, n_sel);
+    done_prev = atomicAdd(lvl + 4, 1u);
+  }
+
+  const int H = lay.H;
+  for (int h = 0; h < H; ++h) {
+    const size_t qh = (size_t)i * H + h;
+    AttnArgs aa;
+    aa.q = a.q + qh * kQHeads * kHeadDim;
+    aa.k_pages = a.k_pages;
+    aa.v_pages = a.v_pages;
+    aa.num_pages = a.num_pages;
+    aa.H = H;
+    aa.h = h;
+    aa.bt_row = nullptr;
+    aa.sel_row = nullptr;
+    aa.pos = L - 1;
+    aa.e0 = 0;
+    aa.e1 = (int)n_sel;
+    aa.split = c;
+    aa.n_splits = nch;
+    aa.scale = a.scale * a.k_scale;
+    aa.v_scale = a.v_scale;
+    aa.out = a.out + qh * kQHeads * kHeadDim;
+    const size_t S = (size_t)lay.part_splits;
+    aa.pm = reinterpret_cast<float*>(a.ws + lay.pm) + qh * S * kQHeads;
+    aa.pl = reinterpret_cast<float*>(a.ws + lay.pl) + qh * S * kQHeads;
+    aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
+    aa.split_cnt = ctrl + lay.attn_cnt + qh;
+    aa.err = err;
+    aa.llist = (const __attribute__((address_space(3))) uint16_t*)lds.list;
+    aa.lptab = (const __attribute__((address_space(3))) int32_t*)lds.ptab;
+    aa.tok0 = tok0;
+    aa.page0 = p_begin;
+    attn_split<Fmt, true>(aa, lds.u.attn);
+    __syncthreads();  // the next head reuses the combine area
+  }
+
+  if (tid == 0) {
+    lds.scratch[kWaves] = base;
+    lds.scratch[kWaves + 1] = done_prev;
+  }
+  __syncthreads();
+  base = lds.scratch[kWaves];
+  done_prev = lds.scratch[kWaves + 1];
+  {
+    int32_t* out = a.sel + (size_t)i * k;
+    uint32_t bits = selm, o = off;
+    while (bits) {
+      const int u = __builtin_ctz(bits);
+      bits &= bits - 1u;
+      const int j = tok0 + 16 * tid + u;
+      const uint32_t slot = all ? (uint32_t)j : base + o;
+      ++o;
+      if (slot < (uint32_t)k) {
+        store_coherent(reinterpret_cast<uint32_t*>(out + slot), (uint32_t)j);
+      } else {
+        raise_error(err, kErrSelection);
+      }
+    }
+    if (all && c == 0)
+      for (int x = L + tid; x < k; x += kBlock) store_coherent(reinterpret_cast<uint32_t*>(out + x), 0xffffffffu);
+  }
+  if (done_prev == (uint32_t)(nch - 1)) {
+    for (int x = tid; x < kHistBins; x += kBlock) {
+      g1[x] = 0u;
+      g2[x] = 0u;
+    }
+    for (int x = tid; x < 1024; x += kBlock) g3[x] = 0u;
+    if (tid < kLocalMaxChunks) gt[tid] = 0u;
+  }
 }
 
 template <int TQ, class Fmt>
@@ -391,9 +792,13 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   attn_split<Fmt>(aa, lds.attn);
 }
 
-template <int TQ, class Fmt>
+// kLocal: the chunk-local step's own instance, holding only the clear and
+// chunk-local items (a far smaller program than the instance with every
+// item kind, whose code does not fit the instruction cache).
+template <int TQ, class Fmt, bool kLocal>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
-  __shared__ StepLds<TQ> lds;
+  static_assert(!kLocal || TQ == 1, "the chunk-local step has one query token per request");
+  __shared__ std::conditional_t<kLocal, LocalLds, StepLds<TQ>> lds;
   __shared__ uint32_t s_item, s_flag, s_clear, s_desc, s_pub;
   const int tid = thread_index();
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
@@ -424,7 +829,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const uint32_t d =
           u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, s_desc);
       const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
-      if (kind == kItemScan) {
+      if constexpr (kLocal) {
+        if (kind == kItemScan) local_item<Fmt>(a, lay, idx, lds, ctrl, err);
+      } else if (kind == kItemScan) {
         scan_item<TQ, Fmt>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
       } else if (kind == kItemSelect) {
         select_item<TQ>(a, lay, idx, lds, ctrl, err, s_pub);
@@ -453,7 +860,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 // Workgroups that fit on the device at once (cached per device and kernel).
 int resident_workgroups(const void* kernel, int variant) {
   static std::mutex mu;
-  static int cache[64][4] = {};
+  static int cache[64][6] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   std::lock_guard<std::mutex> lock(mu);
@@ -472,11 +879,14 @@ int resident_workgroups(const void* kernel, int variant) {
 int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream, const char* what) {
   const bool tq4 = lay_in.T > 1 && (lay_in.mode & kModeIndex);
   const bool f8 = a.fmt == kFmtFp8;
-  const void* const kernels[4] = {
-      reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format>), reinterpret_cast<const void*>(&step_kernel<4, Mxfp4Format>),
-      reinterpret_cast<const void*>(&step_kernel<1, Fp8Format>), reinterpret_cast<const void*>(&step_kernel<4, Fp8Format>)};
-  const int variant = (tq4 ? 1 : 0) + (f8 ? 2 : 0);
-  const int cap = resident_workgroups(kernels[variant], variant);
+  const void* const kernels[6] = {reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, false>),
+                                  reinterpret_cast<const void*>(&step_kernel<4, Mxfp4Format, false>),
+                                  reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, false>),
+                                  reinterpret_cast<const void*>(&step_kernel<4, Fp8Format, false>),
+                                  reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, true>),
+                                  reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, true>)};
+  int variant = (tq4 ? 1 : 0) + (f8 ? 2 : 0);
+  int cap = resident_workgroups(kernels[variant], variant);
   StepLayout lay = lay_in;
   if (lay.mode & kModeIndex) {
     // Scan chunks sized so the scan items make about one round of the
@@ -515,6 +925,32 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
     if (!(lay.mode & kModeIndex)) lay.n_ready0 = lay.n_attn;
     lay.n_queue = (lay.mode & kModeIndex) ? lay.n_select + lay.n_filter + lay.n_attn : 0u;
   }
+  if (lay.mode == kModeFused && lay.T == 1 && lay.part_splits >= kLocalMaxChunks && a.sel_scores == nullptr &&
+      lay.win_lo == 0) {
+    // Chunk-local step: at most kLocalMaxChunks chunks of at most
+    // kLocalTokens scores per request, and every scan item a first ticket
+    // of a resident workgroup of its own kernel instance (the chunks of a
+    // request wait for each other).
+    const int lvariant = f8 ? 5 : 4;
+    const int lcap = resident_workgroups(kernels[lvariant], lvariant);
+    const int groups = lay.B;
+    const int span = lay.win_hi - lay.win_lo;
+    const int per_group = std::max(1, lcap / std::max(1, groups));
+    const int cp = std::max((span + per_group - 1) / per_group, (span + kLocalMaxChunks - 1) / kLocalMaxChunks);
+    const int ch = (span + cp - 1) / cp;
+    if (cp * kPageTokens <= kLocalTokens && ch <= kLocalMaxChunks && (size_t)groups * ch <= (size_t)lcap) {
+      variant = lvariant;
+      cap = lcap;
+      lay.local = 1;
+      lay.chunk_pages = cp;
+      lay.chunks = ch;
+      lay.n_scan = (uint32_t)(groups * ch);
+      lay.n_ready0 = lay.n_scan;
+      lay.select_mode = 0;
+      lay.n_select = lay.n_filter = lay.n_attn = 0u;
+      lay.n_queue = 0u;
+    }
+  }
   const uint32_t n_items = lay.n_clear + lay.n_ready0 + lay.n_queue;
   if (n_items == 0) return MONO_OK;
   if ((uint64_t)lay.n_scan + lay.n_select + lay.n_filter + lay.n_attn > kIndexMask)
@@ -526,10 +962,12 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
                   : lay.mode == kModeAttn  ? (f8 ? kKPaDecodeFp8 : kKPaDecode)
                                            : (f8 ? kKStepFp8 : kKStep);
   switch (variant) {
-    case 0: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 1: MONO_LAUNCH(kid, (step_kernel<4, Mxfp4Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    default: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 0: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 1: MONO_LAUNCH(kid, (step_kernel<4, Mxfp4Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 3: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 4: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, true>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    default: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, true>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
   }
   return check_launch(what);
 }

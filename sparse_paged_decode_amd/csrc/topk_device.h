@@ -68,8 +68,16 @@ struct ScanArgs {
   int p_begin, p_end;       // pages of the chunk
 };
 
-template <int TQ, class Fmt>
-__device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) {
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32w;
+
+// With kLocal (one query token), the scores go to lds_scores (token j of the
+// chunk at j - 128 * p_begin) instead of global memory, and the chunk's page
+// ids to lds_ptab, for the chunk-local step.
+template <int TQ, class Fmt, bool kLocal = false>
+__device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, lds_f32* lds_scores = nullptr,
+                                           lds_i32w* lds_ptab = nullptr) {
+  static_assert(!kLocal || TQ == 1, "chunk-local scans hold one query token");
   constexpr int kBatch = Fmt::kScanBatch;  // pages per prefetch batch
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
@@ -108,6 +116,9 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
     raise_error(a.err, kErrPageId);
     lane_pid = 0;
   }
+  if constexpr (kLocal) {
+    if (wave == 0 && lane < n_cp) lds_ptab[lane] = lane_pid;
+  }
 
   // Pages are fetched in batches of kBatch, one batch ahead of the one being
   // scored.  Loads are unconditional (past the chunk end they repeat its last
@@ -142,7 +153,11 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds) 
 #pragma unroll
         for (int i = 0; i < TQ; ++i) {
           if (i < a.tq && j <= a.pos0 + i) {
-            store_coherent(a.q_scores + (size_t)i * a.lcap + j, c[i]);
+            if constexpr (kLocal) {
+              lds_scores[j - p_begin * kPageTokens] = c[i];
+            } else {
+              store_coherent(a.q_scores + (size_t)i * a.lcap + j, c[i]);
+            }
             atomicAdd(&lds.hist[i * kHistBins + (score_key(c[i]) >> kHistShift)], 1u);
           }
         }

@@ -228,6 +228,97 @@ def test_step_multiple_kv_heads(spd):
             assert rel <= 5e-3 and np.max(np.abs(o - ref)) <= 1e-2 * vmax, (i, h, rel)
 
 
+def _fixed_index_pool(w, codes):
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+
+
+def test_step_one_token_all_equal_scores(spd):
+    """One query token per request (chunks resolve the threshold among
+    themselves) and every index score equal: the k lowest positions are
+    selected; a request with fewer valid tokens than k takes them all."""
+    w = make_workload("eqstep", B=3, T=1, seq_lens=[9000, 5000, 300], bt_width=71, k=1000, seed=41,
+                      exp_range=(124, 127))
+    _fixed_index_pool(w, np.full((w.num_pages, 128, 128), 2, dtype=np.uint8))
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i, L in enumerate(w.seq_lens):
+        n = min(w.k, int(L))
+        assert sorted(sel_np[i][:n].tolist()) == list(range(n)) and np.all(sel_np[i][n:] == -1), i
+        _check_token(w, i, sel_np[i], out_bits)
+
+
+def test_step_one_token_exact_ties_at_threshold(spd):
+    """A few distinct score values, so every radix level ends in a bin of
+    exact ties: the selection equals the oracle's, lowest positions first."""
+    w = make_workload("tiestep", B=4, T=1, seq_lens=[3000, 7000, 12000, 640], bt_width=96, k=777, seed=42,
+                      exp_range=(124, 127))
+    rng = np.random.default_rng(43)
+    codes = np.zeros((w.num_pages, 128, 128), dtype=np.uint8)
+    codes[:, :, 0] = rng.integers(0, 8, size=(w.num_pages, 128))  # score = iq[0] * value
+    _fixed_index_pool(w, codes)
+    w.index_q[:, 0] = mxfp4.round_to_bf16_bits(np.array([1.0]))[0]
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    for rep in range(2):  # the second call reuses the workspace the first left clean
+        out, sel = _step(spd, w, d, ws)
+        assert spd.check_device_errors(ws) == 0
+        sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+        for i, L in enumerate(w.seq_lens):
+            pos = int(L) - 1
+            ref = decode.topk(decode.index_scores(w.index_q[i], w.index_pool, w.block_table[i], pos), w.k)
+            n = min(w.k, pos + 1)
+            assert sorted(sel_np[i][:n].tolist()) == sorted(ref.tolist()), (rep, i)
+            _check_token(w, i, sel_np[i], out_bits)
+
+
+def test_step_one_token_three_kv_heads(spd):
+    """Three KV heads with one query token per request: every chunk attends
+    over its selected tokens for each head."""
+    w = make_workload("h3t1", B=3, T=1, seq_lens=[900, 3000, 5000], bt_width=40, k=700, seed=44,
+                      exp_range=(124, 127))
+    H = 3
+    rng = np.random.default_rng(45)
+    kh = rng.integers(0, 256, size=(w.num_pages, H, 8704), dtype=np.uint8)
+    vh = rng.integers(0, 256, size=(w.num_pages, H, 8704), dtype=np.uint8)
+    kh[..., 8192:] = rng.integers(124, 128, size=(w.num_pages, H, 512))
+    vh[..., 8192:] = rng.integers(124, 128, size=(w.num_pages, H, 512))
+    w.k_pool, w.v_pool = kh, vh
+    w.q = mxfp4.round_to_bf16_bits(rng.standard_normal((w.N, 16 * H, 128)))
+    d = to_device(w)
+    out, sel = _step(spd, w, d, spd.Workspace("cuda"))
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(w.N):
+        check_topk_row(sel_np[i], w, i, w.k)
+        pos = int(w.seq_lens[i]) - 1
+        for h in range(H):
+            ref = decode.decode_one(w.q[i, 16 * h : 16 * h + 16], kh, vh, w.block_table[i], pos, w.scale, sel_np[i],
+                                    head=h)
+            vmax = float(np.abs(decode.sequence_rows(vh, w.block_table[i], pos + 1, h)).max())
+            o = mxfp4.bf16_bits_to_f64(out_bits[i, 16 * h : 16 * h + 16])
+            rel = np.linalg.norm(o - ref) / np.linalg.norm(ref)
+            assert rel <= 5e-3 and np.max(np.abs(o - ref)) <= 1e-2 * vmax, (i, h, rel)
+
+
+def test_step_one_token_mid_batch(spd):
+    """40 requests of ragged length (12 chunks each, 480 resident chunk
+    items): sampled tokens against the oracle, every selection valid."""
+    w = make_workload("mid40", B=40, T=1, seq_lens=(6000, 16384), bt_width=128, k=1500, seed=46,
+                      exp_range=(124, 127))
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    for i in range(0, w.N, 5):
+        _check_token(w, i, sel_np[i], out_bits)
+    for i, L in enumerate(w.seq_lens):
+        row = sel_np[i]
+        assert np.unique(row).size == w.k and np.all((row >= 0) & (row < L))
+
+
 def test_one_workspace_across_formats_windows_and_inserts(spd):
     """One buffer for MXFP4 and fp8 steps, window scans, dense attention and
     inserts, in a mixed order: each result equals the same call on a fresh
