@@ -346,7 +346,16 @@ template <class Fmt>
 __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& lay, uint32_t t, LocalLds& lds,
                                            uint32_t* ctrl, uint32_t* err) {
   const int tid = thread_index();
-  const int b = (int)(t / (uint32_t)lay.chunks), c = (int)(t % (uint32_t)lay.chunks);
+  // Workgroups are dealt to the 8 XCDs in turn (workgroup x to XCD x % 8),
+  // and the first ticket of each is its index.  XCD x takes one contiguous
+  // run of the (request, chunk) pairs in request-major order, so the chunks
+  // of a request, which hand data to each other, mostly share an XCD.
+  uint32_t pair;
+  {
+    const uint32_t n = lay.n_scan, q = n >> 3, r = n & 7u, x = t & 7u, y = t >> 3;
+    pair = x * q + min(x, r) + y;
+  }
+  const int b = (int)(pair / (uint32_t)lay.chunks), c = (int)(pair % (uint32_t)lay.chunks);
   const int L = a.seq_lens[b];
   if (L < 1 || L > lay.lcap) {
     if (c == 0 && tid == 0) raise_error(err, kErrSeqLen);
@@ -435,14 +444,16 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       if (tid == 0) store_coherent(xn_all + c, my_cnt);
       arrive_wait(lvl + 1, (uint32_t)nch, err);
       // Counts and the first `win` entries of every chunk are requested at
-      // once; chunks with more follow in a second round.
-      const int win = kExchCap / nch;
+      // once (win: a power of two, nch * win <= kExchCap); chunks with more
+      // follow in a second round.
+      const int win_log2 = 11 - (32 - __builtin_clz((uint32_t)(nch - 1) | 1u)) + (nch == 1 ? 1 : 0);
+      const int win = 1 << win_log2;
       constexpr int kPer = kExchCap / kBlock;
       uint64_t v[kPer];
       const uint32_t cnt_ld = tid < nch ? load_coherent(xn_all + tid) : 0u;
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        const int e = q * kBlock + tid, cc = e / win, r = e % win;
+        const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
         v[q] = cc < nch ? load_coherent(xc_all + (size_t)cc * kExchCap + r) : 0ull;
       }
       if (tid < nch) lds.xc[tid] = cnt_ld;
@@ -459,7 +470,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       uint2* cand = reinterpret_cast<uint2*>(lds.u.sel.scores);
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        const int e = q * kBlock + tid, cc = e / win, r = e % win;
+        const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
         if (cc < nch && (uint32_t)r < lds.xc[cc]) {
           const uint32_t at = lds.xpre[cc] + (uint32_t)r;
           if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)v[q], (uint32_t)(v[q] >> 32));
