@@ -99,6 +99,9 @@ def parse():
     p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
     p.add_argument("--skip-insert", action="store_true", help="do not time the cache insert")
     p.add_argument("--skip-cp", action="store_true", help="do not time the indexer context-parallel emulation")
+    p.add_argument("--skip-clocks", action="store_true",
+                   help="do not read the clocks through rocm-smi (under a profiler, whose preloaded library has "
+                        "already opened the GPU, the child process may not start)")
     p.add_argument("--skip-two-call", action="store_true",
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -271,7 +274,7 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    clocks = gpu_clocks()
+    clocks = None if args.skip_clocks else gpu_clocks()
 
     import torch
 
@@ -414,7 +417,10 @@ def main():
         ins = time_insert(spd, torch, dev, w, kp, vp, ip, min(K, 100))
     cp = None
     if w.sparse and not f8 and not args.skip_cp:
-        cp = time_cp(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
+        if 4 * w.k <= 8192:  # the merge takes at most 8192 candidates per query token
+            cp = time_cp(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
+        else:
+            cp = {"skipped": f"4 shards x top-{w.k} = {4 * w.k} candidates per query token; the merge takes 8192"}
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(w, args.cpu_sample)

@@ -25,7 +25,9 @@
 // roundings are fp32 accumulation, exp2, and the bf16 rounding of the
 // probabilities (the row sums use the same rounded values).  Split partials
 // (max, sum, 16x128 accumulator) are handed over with coherent stores; the
-// last split to arrive merges them and writes the bf16 output.
+// last split to arrive merges them and writes the bf16 output.  The
+// chunk-local instance (kLocal) reads its candidates from an LDS list and
+// their pages from an LDS table instead of global memory.
 #pragma once
 
 #include "block_ops.h"

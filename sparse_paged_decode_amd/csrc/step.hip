@@ -9,6 +9,10 @@
 //          (the last split of (i, h) to finish merges them)
 // mono_index_score_topk runs the scan and filter items, mono_pa_decode_mxfp4
 // the attention items, mono_sparse_decode_mxfp4 all three in one launch.
+// With one query token per request, mono_sparse_decode_mxfp4 runs a separate
+// instance whose only items are chunk-local steps (local_item): each chunk
+// scans, selects together with the other chunks of its request, and attends
+// over its own share of the selection.
 //
 // Workgroups take tickets from one atomic counter.  The first tickets are
 // the items that are ready at the start (the scans, or the attention splits
