@@ -274,6 +274,32 @@ def test_step_one_token_exact_ties_at_threshold(spd):
             _check_token(w, i, sel_np[i], out_bits)
 
 
+def test_step_one_token_concentrated_threshold_bin(spd):
+    """The tokens of the threshold bin sit in the first chunks only (more of
+    them in one chunk than the exchange requests at once) and tie exactly:
+    the k lowest positions of the tied tokens are selected.  A second request
+    with fewer tokens than k takes all of them in the same launch."""
+    w = make_workload("concstep", B=2, T=1, seq_lens=[4096, 250], bt_width=32, k=300, seed=47,
+                      exp_range=(124, 127))
+    codes = np.zeros((w.num_pages, 128, 128), dtype=np.uint8)
+    rng = np.random.default_rng(48)
+    codes[:, :, 0] = rng.integers(1, 4, size=(w.num_pages, 128))  # scores 0.5 .. 1.5 times iq[0]
+    bt0 = w.block_table[0]
+    for p in range(4):  # the first 512 positions of request 0 all score 6 * iq[0]
+        codes[bt0[p], :, 0] = 7
+    _fixed_index_pool(w, codes)
+    w.index_q[:, 0] = mxfp4.round_to_bf16_bits(np.array([1.0]))[0]
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    out, sel = _step(spd, w, d, ws)
+    assert spd.check_device_errors(ws) == 0
+    sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+    assert sorted(sel_np[0].tolist()) == list(range(300))
+    assert sorted(sel_np[1][:250].tolist()) == list(range(250)) and np.all(sel_np[1][250:] == -1)
+    for i in range(2):
+        _check_token(w, i, sel_np[i], out_bits)
+
+
 def test_step_one_token_three_kv_heads(spd):
     """Three KV heads with one query token per request: every chunk attends
     over its selected tokens for each head."""
