@@ -194,6 +194,14 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev,
  * are still being scored.  This composes the two operations the
  * mxfp4_pages page names (index top-k, then the pa_decode gather over the
  * chosen tokens); the results equal those of the two calls in sequence.
+ * With T = 1 and rows that fit (at most 16 chunks of 32 pages per request,
+ * one workgroup per chunk, all resident at once), the launch runs
+ * chunk-local: the chunks of a request exchange histogram counts and the
+ * candidates of the threshold bin through the workspace, and each attends
+ * over its own share of the selection.  The selected set is the same; the
+ * order of the positions in a row may differ.  The workspace size depends
+ * on how many workgroups fit the current device, which the workspace
+ * function queries (size and call on the same device).
  *
  * index_q_dev, index_pages_dev   as for mono_index_score_topk.
  * q_dev, k_pages_dev, v_pages_dev, kv_heads, scale, out_dev   as for
