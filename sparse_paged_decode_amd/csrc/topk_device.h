@@ -493,6 +493,15 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
   // Bit u of lds.marks[b][tid]: token b * kSelBatch + tid * kSelPer + u is
   // above B1.  The batch loop is rolled over groups of kSelAhead + 1 batches
   // (a static ring of registers within a group).
+  // The bin tests as two float comparisons against the smallest values of
+  // bins B1 and B1 + 1: key order is float order except that -0 and +0
+  // have different keys, NaN has key 0, and the keys of bins 0..3 below
+  // -inf's are NaN bit patterns.  So the integer keys decide when a bound
+  // is +0 (B1 is 1023 or 1024), when B1 is below bin 4, or when B1 + 1
+  // would be past +inf's bin.
+  const bool fcmp = B1 >= 4u && B1 != 1023u && B1 != 1024u && B1 <= 2043u;
+  auto key_value = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key); };
+  const float f_lo = key_value(B1 << kHistShift), f_hi = key_value((B1 + 1u) << kHistShift);
   uint32_t mine = 0;
   for (int b0 = 0; b0 < nb; b0 += kSelAhead + 1) {
 #pragma unroll
@@ -502,14 +511,27 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
       if (b >= nb) continue;  // uniform
       const f32x4_t* cur = v[bb];
       const int j0 = b * kSelBatch + tid * kSelPer;
+      const int n_in = max(0, min(kSelPer, n_valid - j0));
+      const uint32_t in_mask = n_in >= 32 ? 0xFFFFFFFFu : ((1u << n_in) - 1u);
       uint32_t hi = 0, eq = 0;
+      if (fcmp) {
 #pragma unroll
-      for (int u = 0; u < kSelPer; ++u) {
-        const uint32_t bin = score_key(cur[u >> 2][u & 3]) >> kHistShift;
-        const bool in = j0 + u < n_valid;
-        hi |= (in && bin > B1) ? (1u << u) : 0u;
-        eq |= (in && bin == B1) ? (1u << u) : 0u;
+        for (int u = 0; u < kSelPer; ++u) {
+          const float x = cur[u >> 2][u & 3];
+          const bool above_hi = x >= f_hi;
+          hi |= above_hi ? (1u << u) : 0u;
+          eq |= (!above_hi && x >= f_lo) ? (1u << u) : 0u;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+          const uint32_t bin = score_key(cur[u >> 2][u & 3]) >> kHistShift;
+          hi |= bin > B1 ? (1u << u) : 0u;
+          eq |= bin == B1 ? (1u << u) : 0u;
+        }
       }
+      hi &= in_mask;
+      eq &= in_mask;
       lds.marks[b][tid] = (uint16_t)hi;
       mine += __popc(hi);
       // Candidates go to LDS now (an LDS atomic, no memory wait), without
