@@ -305,14 +305,16 @@ __device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, in
   return sp;
 }
 
-// Where pick_in_bin reads the tokens of the threshold bin from.
-enum : int { kSrcLds = 0, kSrcList = 1, kSrcScores = 2 };
+// Where pick_in_bin reads the tokens of the threshold bin from: LDS pairs
+// of (key, j), LDS pairs of (score bits, j), the candidate list, or the
+// score row itself.
+enum : int { kSrcLds = 0, kSrcList = 1, kSrcScores = 2, kSrcLdsBits = 3 };
 
 // The remaining k - above tokens, all in histogram bin B1 (which holds
 // in_bin tokens), by two more radix passes (key bits 20..10, then 9..0);
 // exact ties at the threshold go to the lowest token indices.  Slots
-// above..k-1 of the output are filled.  With kSrcLds the candidates are in
-// lds.cand[0..in_bin) already.
+// above..k-1 of the output are filled.  With kSrcLds or kSrcLdsBits the
+// candidates are in lds.cand[0..in_bin) already.
 __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds, uint32_t B1, uint32_t above,
                                             uint32_t in_bin, int src) {
   const int tid = thread_index();
@@ -321,12 +323,12 @@ __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds
   __syncthreads();
 
   const uint32_t R = (uint32_t)a.k - above;  // 1 <= R <= in_bin
-  const int n_src = src == kSrcScores ? n_valid : (int)in_bin;
+  const int n_src = src == kSrcScores ? n_valid : (int)in_bin;  // every source but the score row holds in_bin entries
   // All three sources yield the same multiset of (key, j).
   auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
-    if (src == kSrcLds) {
+    if (src == kSrcLds || src == kSrcLdsBits) {
       const uint2 c = lds.cand[e];
-      key = c.x;
+      key = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
       j = (int)c.y;
       return true;
     }
@@ -536,14 +538,15 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
       mine += __popc(hi);
       // Candidates go to LDS now (an LDS atomic, no memory wait), without
       // branches: lanes write every slot u, the ones that are not
-      // candidates into a spare entry.
+      // candidates into a spare entry.  They hold the score bits; the radix
+      // passes turn the few real candidates into keys.
       if (in_lds && __ballot(eq != 0u) != 0ull) {
         uint32_t c = 0;
         if (eq) c = atomicAdd(&lds.cnt, (uint32_t)__popc(eq));
 #pragma unroll
         for (int u = 0; u < kSelPer; ++u) {
           const uint32_t pos = ((eq >> u) & 1u) ? c + (uint32_t)__popc(eq & ((1u << u) - 1u)) : (uint32_t)kLdsCand;
-          lds.cand[min(pos, (uint32_t)kLdsCand)] = make_uint2(score_key(cur[u >> 2][u & 3]), (uint32_t)(j0 + u));
+          lds.cand[min(pos, (uint32_t)kLdsCand)] = make_uint2(__float_as_uint(cur[u >> 2][u & 3]), (uint32_t)(j0 + u));
         }
       }
     }
@@ -574,7 +577,7 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
     if (tid == 0) raise_error(a.err, kErrSelection);
     return;
   }
-  pick_in_bin(a, lds, B1, above, in_bin, in_lds ? kSrcLds : kSrcScores);
+  pick_in_bin(a, lds, B1, above, in_bin, in_lds ? kSrcLdsBits : kSrcScores);
 }
 
 }  // namespace mono
