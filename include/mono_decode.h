@@ -199,9 +199,9 @@ int mono_pa_decode_mxfp4(const uint16_t* q_dev, const uint8_t* k_pages_dev,
  * chunk-local: the chunks of a request exchange histogram counts and the
  * candidates of the threshold bin through the workspace, and each attends
  * over its own share of the selection.  The selected set is the same; the
- * order of the positions in a row may differ.  The workspace size depends
- * on how many workgroups fit the current device, which the workspace
- * function queries (size and call on the same device).
+ * order of the positions in a row may differ.  The workspace then also
+ * holds, per query token, 16 exchange regions of 2048 (key, position)
+ * pairs (256 KiB), included in mono_sparse_decode_workspace().
  *
  * index_q_dev, index_pages_dev   as for mono_index_score_topk.
  * q_dev, k_pages_dev, v_pages_dev, kv_heads, scale, out_dev   as for
