@@ -857,6 +857,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       }
     }
     __syncthreads();  // the next item reuses the LDS
+    if (n_items <= gridDim.x) break;  // every item was a first ticket: no ticket is left
     if (tid == 0) s_item = gridDim.x + atomicAdd(ctrl + kHdrTicket, 1u);
     __syncthreads();
     t = s_item;
