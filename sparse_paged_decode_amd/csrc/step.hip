@@ -297,12 +297,12 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
 }
 
 // Every thread's memory updates are complete, then this workgroup arrives at
-// *cnt and waits until `target` workgroups have.
+// *cnt and waits until `target` workgroups have.  The arrival returns the
+// count, so the last workgroup to arrive does not poll.
 __device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint32_t* err) {
   wait_vmem();
   __syncthreads();
-  if (thread_index() == 0) {
-    atomicAdd(cnt, 1u);
+  if (thread_index() == 0 && atomicAdd(cnt, 1u) + 1u < target) {
     uint32_t spins = 0;
     while (load_coherent(cnt) < target) {
       __builtin_amdgcn_s_sleep(1);
