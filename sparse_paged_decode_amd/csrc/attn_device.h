@@ -97,8 +97,10 @@ struct AttnGroup {
   uint32_t valid;            // token m is a candidate
 };
 
+// Returns true in the workgroup that wrote the output (the only split, or
+// the last split to arrive, which merged the others).
 template <class Fmt, bool kLocal = false>
-__device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
+__device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
   const int e0 = a.e0, e1 = a.e1, pos = a.pos, H = a.H, h = a.h, split = a.split, n_splits = a.n_splits;
@@ -323,7 +325,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
   uint16_t* orow = a.out + (size_t)hd * kHeadDim + d0;
   if (n_splits == 1) {
     store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
-    return;
+    return true;
   }
 
   const size_t slot = (size_t)split;
@@ -346,7 +348,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     *s_last = (prev == (uint32_t)(n_splits - 1)) ? 1u : 0u;
   }
   __syncthreads();
-  if (!*s_last) return;
+  if (!*s_last) return false;
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
   // All partials are requested at once (up to kMergeBatch splits a round
@@ -393,6 +395,7 @@ __device__ __forceinline__ void attn_split(const AttnArgs& a, AttnLds& lds) {
     M = Mb;
   }
   store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
+  return true;
 }
 
 }  // namespace mono

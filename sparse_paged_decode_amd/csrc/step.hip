@@ -622,7 +622,18 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     aa.lptab = (const __attribute__((address_space(3))) int32_t*)lds.ptab;
     aa.tok0 = tok0;
     aa.page0 = p_begin;
-    attn_split<Fmt, true>(aa, lds.u.attn);
+    const bool merged = attn_split<Fmt, true>(aa, lds.u.attn);
+    // The workgroup that wrote the output is the last to use the split
+    // counter, and every chunk's output-slot atomic completed before its
+    // split arrived (the wait before the arrival covers it): both counters
+    // can start from zero for the next call.
+    if (merged && tid == 0) {
+      aa.split_cnt[0] = 0u;
+      if (h == 0) {
+        wait_vmem();
+        ctrl[lay.out_cnt + i] = 0u;
+      }
+    }
     __syncthreads();  // the next head reuses the combine area
   }
 
@@ -652,12 +663,14 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       for (int x = L + tid; x < k; x += kBlock) store_coherent(reinterpret_cast<uint32_t*>(out + x), 0xffffffffu);
   }
   if (done_prev == (uint32_t)(nch - 1)) {
+    // Every chunk of the request has passed its barriers and read the rows.
     for (int x = tid; x < kHistBins; x += kBlock) {
       g1[x] = 0u;
       g2[x] = 0u;
     }
     for (int x = tid; x < 1024; x += kBlock) g3[x] = 0u;
     if (tid < kLocalMaxChunks) gt[tid] = 0u;
+    if (tid < kLvlWords) lvl[tid] = 0u;
   }
 }
 
@@ -863,6 +876,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
     t = s_item;
   }
 
+  // A chunk-local launch without clear items, whose every item was a first
+  // ticket, leaves the control block as it found it: each request's chunks
+  // reset their own counters, the ticket counter was never taken and the
+  // header's zero record stands.
+  if (kLocal && n_clear == 0u && n_items <= gridDim.x) return;
   // Every workgroup has taken its last ticket before it counts itself out,
   // so the last one to leave can reset the control block for the next call
   // and record this layout's zero region as clean.
