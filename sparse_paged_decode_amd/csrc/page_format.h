@@ -33,6 +33,12 @@ struct Mxfp4Format {
   __device__ static Chunk load_chunk(const uint8_t* page, ChunkAddr o) {
     return {*reinterpret_cast<const u32x4_t*>(page + o.d), page[o.e]};
   }
+  // As load_chunk, for the index scan, which reads each page once: the loads
+  // carry the non-temporal (streaming) hint.
+  __device__ static Chunk load_chunk_stream(const uint8_t* page, ChunkAddr o) {
+    return {__builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(page + o.d)),
+            __builtin_nontemporal_load(page + o.e)};
+  }
   __device__ static Chunk zero_chunk() { return {u32x4_t{0u, 0u, 0u, 0u}, 127u}; }
   __device__ static bf16x8_t chunk_bf16(const Chunk& c, int s) {
     return dequant8_bf16(c.d[s], e8m0_scale_operand(c.e));
@@ -70,6 +76,9 @@ struct Fp8Format {
     const u32x4_t* p = reinterpret_cast<const u32x4_t*>(page + o.d);
     return {{p[0], p[1]}};
   }
+  // The index scan's loads: plain here (the streaming hint made the fp8 scan
+  // slower, where it speeds up the MXFP4 one).
+  __device__ static Chunk load_chunk_stream(const uint8_t* page, ChunkAddr o) { return load_chunk(page, o); }
   __device__ static Chunk zero_chunk() { return {{u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}}}; }
   // Four e4m3 bytes of one dword -> bf16 pairs (bytes 0,1) and (bytes 2,3).
   __device__ static uint32_t pair_lo(uint32_t w) {

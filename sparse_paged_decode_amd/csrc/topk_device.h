@@ -133,8 +133,8 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
     for (int u = 0; u < kBatch; ++u) {
       const int cp = min(p0 + u - p_begin, n_cp - 1);
       const uint8_t* pg = a.pages + (size_t)__builtin_amdgcn_readlane(lane_pid, cp) * Fmt::kPageBytes;
-      r[u].c[0] = Fmt::load_chunk(pg, off0);
-      r[u].c[1] = Fmt::load_chunk(pg, off1);
+      r[u].c[0] = Fmt::load_chunk_stream(pg, off0);
+      r[u].c[1] = Fmt::load_chunk_stream(pg, off1);
     }
   };
   auto score_page = [&](const Rows& r, int p) {
