@@ -22,6 +22,9 @@ struct Mxfp4Format {
   // The same in the chunk-local step, whose 512 chunk scans all stream at
   // once: two pages ahead measured faster there than one, three or four.
   static constexpr int kScanBatchLocal = 2;
+  // The four-token instance (each page scored for up to four query tokens):
+  // three pages ahead measured faster there than four.
+  static constexpr int kScanBatchMulti = 3;
 
   struct ChunkAddr {
     uint32_t d, e;  // byte offsets of the 16 data bytes and of the scale byte
@@ -68,6 +71,7 @@ struct Fp8Format {
   static constexpr int kRowBytes8 = 128;
   static constexpr int kScanBatch = 2;  // the same bytes in flight as 4 MXFP4 pages
   static constexpr int kScanBatchLocal = 2;  // one page ahead measured slower
+  static constexpr int kScanBatchMulti = 2;
 
   struct ChunkAddr {
     uint32_t d;
