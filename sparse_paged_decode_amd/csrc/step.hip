@@ -827,7 +827,7 @@ template <int TQ, class Fmt, bool kLocal>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
   static_assert(!kLocal || TQ == 1, "the chunk-local step has one query token per request");
   __shared__ std::conditional_t<kLocal, LocalLds, StepLds<TQ>> lds;
-  __shared__ uint32_t s_item, s_flag, s_clear, s_desc, s_pub;
+  __shared__ uint32_t s_item, s_flag, s_clear, s_rec, s_desc, s_pub;
   const int tid = thread_index();
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + lay.ctrl_base);
@@ -837,9 +837,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   // a larger shape than before), the first tickets clear it and every other
   // item waits for them.  The record only changes after every workgroup has
   // read it, so all workgroups agree.
-  if (tid == 0) s_clear = load_coherent(ctrl + kHdrZeroed) < (uint32_t)lay.zero_units ? lay.n_clear : 0u;
+  if (tid == 0) {
+    const uint32_t rec = load_coherent(ctrl + kHdrZeroed);
+    s_clear = rec < (uint32_t)lay.zero_units ? lay.n_clear : 0u;
+    s_rec = rec;
+  }
   __syncthreads();
   const uint32_t n_clear = s_clear;
+  // The record stands for this layout exactly (a larger record means bytes
+  // past this layout's zero region that this call will dirty).
+  const bool record_exact = s_rec == (uint32_t)lay.zero_units;
   const uint32_t n_items = n_clear + lay.n_ready0 + lay.n_queue;
 
   // A workgroup's first ticket is its index (no start-up rush on the
@@ -878,9 +885,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
 
   // A chunk-local launch without clear items, whose every item was a first
   // ticket, leaves the control block as it found it: each request's chunks
-  // reset their own counters, the ticket counter was never taken and the
-  // header's zero record stands.
-  if (kLocal && n_clear == 0u && n_items <= gridDim.x) return;
+  // reset their own counters and the ticket counter was never taken.  It
+  // may leave the header's zero record as it is only when the record is
+  // this layout's own: a record left by a larger layout also covers bytes
+  // past this layout's zero region, which this call used as scratch, so
+  // the exit below must lower it.
+  if (kLocal && n_clear == 0u && n_items <= gridDim.x && record_exact) return;
   // Every workgroup has taken its last ticket before it counts itself out,
   // so the last one to leave can reset the control block for the next call
   // and record this layout's zero region as clean.
