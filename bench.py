@@ -266,6 +266,72 @@ def time_cp(spd, torch, dev, w, iq, ip, bt, sl, reps, heads=4):
     }
 
 
+class StepRunner:
+    """One workload's inputs in HBM and its step.
+
+    The K, V and index-key pools are replicated ``copies`` times; ``step(c)``
+    runs one step over copy c: on sparse workloads one
+    mono_sparse_decode_{mxfp4,fp8} call, on dense ones mono_pa_decode_* alone.
+    ``two_calls(c)`` is the same step as the index call followed by the
+    attention call.  Outputs go to ``out`` / ``sel`` unless others are given.
+    """
+
+    def __init__(self, spd, torch, dev, w, copies):
+        self.spd, self.w = spd, w
+        self.f8 = w.cache == "fp8"
+
+        def bf16(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.q = bf16(w.q)
+        self.bt = torch.from_numpy(w.block_table).to(dev)
+        self.sl = torch.from_numpy(w.seq_lens).to(dev)
+        self.iq = bf16(w.index_q) if w.sparse else None
+        self.kp = [torch.from_numpy(w.k_pool).to(dev)]
+        self.vp = [torch.from_numpy(w.v_pool).to(dev)]
+        self.ip = [torch.from_numpy(w.index_pool).to(dev)] if w.sparse else [None]
+        for _ in range(copies - 1):
+            self.kp.append(self.kp[0].clone())
+            self.vp.append(self.vp[0].clone())
+            self.ip.append(self.ip[0].clone() if w.sparse else None)
+        self.copies = copies
+        self.sel = torch.empty((w.N, w.k), dtype=torch.int32, device=dev) if w.sparse else None
+        self.out = torch.empty_like(self.q)
+        self.ws = spd.Workspace(dev)
+        self.ws_topk = spd.Workspace(dev)
+        self.ws_pa = spd.Workspace(dev)
+
+    def step(self, c, out=None, sel=None):
+        spd, w = self.spd, self.w
+        out = self.out if out is None else out
+        sel = self.sel if sel is None else sel
+        iq, q, bt, sl, kp, vp, ip = self.iq, self.q, self.bt, self.sl, self.kp[c], self.vp[c], self.ip[c]
+        if w.sparse and self.f8:
+            spd.mono_sparse_decode_fp8(iq, ip, q, kp, vp, bt, sl, w.k, w.scale, w.k_scale, w.v_scale, T=w.T,
+                                       out=out, selected_idx=sel, workspace=self.ws)
+        elif w.sparse:
+            spd.mono_sparse_decode_mxfp4(iq, ip, q, kp, vp, bt, sl, w.k, w.scale, T=w.T, out=out, selected_idx=sel,
+                                         workspace=self.ws)
+        elif self.f8:
+            spd.mono_pa_decode_fp8(q, kp, vp, bt, sl, None, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
+                                   workspace=self.ws_pa)
+        else:
+            spd.mono_pa_decode_mxfp4(q, kp, vp, bt, sl, None, w.scale, T=w.T, out=out, workspace=self.ws_pa)
+
+    def two_calls(self, c, out=None, sel=None):
+        spd, w = self.spd, self.w
+        out = self.out if out is None else out
+        sel = self.sel if sel is None else sel
+        iq, q, bt, sl, kp, vp, ip = self.iq, self.q, self.bt, self.sl, self.kp[c], self.vp[c], self.ip[c]
+        if self.f8:
+            spd.mono_index_score_topk_fp8(iq, ip, bt, sl, w.k, T=w.T, out=sel, workspace=self.ws_topk)
+            spd.mono_pa_decode_fp8(q, kp, vp, bt, sl, sel, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
+                                   workspace=self.ws_pa)
+        else:
+            spd.mono_index_score_topk(iq, ip, bt, sl, w.k, T=w.T, out=sel, workspace=self.ws_topk)
+            spd.mono_pa_decode_mxfp4(q, kp, vp, bt, sl, sel, w.scale, T=w.T, out=out, workspace=self.ws_pa)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -285,50 +351,12 @@ def main():
     dev = torch.device("cuda:0")
     w = workload(args.workload, cache=args.cache)
     f8 = args.cache == "fp8"
-
-    def bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    q = bf16(w.q)
-    bt = torch.from_numpy(w.block_table).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
-    iq = bf16(w.index_q) if w.sparse else None
     copies = max(1, args.copies)
-    kp = [torch.from_numpy(w.k_pool).to(dev)]
-    vp = [torch.from_numpy(w.v_pool).to(dev)]
-    ip = [torch.from_numpy(w.index_pool).to(dev)] if w.sparse else [None]
-    for _ in range(copies - 1):
-        kp.append(kp[0].clone())
-        vp.append(vp[0].clone())
-        ip.append(ip[0].clone() if w.sparse else None)
-    sel = torch.empty((w.N, w.k), dtype=torch.int32, device=dev) if w.sparse else None
-    out = torch.empty_like(q)
-    ws = spd.Workspace(dev)
-    ws_topk = spd.Workspace(dev)
-    ws_pa = spd.Workspace(dev)
+    run = StepRunner(spd, torch, dev, w, copies)
+    q, bt, sl, iq, kp, vp, ip = run.q, run.bt, run.sl, run.iq, run.kp, run.vp, run.ip
+    sel = run.sel
     stream = torch.cuda.current_stream(dev)
-
-    def step(c):
-        if w.sparse and f8:
-            spd.mono_sparse_decode_fp8(iq, ip[c], q, kp[c], vp[c], bt, sl, w.k, w.scale, w.k_scale, w.v_scale, T=w.T,
-                                       out=out, selected_idx=sel, workspace=ws)
-        elif w.sparse:
-            spd.mono_sparse_decode_mxfp4(iq, ip[c], q, kp[c], vp[c], bt, sl, w.k, w.scale, T=w.T, out=out,
-                                         selected_idx=sel, workspace=ws)
-        elif f8:
-            spd.mono_pa_decode_fp8(q, kp[c], vp[c], bt, sl, None, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
-                                   workspace=ws_pa)
-        else:
-            spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, None, w.scale, T=w.T, out=out, workspace=ws_pa)
-
-    def two_calls(c):
-        if f8:
-            spd.mono_index_score_topk_fp8(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
-            spd.mono_pa_decode_fp8(q, kp[c], vp[c], bt, sl, sel, w.scale, w.k_scale, w.v_scale, T=w.T, out=out,
-                                   workspace=ws_pa)
-        else:
-            spd.mono_index_score_topk(iq, ip[c], bt, sl, w.k, T=w.T, out=sel, workspace=ws_topk)
-            spd.mono_pa_decode_mxfp4(q, kp[c], vp[c], bt, sl, sel, w.scale, T=w.T, out=out, workspace=ws_pa)
+    step, two_calls = run.step, run.two_calls
 
     for s in range(args.warmup):
         step(s % copies)

@@ -318,7 +318,10 @@ int fp8_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t 
  * value nearest v / 2^(byte-127), ties to the even code, magnitudes above 6
  * saturating to 6, sign in bit 3 (-0.0 gives code 8); an all-zero block
  * has byte 0; a block holding NaN or +-inf gets byte 0xFF and codes 0.
- * The result is exact (integer arithmetic on the bf16 fields).
+ * The scale byte comes from integer arithmetic on the bf16 exponent
+ * fields; each pair of elements is converted by the gfx950 scaled fp4
+ * conversion with the fp32 scale 2^(byte-127), which rounds to nearest,
+ * ties to even, and saturates at 6 exactly as above.
  *
  * k_rows_dev, v_rows_dev  bf16 [n, kv_heads, 128]; index_rows_dev bf16
  *                  [n, 128].  Each may be NULL together with its pool, and

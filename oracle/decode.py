@@ -78,15 +78,23 @@ def sequence_rows(pool, bt_row, n_tokens, head=None):
     return rows[:n_tokens]
 
 
+def scores_of_rows(index_q_bits, rows):
+    """Exact scores of dequantised index-key rows ``[n, 128]`` for one query token.
+
+    ``index_q_bits``: bf16 bit patterns ``[128]``.  The score of a row is its
+    dot product with the dequantised index-q row (float64; every product of a
+    bf16 value and an MXFP4 or e4m3 value is exact).
+    """
+    return rows @ mxfp4.bf16_bits_to_f64(index_q_bits)
+
+
 def index_scores(index_q_bits, index_pool, bt_row, pos):
     """Exact scores ``s[j]`` of tokens ``j = 0..pos`` for one query token.
 
     ``index_q_bits``: bf16 bit patterns ``[128]``.  The score is the dot
     product of the dequantised index-q row with each dequantised index-K row.
     """
-    iq = mxfp4.bf16_bits_to_f64(index_q_bits)
-    rows = sequence_rows(index_pool, bt_row, int(pos) + 1)
-    return rows @ iq
+    return scores_of_rows(index_q_bits, sequence_rows(index_pool, bt_row, int(pos) + 1))
 
 
 def topk(scores, k):
@@ -124,20 +132,38 @@ def candidates(pos, selected_row=None):
     return sel[(sel >= 0) & (sel <= pos)]
 
 
+def softmax_weights(q_bits, k_rows, scale):
+    """Softmax weights ``p [16, n]`` of 16 query heads over K rows ``[n, 128]``
+    (float64): ``p_hj = exp(z_hj - max_j z_hj) / sum_j exp(...)`` with
+    ``z_hj = scale * q_h . k_j``."""
+    q = mxfp4.bf16_bits_to_f64(q_bits)
+    z = scale * (q @ k_rows.T)  # [16, n]
+    z = z - z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    return p / p.sum(axis=1, keepdims=True)
+
+
 def attend(q_bits, k_rows, v_rows, scale):
     """Softmax attention of 16 query heads over gathered K/V rows (float64).
 
     ``q_bits`` bf16 bits ``[16, 128]``; ``k_rows``/``v_rows`` ``[n, 128]``.
     Returns ``[16, 128]``; zeros when n == 0.
     """
-    q = mxfp4.bf16_bits_to_f64(q_bits)
     if k_rows.shape[0] == 0:
-        return np.zeros((q.shape[0], HEAD_DIM))
-    z = scale * (q @ k_rows.T)  # [16, n]
-    z = z - z.max(axis=1, keepdims=True)
-    p = np.exp(z)
-    p = p / p.sum(axis=1, keepdims=True)
-    return p @ v_rows
+        return np.zeros((np.asarray(q_bits).shape[0], HEAD_DIM))
+    return softmax_weights(q_bits, k_rows, scale) @ v_rows
+
+
+def decode_rows(q_bits, k_rows, v_rows, pos, scale, selected_row=None, k_scale=1.0, v_scale=1.0):
+    """Attention output ``[16, 128]`` for one query token from its request's rows.
+
+    ``k_rows`` / ``v_rows``: the request's dequantised K and V rows of tokens
+    ``0..n-1`` (``sequence_rows``), with n past every candidate.  ``k_scale``
+    / ``v_scale`` multiply every K / V value (the fp8 caches' per-tensor
+    scales; 1 for MXFP4); the products are exact in float64.
+    """
+    cand = candidates(pos, selected_row)
+    return attend(q_bits, k_rows[cand] * float(k_scale), v_rows[cand] * float(v_scale), scale)
 
 
 def decode_one(q_bits, k_pool, v_pool, bt_row, pos, scale, selected_row=None, head=0, k_scale=1.0, v_scale=1.0):
@@ -148,9 +174,9 @@ def decode_one(q_bits, k_pool, v_pool, bt_row, pos, scale, selected_row=None, he
     """
     cand = candidates(pos, selected_row)
     n_seen = int(cand.max()) + 1 if cand.size else 0
-    k_all = sequence_rows(k_pool, bt_row, n_seen, head) * float(k_scale)
-    v_all = sequence_rows(v_pool, bt_row, n_seen, head) * float(v_scale)
-    return attend(q_bits, k_all[cand], v_all[cand], scale)
+    k_all = sequence_rows(k_pool, bt_row, n_seen, head)
+    v_all = sequence_rows(v_pool, bt_row, n_seen, head)
+    return decode_rows(q_bits, k_all, v_all, pos, scale, selected_row, k_scale, v_scale)
 
 
 def pa_decode(q_bits, k_pool, v_pool, block_table, seq_lens, T, scale, selected=None, head=0, k_scale=1.0,

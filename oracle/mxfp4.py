@@ -36,29 +36,27 @@ E2M1_MAGNITUDES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
 def page_views(pages):
     """(data, scale) zero-copy views of uint8 pages ``[..., 8704]``.
 
-    Follows ``mxfp4_page_views`` on the mxfp4_pages page: the data view is
-    ``[..., 128, 64]`` at byte offset 0 with row stride 64, the scale view is
-    ``[..., 128, 4]`` at byte offset 128*64 with row stride 4, and both keep
-    the leading dims and their strides.  A wrong dtype, a last dim other than
-    8704 or a non-unit byte stride raises ValueError, as there.
+    The page geometry of the mxfp4_pages page (module docstring and
+    ``mxfp4_page_views``): bytes 0..8191 of a page are its 128 rows of 64
+    packed e2m1 bytes, bytes 8192..8703 its 128 rows of 4 e8m0 bytes.  The
+    data view is the first region of the last axis split into
+    ``[..., 128, 64]``, the scale view the second split into ``[..., 128, 4]``;
+    both keep the leading dims and their strides, and writes through them
+    land in ``pages``.  A dtype other than uint8, a last dim other than 8704
+    or bytes of a page that are not adjacent raise ValueError.
     """
     pages = np.asarray(pages)
-    if pages.dtype != np.uint8 or pages.ndim < 1 or pages.shape[-1] != PAGE_BYTES:
-        raise ValueError(
-            f"MXFP4 pages must be uint8 [..., {PAGE_BYTES}], got {pages.dtype} {pages.shape}"
-        )
+    if pages.dtype != np.uint8:
+        raise ValueError(f"page views need uint8 bytes, not {pages.dtype}")
+    if pages.ndim < 1 or pages.shape[-1] != PAGE_BYTES:
+        raise ValueError(f"the last axis must be one {PAGE_BYTES}-byte page; shape is {pages.shape}")
     if pages.strides[-1] != 1:
-        raise ValueError("MXFP4 pages need a contiguous byte axis")
+        raise ValueError(f"the bytes of a page must be adjacent (last-axis stride {pages.strides[-1]}, not 1)")
     lead = pages.shape[:-1]
-    lead_strides = pages.strides[:-1]
-    data = np.lib.stride_tricks.as_strided(
-        pages, shape=(*lead, PAGE_TOKENS, DATA_BYTES), strides=(*lead_strides, DATA_BYTES, 1)
-    )
-    # The scale view starts DATA_REGION bytes into each page.
-    tail = pages[..., DATA_REGION:]
-    scale = np.lib.stride_tricks.as_strided(
-        tail, shape=(*lead, PAGE_TOKENS, SCALE_BYTES), strides=(*lead_strides, SCALE_BYTES, 1)
-    )
+    data = pages[..., :DATA_REGION].view()
+    data.shape = (*lead, PAGE_TOKENS, DATA_BYTES)  # splits the unit-stride axis in place: never a copy
+    scale = pages[..., DATA_REGION:].view()
+    scale.shape = (*lead, PAGE_TOKENS, SCALE_BYTES)
     return data, scale
 
 
@@ -94,11 +92,20 @@ def unpack(pages):
     return codes, np.array(scale, dtype=np.uint8)
 
 
+def _e2m1_table():
+    """float64 values of the 16 e2m1 codes: bits 2..0 give the magnitude and
+    bit 3 the sign (code 8 is -0.0)."""
+    mags = np.asarray(E2M1_MAGNITUDES, dtype=np.float64)
+    return np.concatenate([mags, -mags])
+
+
+_E2M1_TABLE = _e2m1_table()
+
+
 def e2m1_value(code):
     """float64 value of e2m1 code(s) 0..15; code 8 gives -0.0."""
-    code = np.asarray(code, dtype=np.int64)
-    mag = np.asarray(E2M1_MAGNITUDES, dtype=np.float64)[code & 7]
-    return np.where((code & 8) != 0, -mag, mag)
+    code = np.asarray(code)
+    return _E2M1_TABLE[(code & 15).astype(np.uint8)]
 
 
 def e8m0_value(e):
@@ -116,9 +123,9 @@ def dequant(pages):
     elements).  Every product is exact in float64.
     """
     codes, scales = unpack(pages)
-    block_scale = e8m0_value(scales)  # [..., 128, 4]
-    per_elem = np.repeat(block_scale, SCALE_BLOCK, axis=-1)  # [..., 128, 128]
-    return e2m1_value(codes) * per_elem
+    block_scale = e8m0_value(scales)  # [..., 128, 4]: block g of row r
+    values = e2m1_value(codes).reshape(*codes.shape[:-1], SCALE_BYTES, SCALE_BLOCK)  # [..., 128, 4, 32]
+    return (values * block_scale[..., None]).reshape(codes.shape)
 
 
 def round_to_f32(x):

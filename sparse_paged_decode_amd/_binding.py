@@ -154,25 +154,26 @@ def _on_gpu(*ts):
 
 
 def mxfp4_page_views(pages):
-    """(data, scale) views of uint8 pages ``[..., 8704]``.
+    """(data, scale) zero-copy views of uint8 pages ``[..., 8704]``.
 
-    As ``mxfp4_page_views`` on the mxfp4_pages page: the data view is
-    ``[..., 128, 64]`` from byte 0 of each page, the scale view ``[..., 128, 4]``
-    from byte 8192, both keeping the leading dims and strides.  Raises
-    ValueError for a dtype other than uint8, a last dim other than 8704 or a
-    non-unit stride on the byte axis.
+    The page geometry of the mxfp4_pages page (module docstring and
+    ``mxfp4_page_views``): bytes 0..8191 of a page are 128 rows of 64 packed
+    e2m1 bytes and bytes 8192..8703 are 128 rows of 4 e8m0 bytes.  So the
+    data view is the first 8192 bytes of the last axis split into
+    ``[..., 128, 64]`` and the scale view the last 512 split into
+    ``[..., 128, 4]``; leading dims and strides are those of ``pages``.
+    Raises ValueError for a dtype other than uint8, a last dim other than
+    8704 or bytes of a page that are not adjacent.
     """
-    if pages.dtype != torch.uint8 or pages.dim() < 1 or pages.shape[-1] != PAGE_BYTES:
-        raise ValueError(f"MXFP4 pages are uint8 [..., {PAGE_BYTES}]; got {pages.dtype} {tuple(pages.shape)}")
+    if pages.dtype != torch.uint8:
+        raise ValueError(f"page views need uint8 bytes, not {pages.dtype}")
+    if pages.dim() < 1 or pages.shape[-1] != PAGE_BYTES:
+        raise ValueError(f"the last axis must be one {PAGE_BYTES}-byte page; shape is {tuple(pages.shape)}")
     if pages.stride(-1) != 1:
-        raise ValueError("MXFP4 pages need a contiguous byte axis")
-    lead = list(pages.shape[:-1])
-    lead_strides = list(pages.stride()[:-1])
-    base = pages.storage_offset()
-    data = pages.as_strided(lead + [PAGE_TOKENS, DATA_BYTES], lead_strides + [DATA_BYTES, 1], base)
-    scale = pages.as_strided(
-        lead + [PAGE_TOKENS, SCALE_BYTES], lead_strides + [SCALE_BYTES, 1], base + PAGE_TOKENS * DATA_BYTES
-    )
+        raise ValueError(f"the bytes of a page must be adjacent (last-axis stride {pages.stride(-1)}, not 1)")
+    data_bytes = PAGE_TOKENS * DATA_BYTES
+    data = pages.narrow(-1, 0, data_bytes).unflatten(-1, (PAGE_TOKENS, DATA_BYTES))
+    scale = pages.narrow(-1, data_bytes, PAGE_TOKENS * SCALE_BYTES).unflatten(-1, (PAGE_TOKENS, SCALE_BYTES))
     return data, scale
 
 

@@ -121,21 +121,6 @@ def test_topk_bad_page_id_is_flagged_not_dereferenced(spd):
     assert spd.check_device_errors(ws) & spd.DEVERR_PAGE_ID
 
 
-@pytest.mark.parametrize("number,samples", [(3, [0, 17, 63]), (4, [0, 1, 2, 3, 258, 511]), (5, [0, 5])])
-def test_topk_full_size_sampled(spd, number, samples):
-    w = workload(number)
-    sel, _ = _run(spd, w, w.k)
-    for i in samples:
-        check_topk_row(sel[i], w, i, w.k)
-    # every row: right count, valid distinct entries, -1 padding
-    pos = decode.query_positions(w.seq_lens, w.T)
-    for i in range(w.N):
-        n = min(w.k, pos[i] + 1)
-        row = sel[i]
-        assert np.all(row[n:] == -1) and np.all((row[:n] >= 0) & (row[:n] <= pos[i]))
-        assert np.unique(row[:n]).size == n
-
-
 # Many query tokens: more filter slices than two rounds of the resident
 # workgroups, so each token's top k is taken by one workgroup.
 MANY = [

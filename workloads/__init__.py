@@ -165,7 +165,8 @@ def make_workload(
 # The five seeded workloads: (name, keyword arguments).  Seeds are 1000 + number.
 WORKLOADS = {
     1: ("tiny_dense_b1_ctx256", dict(B=1, T=1, seq_lens=256, bt_width=2, k=0, identity_table=True)),
-    2: ("dense_b32_ctx8k", dict(B=32, T=1, seq_lens=8192, bt_width=64, k=0)),
+    # 32 x 64 pages taken from a permuted pool of 4096
+    2: ("dense_b32_ctx8k", dict(B=32, T=1, seq_lens=8192, bt_width=64, k=0, extra_pages=2048)),
     3: ("sparse_b64_ctx32k_top2048", dict(B=64, T=1, seq_lens=32768, bt_width=256, k=2048)),
     4: (
         "multitoken_sparse_b128_t4_ctx16k-64k_top2048",
