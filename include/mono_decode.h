@@ -221,6 +221,37 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * mono_sparse_decode_mxfp4 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument.  Its workspace is a static device
+ * array of MONO_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * device it runs on until the process ends.  The call allocates nothing and
+ * calls no allocating routine.
+ *
+ * Arguments, results and errors are those of mono_sparse_decode_mxfp4,
+ * except:
+ *   - a shape whose workspace (mono_sparse_decode_workspace) exceeds
+ *     MONO_NOALLOC_SCRATCH_BYTES gives MONO_ENOSPC;
+ *   - err_dev: NULL, or a device uint32 word into which the device error
+ *     bits (MONO_DEVERR_*) this call raised are OR-ed (by a second small
+ *     launch on the same stream); the scratch's own error word is cleared.
+ *   - The first call on a device sets the scratch up (zeroes its header)
+ *     and synchronises `stream` once; it is refused (MONO_EINVAL) while
+ *     `stream` is being captured.  Later calls only enqueue work.
+ * All calls on one device share its scratch, which keeps the last call's
+ * contents (each call leaves what must start at zero zero again): calls
+ * that overlap in time on one device race and give unspecified results.
+ * ------------------------------------------------------------------------- */
+#define MONO_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int mono_sparse_decode_mxfp4_noalloc(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                                     const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                                     const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                                     const int32_t* block_table_dev, int bt_stride,
+                                     const int32_t* seq_lens_dev, int B, int T, int k, float scale,
+                                     int32_t* selected_idx_dev, uint16_t* out_dev, uint32_t* err_dev,
+                                     void* stream);
+
+/* ---------------------------------------------------------------------------
  * Indexer context parallelism, emulated on one GPU.  Page
  * "vllm.models.minimax_m3.amd.mono.weights", _build_cp_qkv: every rank keeps
  * all ranks' index-q heads, so rank r can score its share of every

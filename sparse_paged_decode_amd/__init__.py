@@ -24,6 +24,10 @@ of all index heads, then a merge of each head's candidates):
 indexer_cp_topk, built on mono_index_score_topk(page_window=...) and
 mono_topk_merge.
 
+Callers that cannot allocate device memory (graph capture, serving loops)
+use mono_sparse_decode_mxfp4_noalloc: the same step with the library's
+static per-device scratch in place of a workspace.
+
 New tokens' K, V and index-key rows enter the pages through the int64 slot
 mapping (dispatch page, _slots_shared):
 
@@ -41,6 +45,12 @@ from ._binding import (  # noqa: F401
     FP8_PAGE_BYTES,
     HEAD_DIM,
     KernelTimer,
+    MONO_EHIP,
+    MONO_EINVAL,
+    MONO_ENOSPC,
+    MONO_ENOTSUP,
+    MONO_OK,
+    NOALLOC_SCRATCH_BYTES,
     PAGE_BYTES,
     PAGE_TOKENS,
     Q_HEADS_PER_KV,
@@ -59,6 +69,7 @@ from ._binding import (  # noqa: F401
     mono_pa_decode_mxfp4,
     mono_sparse_decode_fp8,
     mono_sparse_decode_mxfp4,
+    mono_sparse_decode_mxfp4_noalloc,
     mono_topk_merge,
     mxfp4_page_views,
     mxfp4_pages_dequant,

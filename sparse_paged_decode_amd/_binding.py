@@ -54,6 +54,7 @@ EXPORTED_SYMBOLS = (
     "mono_pa_decode_mxfp4",
     "mono_sparse_decode_workspace",
     "mono_sparse_decode_mxfp4",
+    "mono_sparse_decode_mxfp4_noalloc",
     "mono_insert_mxfp4",
     "mono_index_score_topk_fp8",
     "mono_index_score_topk_window",
@@ -104,6 +105,7 @@ def load_library(path=LIB_PATH):
         "mono_pa_decode_mxfp4": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, P, P, SZ, P]),
         "mono_sparse_decode_workspace": (SZ, [I, I, I, I, I]),
         "mono_sparse_decode_mxfp4": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, SZ, P]),
+        "mono_sparse_decode_mxfp4_noalloc": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, P, P, P, P]),
         "mono_insert_mxfp4": (I, [P, P, P, P, I64, I, P, P, P, I64, P, P]),
         "mono_index_score_topk_fp8": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
         "mono_index_score_topk_window": (I, [P, P, I64, P, I, P, I, I, I, I, I, P, P, P, SZ, P]),
@@ -579,6 +581,51 @@ def _sparse_decode(fmt, index_q, index_pages, q, k_pages, v_pages, block_table, 
     else:
         _check(lib.mono_sparse_decode_fp8(*args, ctypes.c_float(float(k_scale)), ctypes.c_float(float(v_scale)),
                                           *tail))
+    return out, selected_idx
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mono_sparse_decode_mxfp4_noalloc(index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, k, scale,
+                                     out, selected_idx, *, T=1, err=None):
+    """:func:`mono_sparse_decode_mxfp4` without a workspace and without any allocation.
+
+    The library's static per-device scratch (64 MiB) serves as the
+    workspace; ``out`` and ``selected_idx`` must be given.  ``err``: None or
+    an int32/uint32 device tensor of one element into which the call's
+    device error bits are OR-ed.  Calls that overlap in time on one device
+    race.  Returns ``(out, selected_idx)``.
+    """
+    lib = load_library()
+    _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM,
+          "index_q must be bf16 [B*T, 128]")
+    _need(index_q.is_contiguous(), "index_q must be contiguous")
+    _check_pages(index_pages, "index_pages", 2)
+    _need(q.dtype == torch.bfloat16 and q.dim() == 3 and q.shape[2] == HEAD_DIM, "q must be bf16 [B*T, 16*H, 128]")
+    _need(q.is_contiguous(), "q must be contiguous")
+    _check_pages(k_pages, "k_pages", 3)
+    _check_pages(v_pages, "v_pages", 3)
+    _need(k_pages.shape == v_pages.shape, "k_pages and v_pages must have the same shape")
+    _need(index_pages.shape[0] == k_pages.shape[0], "the index pool and the K/V pools must have the same page count")
+    H = k_pages.shape[1]
+    _need(q.shape[1] == Q_HEADS_PER_KV * H, f"q has {q.shape[1]} heads; the pools have {H} KV heads x 16")
+    N = q.shape[0]
+    _need(index_q.shape[0] == N, "index_q and q must have the same number of query tokens")
+    B = _check_tables(block_table, seq_lens, N, T)
+    dev = _on_gpu(index_q, index_pages, q, k_pages, v_pages, block_table, seq_lens, out, selected_idx)
+    k = int(k)
+    _need(k >= 1, "k must be >= 1")
+    _need(selected_idx.dtype == torch.int32 and tuple(selected_idx.shape) == (N, k) and selected_idx.is_contiguous(),
+          "selected_idx must be int32 [B*T, k]")
+    _need(out.dtype == torch.bfloat16 and out.shape == q.shape and out.is_contiguous(), "out must match q")
+    if err is not None:
+        _on_gpu(q, err)
+        _need(err.dtype in (torch.int32, torch.uint32) and err.numel() == 1, "err must be one 32-bit device word")
+    _check(lib.mono_sparse_decode_mxfp4_noalloc(
+        _ptr(index_q), _ptr(index_pages), _ptr(q), _ptr(k_pages), _ptr(v_pages), k_pages.shape[0], H,
+        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), B, T, k, ctypes.c_float(float(scale)),
+        _ptr(selected_idx), _ptr(out), _ptr(err), _stream(dev)))
     return out, selected_idx
 
 

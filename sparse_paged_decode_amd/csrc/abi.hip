@@ -351,6 +351,31 @@ int mono_sparse_decode_mxfp4(const uint16_t* index_q_dev, const uint8_t* index_p
                             1.f, 1.f, selected_idx_dev, out_dev, ws_dev, ws_bytes, stream);
 }
 
+int mono_sparse_decode_mxfp4_noalloc(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                                     const uint16_t* q_dev, const uint8_t* k_pages_dev,
+                                     const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
+                                     const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
+                                     int B, int T, int k, float scale, int32_t* selected_idx_dev,
+                                     uint16_t* out_dev, uint32_t* err_dev, void* stream) {
+  clear_error();
+  const char* what = "mono_sparse_decode_mxfp4_noalloc";
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (kv_heads < 1 || kv_heads > kMaxHeads)
+    return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
+  if (err_dev && !aligned(err_dev, 4)) return set_error(MONO_EINVAL, "%s: err needs 4-byte alignment", what);
+  const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
+  if (lay.total > kNoAllocScratchBytes)
+    return set_error(MONO_ENOSPC, "%s: this shape needs %zu B of scratch; the static scratch holds %zu B", what,
+                     lay.total, kNoAllocScratchBytes);
+  uint8_t* ws = nullptr;
+  if (int rc = noalloc_scratch((hipStream_t)stream, &ws)) return rc;
+  if (int rc = sparse_decode_impl(kFmtMxfp4, what, index_q_dev, index_pages_dev, q_dev, k_pages_dev, v_pages_dev,
+                                  num_pages, kv_heads, block_table_dev, bt_stride, seq_lens_dev, B, T, k, scale, 1.f,
+                                  1.f, selected_idx_dev, out_dev, ws, kNoAllocScratchBytes, stream))
+    return rc;
+  return err_dev ? launch_scratch_errors(ws, lay.err, err_dev, (hipStream_t)stream) : MONO_OK;
+}
+
 int mono_sparse_decode_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, const uint16_t* q_dev,
                            const uint8_t* k_pages_dev, const uint8_t* v_pages_dev, int64_t num_pages, int kv_heads,
                            const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B, int T,

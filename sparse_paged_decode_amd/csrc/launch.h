@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "mono_decode.h"
+
 namespace mono {
 
 // Records `what` and the pending HIP launch error (if any) as the thread's
@@ -128,5 +130,14 @@ struct StepArgs {
   uint8_t* ws;
 };
 int launch_step(const StepArgs& a, const StepLayout& lay, hipStream_t stream, const char* what);
+
+// The allocation-free step call's static scratch (step.hip): its size, and
+// its address on the current device, set up on the first call per device
+// (zeroed header; the stream is synchronised once).  Refused while the
+// stream is being captured.
+constexpr size_t kNoAllocScratchBytes = MONO_NOALLOC_SCRATCH_BYTES;
+int noalloc_scratch(hipStream_t stream, uint8_t** ptr);
+// Moves the error bits of the scratch's error word (at err_offset) into *dst.
+int launch_scratch_errors(uint8_t* scratch_ptr, size_t err_offset, uint32_t* dst, hipStream_t stream);
 
 }  // namespace mono

@@ -1016,4 +1016,65 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
   return check_launch(what);
 }
 
+// ---------------------------------------------------------------------------
+// Static scratch for callers that cannot allocate (the allocation-free step
+// call).  One array per device holds that call's workspace; the code below
+// reaches it only through the address hipGetSymbolAddress returns on each
+// device (in host code the array's name is not a device address).
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kScratchInitWords = 1024;  // error word and header (the first 4 KiB)
+
+// Zeroes the error word and the control-block header once per device, so
+// the first call clears its own zero region (the header records none).
+__global__ void scratch_init_kernel(uint32_t* p) {
+  for (int x = threadIdx.x; x < kScratchInitWords; x += blockDim.x) store_coherent(p + x, 0u);
+}
+
+// Moves the error bits of the scratch's error word into *dst.
+__global__ void scratch_errors_kernel(uint32_t* scratch_err, uint32_t* dst) {
+  const uint32_t v = atomicExch(scratch_err, 0u);
+  if (v) atomicOr(dst, v);
+}
+
+}  // namespace
+
+int noalloc_scratch(hipStream_t stream, uint8_t** ptr) {
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return set_error(MONO_EHIP, "no current HIP device (or device id past %d)", kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &st) != hipSuccess)
+      return set_error(MONO_EHIP, "cannot query the stream's capture status");
+    if (st != hipStreamCaptureStatusNone)
+      return set_error(MONO_EINVAL, "the first call on device %d sets up its scratch and must not be captured", dev);
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return set_error(MONO_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    hipLaunchKernelGGL(scratch_init_kernel, dim3(1), dim3(kBlock), 0, stream, static_cast<uint32_t*>(p));
+    if (int rc = check_launch("scratch set-up")) return rc;
+    // Later calls may come on other streams: the set-up is complete first.
+    const hipError_t es = hipStreamSynchronize(stream);
+    if (es != hipSuccess) return set_error(MONO_EHIP, "scratch set-up on device %d: %s", dev, hipGetErrorString(es));
+    addr[dev] = static_cast<uint8_t*>(p);
+  }
+  *ptr = addr[dev];
+  return MONO_OK;
+}
+
+int launch_scratch_errors(uint8_t* scratch_ptr, size_t err_offset, uint32_t* dst, hipStream_t stream) {
+  hipLaunchKernelGGL(scratch_errors_kernel, dim3(1), dim3(1), 0, stream,
+                     reinterpret_cast<uint32_t*>(scratch_ptr + err_offset), dst);
+  return check_launch("scratch error report");
+}
+
 }  // namespace mono
