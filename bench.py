@@ -100,8 +100,9 @@ def parse():
     p.add_argument("--skip-insert", action="store_true", help="do not time the cache insert")
     p.add_argument("--skip-cp", action="store_true", help="do not time the indexer context-parallel emulation")
     p.add_argument("--skip-clocks", action="store_true",
-                   help="do not read the clocks through rocm-smi (under a profiler, whose preloaded library has "
-                        "already opened the GPU, the child process may not start)")
+                   help="do not sample the clocks under load (about one second of extra steps)")
+    p.add_argument("--skip-ceilings", action="store_true",
+                   help="do not time the read-bandwidth references over the index pool")
     p.add_argument("--skip-two-call", action="store_true",
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -122,20 +123,88 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
 
 
-def gpu_clocks():
-    """Current clocks of GPU 0 from rocm-smi (a child process, run before this
-    process touches the GPU), or None when rocm-smi is unavailable."""
-    import subprocess
-
+def _read_text(path):
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
-        data = json.loads(r.stdout)
-    except Exception:
+        with open(path) as f:
+            return f.read().strip()
+    except OSError:
         return None
-    card = next((v for k, v in sorted(data.items()) if k.startswith("card")), None)
-    if not isinstance(card, dict):
+
+
+def _pci_dir(props):
+    path = f"/sys/bus/pci/devices/{props.pci_domain_id:04x}:{props.pci_bus_id:02x}:{props.pci_device_id:02x}.0"
+    return path if os.path.isdir(path) else None
+
+
+def _dpm_levels(text):
+    """(levels in MHz, index of the current level) of a pp_dpm_* file."""
+    levels, cur = [], None
+    for line in (text or "").splitlines():
+        parts = line.replace(":", " ").split()
+        if len(parts) >= 2 and parts[1].lower().endswith("mhz"):
+            try:
+                levels.append(int(parts[1][:-3]))
+            except ValueError:
+                continue
+            if line.rstrip().endswith("*"):
+                cur = len(levels) - 1
+    return levels, cur
+
+
+def device_info(torch, dev):
+    """The GPU's identity: name, arch, compute units, memory, and from sysfs
+    (when readable) its PCI device id, product name and clock levels."""
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": props.gcnArchName, "compute_units": props.multi_processor_count,
+            "memory_GiB": round(props.total_memory / 2**30, 1)}
+    d = _pci_dir(props)
+    if d:
+        info["pci"] = os.path.basename(d)
+        for key, fname in (("pci_device_id", "device"), ("pci_revision", "revision"),
+                           ("product_name", "product_name")):
+            v = _read_text(os.path.join(d, fname))
+            if v:
+                info[key] = v
+        for key, fname in (("sclk_levels_MHz", "pp_dpm_sclk"), ("mclk_levels_MHz", "pp_dpm_mclk")):
+            levels, _ = _dpm_levels(_read_text(os.path.join(d, fname)))
+            if levels:
+                info[key] = levels
+    return info, d
+
+
+def clocks_under_load(pci_dir, run_steps, seconds=1.0):
+    """Current sclk/mclk levels sampled from sysfs every 2 ms while steps run
+    back to back for about `seconds` (a thread of this process reads the
+    files; nothing is started).  None when sysfs does not expose them."""
+    import threading
+
+    if not pci_dir or not os.path.exists(os.path.join(pci_dir, "pp_dpm_sclk")):
         return None
-    return {k: v for k, v in card.items() if "clock" in k.lower() or k.lower().startswith(("sclk", "mclk", "fclk"))}
+    samples = {"sclk": [], "mclk": []}
+    stop = threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            for key in samples:
+                levels, cur = _dpm_levels(_read_text(os.path.join(pci_dir, f"pp_dpm_{key}")))
+                if cur is not None:
+                    samples[key].append(levels[cur])
+            time.sleep(0.002)
+
+    th = threading.Thread(target=sample)
+    th.start()
+    try:
+        run_steps(seconds)
+    finally:
+        stop.set()
+        th.join()
+    out = {}
+    for key, v in samples.items():
+        if v:
+            out[f"{key}_MHz_median"] = float(np.median(v))
+            out[f"{key}_MHz_max"] = int(max(v))
+            out[f"{key}_samples"] = len(v)
+    return out or None
 
 
 def algorithmic_bytes(w, sel):
@@ -332,6 +401,36 @@ class StepRunner:
             spd.mono_pa_decode_mxfp4(q, kp, vp, bt, sl, sel, w.scale, T=w.T, out=out, workspace=self.ws_pa)
 
 
+def read_ceilings(spd, torch, dev, run, reps, grids=(256, 512, 1024, 2048)):
+    """Read-bandwidth references over the workload's index pool, the pool
+    copies rotated (cold reads): every byte in address order ("stream"), and
+    the pages in block-table order with the index scan's lane pattern
+    ("gather").  GB/s per grid size, from the kernel's mean duration."""
+    w = run.w
+    ids = np.concatenate([w.block_table[b, : -(-int(w.seq_lens[b]) // 128)] for b in range(w.B)]).astype(np.int32)
+    ids_t = torch.from_numpy(ids).to(dev)
+    sink = torch.empty(max(grids), dtype=torch.int32, device=dev)
+    res = {}
+    for mode, name in ((0, "stream"), (1, "gather")):
+        n_pages = run.ip[0].shape[0] if mode == 0 else ids.size
+        nbytes = n_pages * 8704
+        kname = "read_stream_kernel" if mode == 0 else "read_gather_kernel"
+        per = {}
+        for grid in grids:
+            for c in range(run.copies):  # warm-up
+                spd.bench_read(run.ip[c], None if mode == 0 else ids_t, grid=grid, sink=sink)
+            torch.cuda.synchronize(dev)
+            with spd.KernelTimer(capacity=reps + 4) as kt:
+                for r in range(reps):
+                    spd.bench_read(run.ip[r % run.copies], None if mode == 0 else ids_t, grid=grid, sink=sink)
+                torch.cuda.synchronize(dev)
+            us = kt.mean_us[kname]
+            per[str(grid)] = {"kernel_us_mean": round(us, 2), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        res[name] = {"bytes_per_launch": nbytes, "by_grid": per,
+                     "best_GBps": max(v["GBps"] for v in per.values())}
+    return res
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -340,7 +439,6 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-    clocks = None if args.skip_clocks else gpu_clocks()
 
     import torch
 
@@ -433,6 +531,21 @@ def main():
         torch.cuda.synchronize(dev)
         graph_ms = ge[0].elapsed_time(ge[1]) / K
 
+    # Clocks while the step runs back to back (sampled from sysfs).
+    info, pci_dir = device_info(torch, dev)
+    clocks = None
+    if not args.skip_clocks:
+        def run_steps(seconds):
+            t_end = time.perf_counter() + seconds
+            s = 0
+            while time.perf_counter() < t_end:
+                for _ in range(50):
+                    step(s % copies)
+                    s += 1
+                torch.cuda.synchronize(dev)
+
+        clocks = clocks_under_load(pci_dir, run_steps)
+
     # Roofline entry of the step kernel (on dense workloads the attention
     # kernel is the step).
     dom = ("sparse_decode_kernel" if w.sparse else "pa_decode_kernel").replace("_kernel", "_fp8_kernel" if f8 else "_kernel")
@@ -449,6 +562,9 @@ def main():
             cp = time_cp(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
         else:
             cp = {"skipped": f"4 shards x top-{w.k} = {4 * w.k} candidates per query token; the merge takes 8192"}
+    ceilings = None
+    if w.sparse and not f8 and not args.skip_ceilings:
+        ceilings = read_ceilings(spd, torch, dev, run, min(K, 50))
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(w, args.cpu_sample)
@@ -497,11 +613,11 @@ def main():
         },
         "insert": ins,
         "cp_emulation": cp,
+        "read_ceilings": ceilings,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),
-        "device": torch.cuda.get_device_name(dev),
-        "arch": torch.cuda.get_device_properties(dev).gcnArchName,
-        "clocks": clocks,
+        "device": info,
+        "clocks_under_load": clocks,
         "hip": torch.version.hip,
     }
     print(json.dumps(line))

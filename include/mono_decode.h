@@ -388,10 +388,27 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev,
  * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
  * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
  * ------------------------------------------------------------------------- */
-#define MONO_NUM_KERNELS 13
+#define MONO_NUM_KERNELS 15
 int mono_profile_start(int capacity);
 int mono_profile_stop(double* total_ms, int* launches, int n);
 const char* mono_kernel_name(int id);
+
+/* ---------------------------------------------------------------------------
+ * Read-bandwidth references, for benchmarks only: how fast the device reads
+ * MXFP4 pages (mxfp4_pages page: 8704-B pages, 128 x 64 data bytes then
+ * 128 x 4 scale bytes) when it has nothing else to do.
+ *
+ * mode 0: every byte of pages_dev [n_pages, 8704] in address order, 16 B per
+ *         lane per load;
+ * mode 1: the pages page_ids_dev[0..n_pages) (int32 ids into pages_dev),
+ *         each read as the index scan reads it (per 16-row tile, 16 data
+ *         bytes and one scale byte per lane).
+ * `grid` workgroups of 256 threads each read a contiguous share and store
+ * one word to sink_dev[0..grid).  Loads carry the non-temporal hint.
+ * MONO_EINVAL for a bad mode, size, grid (1..65536) or pointer.
+ * ------------------------------------------------------------------------- */
+int mono_bench_read(const uint8_t* pages_dev, const int32_t* page_ids_dev, int64_t n_pages, int mode,
+                    int grid, uint32_t* sink_dev, void* stream);
 
 /* Debug/test only.  Waits for `stream`, then returns the device error bits
  * (MONO_DEVERR_*) accumulated in the workspace and clears them, or a

@@ -56,6 +56,7 @@ from ._binding import (  # noqa: F401
     Q_HEADS_PER_KV,
     MonoError,
     Workspace,
+    bench_read,
     check_device_errors,
     cp_shard_windows,
     fp8_pages_dequant_bf16,

@@ -63,6 +63,7 @@ EXPORTED_SYMBOLS = (
     "mono_sparse_decode_fp8",
     "fp8_pages_dequant_bf16",
     "mono_check_device_errors",
+    "mono_bench_read",
     "mono_profile_start",
     "mono_profile_stop",
     "mono_kernel_name",
@@ -114,6 +115,7 @@ def load_library(path=LIB_PATH):
         "mono_sparse_decode_fp8": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, F, F, P, P, P, SZ, P]),
         "fp8_pages_dequant_bf16": (I, [P, P, I64, P]),
         "mono_check_device_errors": (I, [P, P]),
+        "mono_bench_read": (I, [P, P, I64, I, I, P, P]),
         "mono_profile_start": (I, [I]),
         "mono_profile_stop": (I, [P, P, I]),
         "mono_kernel_name": (ctypes.c_char_p, [I]),
@@ -669,6 +671,27 @@ def mono_insert_mxfp4(slots, *, k_rows=None, v_rows=None, index_rows=None, k_pag
         _ptr(k_rows), _ptr(v_rows), _ptr(index_rows), _ptr(slots), n, H, _ptr(k_pages), _ptr(v_pages),
         _ptr(index_pages), num_pages, _ptr(ws.buf), _stream(dev)))
     return ws
+
+
+def bench_read(pages, page_ids=None, grid=512, sink=None):
+    """Read-bandwidth reference: stream every byte of ``pages`` ``[n, 8704]``
+    (``page_ids`` None) or gather the pages ``page_ids`` (int32 ``[m]``) with
+    the index scan's lane pattern.  Returns the sink (one word per workgroup)."""
+    lib = load_library()
+    _check_pages(pages, "pages", 2)
+    dev = _on_gpu(pages)
+    mode = 0 if page_ids is None else 1
+    n = pages.shape[0]
+    if mode == 1:
+        _on_gpu(pages, page_ids)
+        _need(page_ids.dtype == torch.int32 and page_ids.dim() == 1 and page_ids.is_contiguous(),
+              "page_ids must be int32 [m], contiguous")
+        n = page_ids.shape[0]
+    if sink is None:
+        sink = torch.empty(grid, dtype=torch.int32, device=dev)
+    _need(sink.dtype == torch.int32 and sink.numel() >= grid, "sink must hold grid int32 words")
+    _check(lib.mono_bench_read(_ptr(pages), _ptr(page_ids), n, mode, int(grid), _ptr(sink), _stream(dev)))
+    return sink
 
 
 # --- per-kernel timing ---------------------------------------------------------------

@@ -47,7 +47,7 @@ const char* const kKernelNames[kNumKernels] = {
     "pack_kernel",          "unpack_kernel",         "dequant_f32_kernel",  "dequant_bf16_kernel",
     "index_topk_kernel",    "pa_decode_kernel",      "sparse_decode_kernel", "insert_kernel",
     "index_topk_fp8_kernel", "pa_decode_fp8_kernel", "sparse_decode_fp8_kernel", "dequant_fp8_bf16_kernel",
-    "topk_merge_kernel"};
+    "topk_merge_kernel",    "read_stream_kernel",    "read_gather_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -422,6 +422,19 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev, co
   const uint16_t* const rows[3] = {k_rows_dev, v_rows_dev, index_rows_dev};
   uint8_t* const pools[3] = {k_pages_dev, v_pages_dev, index_pages_dev};
   return launch_insert(rows, pools, row_heads, slots_dev, n, num_pages, err_dev, (hipStream_t)stream);
+}
+
+int mono_bench_read(const uint8_t* pages_dev, const int32_t* page_ids_dev, int64_t n_pages, int mode, int grid,
+                    uint32_t* sink_dev, void* stream) {
+  clear_error();
+  if (mode != 0 && mode != 1) return set_error(MONO_EINVAL, "mono_bench_read: mode must be 0 or 1 (got %d)", mode);
+  if (n_pages < 1 || n_pages > ((int64_t)1 << 30)) return set_error(MONO_EINVAL, "mono_bench_read: n_pages out of range");
+  if (grid < 1 || grid > (1 << 16)) return set_error(MONO_EINVAL, "mono_bench_read: grid must be in [1, 65536]");
+  if (!pages_dev || !sink_dev || (mode == 1 && !page_ids_dev))
+    return set_error(MONO_EINVAL, "mono_bench_read: NULL buffer");
+  if (!aligned(pages_dev, 16) || !aligned(sink_dev, 4) || !aligned(page_ids_dev, 4))
+    return set_error(MONO_EINVAL, "mono_bench_read: pages need 16-byte, ids and sink 4-byte alignment");
+  return launch_read_reference(pages_dev, page_ids_dev, n_pages, mode, grid, sink_dev, (hipStream_t)stream);
 }
 
 int mono_profile_start(int capacity) {

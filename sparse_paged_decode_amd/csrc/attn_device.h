@@ -70,7 +70,7 @@ struct AttnArgs {
   uint16_t* out;            // [16, 128] bf16 output of (query token, KV head)
   float* pm;                // [n_splits, 16] partial maxima of (query token, KV head)
   float* pl;                // [n_splits, 16] partial sums
-  float* pacc;              // [n_splits, 16, 128] partial accumulators
+  float* pacc;              // [n_splits, 2, 256, 4] partial accumulators (see the split's store)
   uint32_t* split_cnt;      // arrivals of (query token, KV head)
   uint32_t* err;
   // Chunk-local attention only: the candidates are LDS entries (token
@@ -337,9 +337,14 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     store_coherent(pl + slot * kQHeads + hd, lsum);
   }
   {
-    float* dst = pacc + (slot * kQHeads + hd) * kHeadDim + d0;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) store_coherent(dst + x, o[x]);
+    // The accumulator slot of a split is 2 x 256 units of 16 B: unit (u, t)
+    // holds dims d0 + 4u .. d0 + 4u + 3 of head hd of thread t, so each
+    // store instruction writes 4 KiB of whole lines.
+    const __amdgpu_buffer_rsrc_t r = buffer_rsrc(pacc + slot * kQHeads * kHeadDim, kQHeads * kHeadDim * 4);
+    store_coherent_x4(r, (uint32_t)tid * 16u, u32x4_t{__float_as_uint(o[0]), __float_as_uint(o[1]),
+                                                      __float_as_uint(o[2]), __float_as_uint(o[3])});
+    store_coherent_x4(r, (uint32_t)(kBlock + tid) * 16u, u32x4_t{__float_as_uint(o[4]), __float_as_uint(o[5]),
+                                                                 __float_as_uint(o[6]), __float_as_uint(o[7])});
   }
   wait_vmem();
   __syncthreads();
@@ -370,9 +375,9 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
       const size_t sl = (size_t)min(s0 + y, n_splits - 1);
       mv[y] = load_coherent(pm + sl * kQHeads + hd);
       lv[y] = load_coherent(pl + sl * kQHeads + hd);
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + (sl * kQHeads + hd) * kHeadDim + d0);
-      av[y][0] = src[0];
-      av[y][1] = src[1];
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + sl * kQHeads * kHeadDim);
+      av[y][0] = src[tid];
+      av[y][1] = src[kBlock + tid];
     }
     float Mb = M;
 #pragma unroll

@@ -128,6 +128,18 @@ __device__ __forceinline__ void store_coherent(float* p, float v) {
   __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16 bytes per lane written with the same agent-scope coherence (the sc1
+// policy), through a raw buffer resource over [base, base + bytes) whose
+// out-of-range offsets the hardware drops.  For hand-offs of whole blocks:
+// with lane-contiguous offsets a wave writes full 64-B lines.
+constexpr int kBufferFormatWord = 0x00020000;  // dword 3 of a raw gfx9 buffer resource
+constexpr int kPolicyAgentCoherent = 16;       // the sc1 bit of the cache-policy operand
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferFormatWord);
+}
+__device__ __forceinline__ void store_coherent_x4(__amdgpu_buffer_rsrc_t r, uint32_t offset, u32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)offset, 0, kPolicyAgentCoherent);
+}
 // Wait until this thread's outstanding vector memory operations (loads,
 // stores, atomics) have completed; also a compiler memory barrier.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

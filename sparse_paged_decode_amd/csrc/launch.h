@@ -30,6 +30,8 @@ enum KernelId {
   kKStepFp8,
   kKDequantFp8Bf16,
   kKTopkMerge,
+  kKReadStream,
+  kKReadGather,
   kNumKernels
 };
 // When timing is on, takes the next pair of timing events for kernel `id`
@@ -60,6 +62,11 @@ int launch_dequant_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hi
 // [G, N, k_in] (positions, -1 = empty; fp32 scores) -> [N, k_out].
 int launch_topk_merge(const int32_t* cand_idx, const float* cand_scores, int G, int N, int k_in, int k_out,
                       int32_t* out_idx, float* out_scores, hipStream_t stream);
+// Read-bandwidth references (bench_read.hip): mode 0 streams the bytes of
+// n_pages pages, mode 1 gathers the pages page_ids[0..n_pages) with the
+// index scan's lane pattern; grid workgroups, one word each to sink.
+int launch_read_reference(const uint8_t* pages, const int32_t* page_ids, int64_t n_pages, int mode, int grid,
+                          uint32_t* sink, hipStream_t stream);
 // fp8 pages [n_pages, 16384] -> bf16 [n_pages, 128, 128] through the step kernel's conversion.
 int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
 // Cache insert: caches c = 0 (K), 1 (V), 2 (index key) with row_heads[c]

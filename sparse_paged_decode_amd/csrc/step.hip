@@ -654,13 +654,13 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       const uint32_t slot = all ? (uint32_t)j : base + o;
       ++o;
       if (slot < (uint32_t)k) {
-        store_coherent(reinterpret_cast<uint32_t*>(out + slot), (uint32_t)j);
+        out[slot] = j;  // read by no item of this launch: plain stores, written back at its end
       } else {
         raise_error(err, kErrSelection);
       }
     }
     if (all && c == 0)
-      for (int x = L + tid; x < k; x += kBlock) store_coherent(reinterpret_cast<uint32_t*>(out + x), 0xffffffffu);
+      for (int x = L + tid; x < k; x += kBlock) out[x] = -1;
   }
   if (done_prev == (uint32_t)(nch - 1)) {
     // Every chunk of the request has passed its barriers and read the rows.
