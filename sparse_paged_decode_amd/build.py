@@ -23,6 +23,11 @@ HIPCC_FLAGS = [
     "-std=c++17",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    # Atomics keep their results where the source uses them: the atomic
+    # optimizer would broadcast each result at once (a wait for the atomic
+    # right after it is issued), even when the result is needed only later.
+    "-mllvm",
+    "-amdgpu-atomic-optimizer-strategy=None",
     # No packed-fp32 instructions in generated code.
     "-Xclang",
     "-target-feature",
