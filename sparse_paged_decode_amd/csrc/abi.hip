@@ -13,26 +13,6 @@
 namespace mono {
 
 namespace {
-thread_local char g_error[512] = "";
-
-inline void clear_error() { g_error[0] = '\0'; }
-
-inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-constexpr int kMaxBtStride = 1 << 20;  // 2^27 tokens per request
-constexpr int kMaxHeads = 64;
-constexpr int kMergeMaxCandidates = 8192;  // 64 KiB of LDS keys per workgroup
-}  // namespace
-
-int set_error(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_error, sizeof(g_error), fmt, ap);
-  va_end(ap);
-  return code;
-}
-
-namespace {
 // Optional per-kernel timing: pairs of HIP events recorded around launches.
 struct Profiler {
   std::mutex mu;
@@ -69,51 +49,16 @@ int check_launch(const char* what) {
 
 namespace {
 
-int check_step_shape(int B, int T, int bt_stride, int k, bool need_k) {
-  if (B < 1) return set_error(MONO_EINVAL, "B must be >= 1 (got %d)", B);
-  if (T < 1) return set_error(MONO_EINVAL, "T must be >= 1 (got %d)", T);
-  if ((long long)B * T > (1LL << 30)) return set_error(MONO_EINVAL, "B*T too large (%d x %d)", B, T);
-  if (bt_stride < 1 || bt_stride > kMaxBtStride)
-    return set_error(MONO_EINVAL, "bt_stride must be in [1, %d] (got %d)", kMaxBtStride, bt_stride);
-  if (need_k && k < 1) return set_error(MONO_EINVAL, "k must be >= 1 (got %d)", k);
-  if (need_k && k > bt_stride * MONO_PAGE_TOKENS)
-    return set_error(MONO_EINVAL, "k (%d) exceeds the block table's capacity (%d tokens)", k,
-                     bt_stride * MONO_PAGE_TOKENS);
-  return MONO_OK;
-}
-
-int check_pages_args(const void* a, const void* b, const void* c, int64_t n_pages, const char* what) {
-  if (n_pages < 0) return set_error(MONO_EINVAL, "%s: n_pages < 0", what);
-  if (n_pages > (int64_t)1 << 34) return set_error(MONO_EINVAL, "%s: n_pages too large", what);
-  if (n_pages > 0 && (!a || !b || !c))
-    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
-  return MONO_OK;
-}
-
-// fp8 tensor scales must be finite and positive.
-bool bad_tensor_scale(float x) { return !(x > 0.f) || x == __builtin_inff(); }
-
-// The step calls, for either cache format (MXFP4 or fp8).
 int index_topk_impl(int fmt, const char* what, const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
                     int64_t num_pages, const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev,
                     int B, int T, int k, int32_t* selected_idx_dev, float* selected_scores_dev, void* ws_dev,
                     size_t ws_bytes, void* stream, int page_lo = 0, int page_hi = -1) {
   clear_error();
-  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
-  if (page_hi < 0) page_hi = bt_stride;
-  if (page_lo < 0 || page_lo >= page_hi || page_hi > bt_stride)
-    return set_error(MONO_EINVAL, "%s: page window [%d, %d) not inside [0, %d)", what, page_lo, page_hi, bt_stride);
-  if (!index_q_dev || !index_pages_dev || !block_table_dev || !seq_lens_dev || !selected_idx_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
-  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
-  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(ws_dev, 256) ||
-      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4) ||
-      !aligned(selected_scores_dev, 4))
-    return set_error(MONO_EINVAL, "%s: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment", what);
-  StepLayout lay = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1);
-  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
-  lay.win_lo = page_lo;
-  lay.win_hi = page_hi;
+  StepLayout lay;
+  if (int rc = check_index_call(what, index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride,
+                                seq_lens_dev, B, T, k, selected_idx_dev, selected_scores_dev, ws_dev, ws_bytes,
+                                page_lo, page_hi, &lay))
+    return rc;
   StepArgs a{};
   a.fmt = fmt;
   a.index_q = index_q_dev;
@@ -134,23 +79,11 @@ int pa_decode_impl(int fmt, const char* what, const uint16_t* q_dev, const uint8
                    float scale, float k_scale, float v_scale, uint16_t* out_dev, void* ws_dev, size_t ws_bytes,
                    void* stream) {
   clear_error();
-  const bool sparse = selected_idx_dev != nullptr;
-  if (int rc = check_step_shape(B, T, bt_stride, k, sparse)) return rc;
-  if (kv_heads < 1 || kv_heads > kMaxHeads)
-    return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
-  if (!q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev || !seq_lens_dev || !out_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
-  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return set_error(MONO_EINVAL, "%s: scale must be finite", what);
-  if (bad_tensor_scale(k_scale) || bad_tensor_scale(v_scale))
-    return set_error(MONO_EINVAL, "%s: k_scale and v_scale must be finite and > 0", what);
-  if (!aligned(q_dev, 16) || !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) ||
-      !aligned(ws_dev, 256) || !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) ||
-      !aligned(selected_idx_dev, 4))
-    return set_error(MONO_EINVAL, "%s: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment", what);
-  const StepLayout lay = step_layout(kModeAttn, B, T, kv_heads, bt_stride, sparse ? k : 0, sparse);
-  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  StepLayout lay;
+  if (int rc = check_pa_call(what, q_dev, k_pages_dev, v_pages_dev, num_pages, kv_heads, block_table_dev, bt_stride,
+                             seq_lens_dev, B, T, selected_idx_dev, k, scale, k_scale, v_scale, out_dev, ws_dev,
+                             ws_bytes, &lay))
+    return rc;
   StepArgs a{};
   a.fmt = fmt;
   a.k_scale = k_scale;
@@ -175,23 +108,11 @@ int sparse_decode_impl(int fmt, const char* what, const uint16_t* index_q_dev, c
                        const int32_t* seq_lens_dev, int B, int T, int k, float scale, float k_scale, float v_scale,
                        int32_t* selected_idx_dev, uint16_t* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
   clear_error();
-  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
-  if (kv_heads < 1 || kv_heads > kMaxHeads)
-    return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
-  if (!index_q_dev || !index_pages_dev || !q_dev || !k_pages_dev || !v_pages_dev || !block_table_dev ||
-      !seq_lens_dev || !selected_idx_dev || !out_dev || !ws_dev)
-    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
-  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
-  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
-    return set_error(MONO_EINVAL, "%s: scale must be finite", what);
-  if (bad_tensor_scale(k_scale) || bad_tensor_scale(v_scale))
-    return set_error(MONO_EINVAL, "%s: k_scale and v_scale must be finite and > 0", what);
-  if (!aligned(index_q_dev, 16) || !aligned(index_pages_dev, 16) || !aligned(q_dev, 16) ||
-      !aligned(k_pages_dev, 16) || !aligned(v_pages_dev, 16) || !aligned(out_dev, 16) || !aligned(ws_dev, 256) ||
-      !aligned(block_table_dev, 4) || !aligned(seq_lens_dev, 4) || !aligned(selected_idx_dev, 4))
-    return set_error(MONO_EINVAL, "%s: q/pages/out need 16-byte, ws 256-byte, tables 4-byte alignment", what);
-  const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
-  if (ws_bytes < lay.total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay.total);
+  StepLayout lay;
+  if (int rc = check_sparse_call(what, index_q_dev, index_pages_dev, q_dev, k_pages_dev, v_pages_dev, num_pages,
+                                 kv_heads, block_table_dev, bt_stride, seq_lens_dev, B, T, k, scale, k_scale, v_scale,
+                                 selected_idx_dev, out_dev, ws_dev, ws_bytes, &lay))
+    return rc;
   StepArgs a{};
   a.fmt = fmt;
   a.k_scale = k_scale;
@@ -221,43 +142,35 @@ extern "C" {
 
 int mono_abi_version(void) { return MONO_ABI_VERSION; }
 
-const char* mono_last_error(void) { return g_error; }
+const char* mono_last_error(void) { return last_error(); }
 
 int mxfp4_pages_pack(const uint8_t* codes_dev, const uint8_t* scales_dev, uint8_t* pages_dev,
                      int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_pages_args(codes_dev, scales_dev, pages_dev, n_pages, "mxfp4_pages_pack")) return rc;
+  if (int rc = check_pages_args(codes_dev, scales_dev, pages_dev, n_pages, 16, 4, 16, "mxfp4_pages_pack")) return rc;
   if (n_pages == 0) return MONO_OK;
-  if (!aligned(codes_dev, 16) || !aligned(pages_dev, 16) || !aligned(scales_dev, 4))
-    return set_error(MONO_EINVAL, "mxfp4_pages_pack: codes/pages need 16-byte and scales 4-byte alignment");
   return launch_pack(codes_dev, scales_dev, pages_dev, n_pages, (hipStream_t)stream);
 }
 
 int mxfp4_pages_unpack(const uint8_t* pages_dev, uint8_t* codes_dev, uint8_t* scales_dev,
                        int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_pages_args(pages_dev, codes_dev, scales_dev, n_pages, "mxfp4_pages_unpack")) return rc;
+  if (int rc = check_pages_args(pages_dev, codes_dev, scales_dev, n_pages, 16, 16, 4, "mxfp4_pages_unpack")) return rc;
   if (n_pages == 0) return MONO_OK;
-  if (!aligned(codes_dev, 16) || !aligned(pages_dev, 16) || !aligned(scales_dev, 4))
-    return set_error(MONO_EINVAL, "mxfp4_pages_unpack: codes/pages need 16-byte and scales 4-byte alignment");
   return launch_unpack(pages_dev, codes_dev, scales_dev, n_pages, (hipStream_t)stream);
 }
 
 int mxfp4_pages_dequant(const uint8_t* pages_dev, float* out_dev, int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "mxfp4_pages_dequant")) return rc;
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, 16, 16, 16, "mxfp4_pages_dequant")) return rc;
   if (n_pages == 0) return MONO_OK;
-  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
-    return set_error(MONO_EINVAL, "mxfp4_pages_dequant: pages and out need 16-byte alignment");
   return launch_dequant_f32(pages_dev, out_dev, n_pages, (hipStream_t)stream);
 }
 
 int mxfp4_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "mxfp4_pages_dequant_bf16")) return rc;
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, 16, 16, 16, "mxfp4_pages_dequant_bf16")) return rc;
   if (n_pages == 0) return MONO_OK;
-  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
-    return set_error(MONO_EINVAL, "mxfp4_pages_dequant_bf16: pages and out need 16-byte alignment");
   return launch_dequant_bf16(pages_dev, out_dev, n_pages, (hipStream_t)stream);
 }
 
@@ -287,16 +200,9 @@ int mono_index_score_topk_window(const uint16_t* index_q_dev, const uint8_t* ind
 int mono_topk_merge(const int32_t* cand_idx_dev, const float* cand_scores_dev, int G, int64_t N, int k_in, int k_out,
                     int32_t* out_idx_dev, float* out_scores_dev, void* stream) {
   clear_error();
-  if (G < 1 || k_in < 1 || k_out < 1 || N < 0 || N > 0x7fffffff)
-    return set_error(MONO_EINVAL, "mono_topk_merge: need G, k_in, k_out >= 1 and 0 <= N < 2^31");
-  if ((int64_t)G * k_in > kMergeMaxCandidates)
-    return set_error(MONO_ENOTSUP, "mono_topk_merge: G * k_in = %lld exceeds %d candidates", (long long)G * k_in,
-                     kMergeMaxCandidates);
+  if (int rc = check_merge_call(cand_idx_dev, cand_scores_dev, G, N, k_in, k_out, out_idx_dev, out_scores_dev))
+    return rc;
   if (N == 0) return MONO_OK;
-  if (!cand_idx_dev || !cand_scores_dev || !out_idx_dev) return set_error(MONO_EINVAL, "mono_topk_merge: NULL buffer");
-  if (!aligned(cand_idx_dev, 4) || !aligned(cand_scores_dev, 4) || !aligned(out_idx_dev, 4) ||
-      !aligned(out_scores_dev, 4))
-    return set_error(MONO_EINVAL, "mono_topk_merge: buffers need 4-byte alignment");
   return launch_topk_merge(cand_idx_dev, cand_scores_dev, G, (int)N, k_in, k_out, out_idx_dev, out_scores_dev,
                            (hipStream_t)stream);
 }
@@ -362,7 +268,7 @@ int mono_sparse_decode_mxfp4_noalloc(const uint16_t* index_q_dev, const uint8_t*
   if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
   if (kv_heads < 1 || kv_heads > kMaxHeads)
     return set_error(MONO_ENOTSUP, "%s: kv_heads must be in [1, %d] (got %d)", what, kMaxHeads, kv_heads);
-  if (err_dev && !aligned(err_dev, 4)) return set_error(MONO_EINVAL, "%s: err needs 4-byte alignment", what);
+  if ((uintptr_t)err_dev % 4) return set_error(MONO_EINVAL, "%s: err needs 4-byte alignment", what);
   const StepLayout lay = step_layout(kModeFused, B, T, kv_heads, bt_stride, k, 1);
   if (lay.total > kNoAllocScratchBytes)
     return set_error(MONO_ENOSPC, "%s: this shape needs %zu B of scratch; the static scratch holds %zu B", what,
@@ -388,10 +294,8 @@ int mono_sparse_decode_fp8(const uint16_t* index_q_dev, const uint8_t* index_pag
 
 int fp8_pages_dequant_bf16(const uint8_t* pages_dev, uint16_t* out_dev, int64_t n_pages, void* stream) {
   clear_error();
-  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, "fp8_pages_dequant_bf16")) return rc;
+  if (int rc = check_pages_args(pages_dev, out_dev, out_dev, n_pages, 16, 16, 16, "fp8_pages_dequant_bf16")) return rc;
   if (n_pages == 0) return MONO_OK;
-  if (!aligned(pages_dev, 16) || !aligned(out_dev, 16))
-    return set_error(MONO_EINVAL, "fp8_pages_dequant_bf16: pages and out need 16-byte alignment");
   return launch_dequant_fp8_bf16(pages_dev, out_dev, n_pages, (hipStream_t)stream);
 }
 
@@ -399,25 +303,11 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev, co
                       const int64_t* slots_dev, int64_t n, int kv_heads, uint8_t* k_pages_dev, uint8_t* v_pages_dev,
                       uint8_t* index_pages_dev, int64_t num_pages, uint32_t* err_dev, void* stream) {
   clear_error();
-  if (n < 0) return set_error(MONO_EINVAL, "mono_insert_mxfp4: n < 0");
-  if (num_pages < 1 || num_pages > ((int64_t)1 << 34))
-    return set_error(MONO_EINVAL, "mono_insert_mxfp4: num_pages out of range");
-  if ((k_rows_dev == nullptr) != (k_pages_dev == nullptr) || (v_rows_dev == nullptr) != (v_pages_dev == nullptr) ||
-      (index_rows_dev == nullptr) != (index_pages_dev == nullptr))
-    return set_error(MONO_EINVAL, "mono_insert_mxfp4: rows and pages of a cache must be both given or both NULL");
-  const bool kv = k_rows_dev || v_rows_dev;
-  if (kv && (kv_heads < 1 || kv_heads > kMaxHeads))
-    return set_error(MONO_ENOTSUP, "mono_insert_mxfp4: kv_heads must be in [1, %d] (got %d)", kMaxHeads, kv_heads);
-  if (!slots_dev || !err_dev) return set_error(MONO_EINVAL, "mono_insert_mxfp4: NULL slots or err");
-  const void* bufs16[6] = {k_rows_dev, v_rows_dev, index_rows_dev, k_pages_dev, v_pages_dev, index_pages_dev};
-  for (const void* b : bufs16)
-    if (b && !aligned(b, 16)) return set_error(MONO_EINVAL, "mono_insert_mxfp4: rows and pages need 16-byte alignment");
-  if (!aligned(slots_dev, 8) || !aligned(err_dev, 4))
-    return set_error(MONO_EINVAL, "mono_insert_mxfp4: slots need 8-byte and err 4-byte alignment");
+  if (int rc = check_insert_call(k_rows_dev, v_rows_dev, index_rows_dev, slots_dev, n, kv_heads, k_pages_dev,
+                                 v_pages_dev, index_pages_dev, num_pages, err_dev))
+    return rc;
   const int row_heads[3] = {k_rows_dev ? kv_heads : 0, v_rows_dev ? kv_heads : 0, index_rows_dev ? 1 : 0};
   const int64_t rows_per_token = row_heads[0] + row_heads[1] + row_heads[2];
-  if (n * rows_per_token * 4 >= ((int64_t)1 << 31))
-    return set_error(MONO_EINVAL, "mono_insert_mxfp4: n x rows per token too large");
   if (n == 0 || rows_per_token == 0) return MONO_OK;
   const uint16_t* const rows[3] = {k_rows_dev, v_rows_dev, index_rows_dev};
   uint8_t* const pools[3] = {k_pages_dev, v_pages_dev, index_pages_dev};
@@ -427,13 +317,7 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev, co
 int mono_bench_read(const uint8_t* pages_dev, const int32_t* page_ids_dev, int64_t n_pages, int mode, int grid,
                     uint32_t* sink_dev, void* stream) {
   clear_error();
-  if (mode != 0 && mode != 1) return set_error(MONO_EINVAL, "mono_bench_read: mode must be 0 or 1 (got %d)", mode);
-  if (n_pages < 1 || n_pages > ((int64_t)1 << 30)) return set_error(MONO_EINVAL, "mono_bench_read: n_pages out of range");
-  if (grid < 1 || grid > (1 << 16)) return set_error(MONO_EINVAL, "mono_bench_read: grid must be in [1, 65536]");
-  if (!pages_dev || !sink_dev || (mode == 1 && !page_ids_dev))
-    return set_error(MONO_EINVAL, "mono_bench_read: NULL buffer");
-  if (!aligned(pages_dev, 16) || !aligned(sink_dev, 4) || !aligned(page_ids_dev, 4))
-    return set_error(MONO_EINVAL, "mono_bench_read: pages need 16-byte, ids and sink 4-byte alignment");
+  if (int rc = check_bench_read_call(pages_dev, page_ids_dev, n_pages, mode, grid, sink_dev)) return rc;
   return launch_read_reference(pages_dev, page_ids_dev, n_pages, mode, grid, sink_dev, (hipStream_t)stream);
 }
 

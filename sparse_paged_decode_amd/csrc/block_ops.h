@@ -7,8 +7,6 @@
 
 namespace mono {
 
-constexpr int kBlock = 256;
-constexpr int kWaves = kBlock / 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

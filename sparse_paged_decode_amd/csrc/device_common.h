@@ -9,15 +9,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "plan.h"
+
 namespace mono {
 
-constexpr int kPageTokens = 128;
-constexpr int kHeadDim = 128;
 constexpr int kRowBytes = 64;        // packed e2m1 bytes per row
 constexpr int kScaleBlock = 32;      // elements per e8m0 scale
 constexpr int kScaleOffset = 8192;   // 128 rows x 64 B
 constexpr int kPageBytes = 8704;     // + 128 rows x 4 B
-constexpr int kQHeads = 16;          // query heads per KV head
 
 // Workspace error word bits (mirrors MONO_DEVERR_* of the public header).
 constexpr uint32_t kErrPageId = 1u;

@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #include "mono_decode.h"
+#include "plan.h"
 
 namespace mono {
 
@@ -49,8 +50,6 @@ bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop);
     else                                                                                     \
       hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                   \
   } while (0)
-// Records a formatted error message; returns `code`.
-int set_error(int code, const char* fmt, ...);
 
 int launch_pack(const uint8_t* codes, const uint8_t* scales, uint8_t* pages, int64_t n_pages,
                 hipStream_t stream);
@@ -75,48 +74,7 @@ int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages
 int launch_insert(const uint16_t* const rows[3], uint8_t* const pools[3], const int row_heads[3],
                   const int64_t* slots, int64_t n, int64_t num_pages, uint32_t* err, hipStream_t stream);
 
-// ---- the persistent step kernel (step.hip) -----------------------------------
-enum StepMode { kModeIndex = 1, kModeAttn = 2, kModeFused = 3 };
-// Header words of the control block (the same offset in every layout).
-constexpr uint32_t kHdrTicket = 0;   // next work-item ticket
-constexpr uint32_t kHdrExits = 1;    // workgroups that have left
-constexpr uint32_t kHdrCleared = 2;  // clear items done
-constexpr uint32_t kHdrZeroed = 3;   // zero region the last call left clean, in 256-B units
-constexpr uint32_t kHdrWords = 4;
-// Work-item descriptors: kind in the top bits, index below.
-constexpr uint32_t kItemScan = 1, kItemFilter = 2, kItemAttn = 3, kItemSelect = 4;
-constexpr uint32_t kKindShift = 28;
-constexpr uint32_t kIndexMask = (1u << kKindShift) - 1u;
-
-struct StepLayout {
-  int mode, B, T, H, k, sparse;
-  int q_groups;      // ceil(T / 4) query-token groups per request
-  int chunk_pages;   // index pages per scan chunk
-  int chunks;        // scan chunks per query group (window pages / chunk_pages, rounded up)
-  int win_lo, win_hi;  // page window [win_lo, win_hi) of every request the index items score
-  int lcap;          // bt_stride * 128: capacity of a score row
-  int slices;        // filter slices per query token (lcap / 4096, rounded up)
-  int split_tokens;  // attention candidates per split
-  int n_splits;      // attention splits per (query token, KV head)
-  int select_mode;   // 1: one workgroup selects each query token's top k
-  int local;         // 1: chunk-local step (one query token per request; see step.hip)
-  int part_splits;   // splits the partial buffers hold per (query token, KV head)
-  uint32_t n_clear, n_scan, n_select, n_filter, n_attn;  // work items of each kind (clear: when needed)
-  uint32_t n_ready0;    // items ready at the start (the first tickets after the clear items)
-  uint32_t ready_kind;  // their kind
-  uint32_t n_queue;     // items published into the ready queue while the kernel runs
-  size_t zero_end;      // [ctrl_base + header, zero_end) must be zero when items start
-  uint64_t zero_units;  // zero_end / 256
-  // control block (u32 words from ctrl_base): word offsets
-  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, lvl_cnt, pub, queue, ctrl_words;
-  // byte offsets in the workspace (hist2, hist3, ties, xcand, xcnt: chunk-local step only)
-  size_t err, ctrl_base, hist, hist2, hist3, ties, scores, xcand, xcnt, cand, pm, pl, pacc, total;
-};
-StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
-
-// Cache page formats (page_format.h).
-enum CacheFormat { kFmtMxfp4 = 0, kFmtFp8 = 1 };
-
+// ---- the persistent step kernel (step.hip); its layout is in plan.h -----------
 struct StepArgs {
   int fmt = kFmtMxfp4;  // CacheFormat of the index, K and V pools
   float k_scale = 1.f;  // fp8 K tensor scale (1 for MXFP4)

@@ -35,112 +35,6 @@
 namespace mono {
 
 constexpr uint32_t kMaxSpins = 1u << 21;  // bound of one wait (seconds, far above any step)
-constexpr size_t kClearBytes = 32768;     // bytes zeroed by one clear item
-constexpr int kMinSplitTokens = 256;      // attention candidates per split: one pass of 4 waves x 4 groups of 16
-constexpr int kMaxSplitTokens = 8192;
-// Chunk-local step: scores a scan item keeps in LDS (32 pages), and chunks
-// per request (its attention splits).
-constexpr int kLocalTokens = 4096;
-constexpr int kLocalMaxChunks = 16;
-constexpr int kLvlWords = 5;  // per query token: arrivals of the four levels, then the finished count
-constexpr int kExchCap = 2048;  // threshold-bin tokens a request's chunks exchange (more: radix levels)
-
-StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse) {
-  StepLayout l{};
-  l.mode = mode;
-  l.B = B;
-  l.T = T;
-  l.H = H;
-  l.k = k;
-  l.sparse = sparse;
-  const size_t N = (size_t)B * T;
-  l.q_groups = (T + 3) / 4;
-  l.chunk_pages = kScanChunkPages;  // launch_step re-balances this to the resident workgroups
-  l.chunks = (bt_stride + l.chunk_pages - 1) / l.chunk_pages;
-  l.lcap = bt_stride * kPageTokens;
-  l.win_lo = 0;  // the index call over a page window narrows these
-  l.win_hi = bt_stride;
-  l.slices = (l.lcap + kSlice - 1) / kSlice;
-  const bool index = (mode & kModeIndex) != 0, attn = (mode & kModeAttn) != 0;
-  // Attention splits: 256 candidates per workgroup unless that makes more
-  // than 4096 items (launch_step may enlarge them; the partial buffers are
-  // sized for this count).
-  const long list_max = sparse ? (long)k : (long)l.lcap;
-  const size_t NH = N * H;
-  int split = kMinSplitTokens;
-  while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > 4096) split *= 2;
-  l.split_tokens = split;
-  l.n_splits = (int)((list_max + split - 1) / split);
-
-  // Selection by slices and a resolve; launch_step may switch to one
-  // workgroup per query token instead (the queue is sized for slices, the
-  // larger of the two).
-  l.select_mode = 0;
-  l.local = 0;  // launch_step decides
-  // The one-launch step with one query token per request may run chunk-local
-  // (launch_step decides); it needs room for up to kLocalMaxChunks splits.
-  const bool local_ok = mode == kModeFused && T == 1;
-  l.n_scan = index ? (uint32_t)(B * l.q_groups * l.chunks) : 0u;
-  l.n_select = 0u;
-  l.n_filter = index ? (uint32_t)(N * l.slices) : 0u;
-  l.n_attn = attn ? (uint32_t)(NH * l.n_splits) : 0u;
-  // Items ready at the start take the first tickets; the rest are published.
-  l.n_ready0 = index ? l.n_scan : l.n_attn;
-  l.ready_kind = index ? kItemScan : kItemAttn;
-  l.n_queue = index ? l.n_select + l.n_filter + l.n_attn : 0u;
-
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return o;
-  };
-  l.err = take(256);
-  // Control block: u32 words zeroed by the last workgroup of every call.
-  // Its 4-word header sits at the same offset in every layout.
-  size_t w = 0;
-  l.ctrl = w;
-  w += kHdrWords;
-  l.scan_done = w;
-  w += index ? (size_t)B * l.q_groups : 0;
-  l.filter_cnt = w;
-  w += index ? N : 0;
-  l.out_cnt = w;
-  w += index ? N : 0;
-  l.cand_cnt = w;
-  w += index ? N : 0;
-  l.attn_cnt = w;
-  w += attn ? NH : 0;
-  l.lvl_cnt = w;
-  w += local_ok ? N * kLvlWords : 0;
-  l.pub = w;
-  w += 1;
-  l.queue = w;
-  w += l.n_queue;
-  l.ctrl_words = w;
-  l.ctrl_base = take(w * 4);
-  l.hist = take(index ? N * kHistBins * 4 : 0);
-  l.hist2 = take(local_ok ? N * kHistBins * 4 : 0);
-  l.hist3 = take(local_ok ? N * 1024 * 4 : 0);
-  l.ties = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
-  // Everything from the end of the header to here must be zero when the
-  // items start; the rest is scratch that each call overwrites.
-  l.zero_end = off;
-  l.zero_units = (uint64_t)(off >> 8);
-  const size_t zero_bytes = off - (l.ctrl_base + kHdrWords * 4);
-  l.n_clear = (uint32_t)((zero_bytes + kClearBytes - 1) / kClearBytes);
-  l.scores = take(index ? N * (size_t)l.lcap * 4 : 0);
-  l.xcand = take(local_ok ? N * kLocalMaxChunks * (size_t)kExchCap * 8 : 0);
-  l.xcnt = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
-  l.cand = take(index ? N * (size_t)kCandCap * 8 : 0);
-  l.part_splits = local_ok ? std::max(l.n_splits, kLocalMaxChunks) : l.n_splits;
-  const size_t S = (size_t)l.part_splits;
-  l.pm = take(attn ? NH * S * kQHeads * 4 : 0);
-  l.pl = take(attn ? NH * S * kQHeads * 4 : 0);
-  l.pacc = take(attn ? NH * S * kQHeads * kHeadDim * 4 : 0);
-  l.total = off;
-  return l;
-}
 
 namespace {
 
@@ -901,10 +795,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// Compute units of the current device (0 if unknown).
+int device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 0;
+  return cus;
+}
+
 // Workgroups that fit on the device at once (cached per device and kernel).
 int resident_workgroups(const void* kernel, int variant) {
   static std::mutex mu;
-  static int cache[64][6] = {};
+  static int cache[64][kStepVariants] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
   std::lock_guard<std::mutex> lock(mu);
@@ -921,97 +824,31 @@ int resident_workgroups(const void* kernel, int variant) {
 }  // namespace
 
 int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream, const char* what) {
-  const bool tq4 = lay_in.T > 1 && (lay_in.mode & kModeIndex);
   const bool f8 = a.fmt == kFmtFp8;
-  const void* const kernels[6] = {reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, false>),
-                                  reinterpret_cast<const void*>(&step_kernel<4, Mxfp4Format, false>),
-                                  reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, false>),
-                                  reinterpret_cast<const void*>(&step_kernel<4, Fp8Format, false>),
-                                  reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, true>),
-                                  reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, true>)};
-  int variant = (tq4 ? 1 : 0) + (f8 ? 2 : 0);
-  int cap = resident_workgroups(kernels[variant], variant);
+  const void* const kernels[kStepVariants] = {reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, false>),
+                                              reinterpret_cast<const void*>(&step_kernel<4, Mxfp4Format, false>),
+                                              reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, false>),
+                                              reinterpret_cast<const void*>(&step_kernel<4, Fp8Format, false>),
+                                              reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, true>),
+                                              reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, true>)};
+  DeviceShape dev{};
+  dev.cus = device_compute_units();
+  for (int v = 0; v < kStepVariants; ++v) dev.resident[v] = resident_workgroups(kernels[v], v);
   StepLayout lay = lay_in;
-  if (lay.mode & kModeIndex) {
-    // Scan chunks sized so the scan items make about one round of the
-    // resident workgroups (all of them start together and end together).
-    const int groups = lay.B * lay.q_groups;
-    const int span = lay.win_hi - lay.win_lo;  // pages of the window (the whole table by default)
-    const int per_group = std::max(1, cap / std::max(1, groups));
-    lay.chunk_pages = std::min(kMaxChunkPages, std::max(1, (span + per_group - 1) / per_group));
-    lay.chunks = (span + lay.chunk_pages - 1) / lay.chunk_pages;
-    lay.n_scan = (uint32_t)((size_t)groups * lay.chunks);
-    lay.n_ready0 = lay.n_scan;
-    // Rows of at most kSelectMax scores are selected by one workgroup each
-    // (inline in the last scan chunk when a request has one query token)
-    // once the slices would take more than two rounds of the resident
-    // workgroups; with fewer query tokens, slices spread each selection
-    // over more compute units and finish sooner.
-    const size_t N = (size_t)lay.B * lay.T;
-    if ((size_t)span * kPageTokens <= kSelectMax && N * (size_t)lay.slices > 2 * (size_t)cap) {
-      lay.select_mode = 1;
-      lay.n_filter = 0u;
-      lay.n_select = lay.T > 1 ? (uint32_t)N : 0u;
-      lay.n_queue = lay.n_select + lay.n_attn;
-    }
-  }
-  if (lay.mode & kModeAttn) {
-    // Attention splits as large as it takes to make about one round of the
-    // resident workgroups (never smaller than the layout's, whose partial
-    // buffers are sized for the most splits).
-    const size_t NH = (size_t)lay.B * lay.T * lay.H;
-    const long list_max = lay.sparse ? (long)lay.k : (long)lay.lcap;
-    int split = lay.split_tokens;
-    while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > (size_t)cap) split *= 2;
-    lay.split_tokens = split;
-    lay.n_splits = (int)((list_max + split - 1) / split);
-    lay.n_attn = (uint32_t)(NH * lay.n_splits);
-    if (!(lay.mode & kModeIndex)) lay.n_ready0 = lay.n_attn;
-    lay.n_queue = (lay.mode & kModeIndex) ? lay.n_select + lay.n_filter + lay.n_attn : 0u;
-  }
-  if (lay.mode == kModeFused && lay.T == 1 && lay.part_splits >= kLocalMaxChunks && a.sel_scores == nullptr &&
-      lay.win_lo == 0) {
-    // Chunk-local step: at most kLocalMaxChunks chunks of at most
-    // kLocalTokens scores per request, and every scan item a first ticket
-    // of a resident workgroup of its own kernel instance (the chunks of a
-    // request wait for each other).
-    const int lvariant = f8 ? 5 : 4;
-    const int lcap = resident_workgroups(kernels[lvariant], lvariant);
-    const int groups = lay.B;
-    const int span = lay.win_hi - lay.win_lo;
-    const int per_group = std::max(1, lcap / std::max(1, groups));
-    const int cp = std::max((span + per_group - 1) / per_group, (span + kLocalMaxChunks - 1) / kLocalMaxChunks);
-    const int ch = (span + cp - 1) / cp;
-    if (cp * kPageTokens <= kLocalTokens && ch <= kLocalMaxChunks && (size_t)groups * ch <= (size_t)lcap) {
-      variant = lvariant;
-      cap = lcap;
-      lay.local = 1;
-      lay.chunk_pages = cp;
-      lay.chunks = ch;
-      lay.n_scan = (uint32_t)(groups * ch);
-      lay.n_ready0 = lay.n_scan;
-      lay.select_mode = 0;
-      lay.n_select = lay.n_filter = lay.n_attn = 0u;
-      lay.n_queue = 0u;
-    }
-  }
-  const uint32_t n_items = lay.n_clear + lay.n_ready0 + lay.n_queue;
-  if (n_items == 0) return MONO_OK;
-  if ((uint64_t)lay.n_scan + lay.n_select + lay.n_filter + lay.n_attn > kIndexMask)
-    return set_error(MONO_ENOTSUP, "%s: too many work items", what);
-  if (lay.zero_units > 0xFFFFFFFFull || lay.ctrl_base != 256)
-    return set_error(MONO_ENOTSUP, "%s: workspace layout too large", what);
-  const unsigned grid = (unsigned)std::min<uint64_t>(n_items, (uint64_t)cap);
+  int variant = 0;
+  const long grid = plan_step(lay, dev, f8, a.sel_scores != nullptr, &variant, what);
+  if (grid <= 0) return (int)grid;  // 0: nothing to do; < 0: refused (message set)
   const int kid = lay.mode == kModeIndex ? (f8 ? kKIndexScanFp8 : kKIndexScan)
                   : lay.mode == kModeAttn  ? (f8 ? kKPaDecodeFp8 : kKPaDecode)
                                            : (f8 ? kKStepFp8 : kKStep);
+  const dim3 g((unsigned)grid);
   switch (variant) {
-    case 0: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 1: MONO_LAUNCH(kid, (step_kernel<4, Mxfp4Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 3: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format, false>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    case 4: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, true>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
-    default: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, true>), dim3(grid), dim3(kBlock), 0, stream, a, lay); break;
+    case 0: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 1: MONO_LAUNCH(kid, (step_kernel<4, Mxfp4Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 3: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 4: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, true>), g, dim3(kBlock), 0, stream, a, lay); break;
+    default: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, true>), g, dim3(kBlock), 0, stream, a, lay); break;
   }
   return check_launch(what);
 }

@@ -34,10 +34,6 @@
 
 namespace mono {
 
-constexpr int kScanChunkPages = 16;  // index pages per scan work item (default)
-constexpr int kMaxChunkPages = 64;   // one page id per lane of a wave
-constexpr int kHistBins = 2048;      // top 11 bits of the score key
-constexpr int kHistShift = 21;
 
 template <int TQ>
 struct ScanLds {
@@ -194,8 +190,6 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
 // candidate list.  resolve_query runs once all slices are done: it picks the
 // remaining tokens from the candidates with two more radix passes.
 // ---------------------------------------------------------------------------
-constexpr int kSlice = 4096;     // scores per filter work item
-constexpr int kCandCap = 8192;   // candidates kept per query token
 constexpr int kLdsCand = 3840;   // candidates the resolving workgroup stages in LDS
 
 struct FilterLds {
@@ -447,7 +441,6 @@ __device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& l
 // higher bins and collects bin B1's tokens in LDS, then the marked tokens
 // are written and pick_in_bin takes the rest.  Leaves the histogram row zero.
 // ---------------------------------------------------------------------------
-constexpr int kSelectMax = 65536;      // longest score row a single workgroup selects from
 constexpr int kSelPer = 16;            // scores per thread per batch
 constexpr int kSelBatch = kBlock * kSelPer;
 static_assert(kSelectMax / kSelBatch == kSelBatchesMax, "select batches");
