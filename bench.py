@@ -531,6 +531,12 @@ def main():
         torch.cuda.synchronize(dev)
         graph_ms = ge[0].elapsed_time(ge[1]) / K
 
+    # Device error bits raised by any of the steps above (a bounded wait
+    # that ran out, a bad page id or length): zero in a valid run.
+    torch.cuda.synchronize(dev)
+    device_errors = {name: int(spd.check_device_errors(wsx)) for name, wsx in
+                     (("step", run.ws), ("index", run.ws_topk), ("attention", run.ws_pa))}
+
     # Clocks while the step runs back to back (sampled from sysfs).
     info, pci_dir = device_info(torch, dev)
     clocks = None
@@ -611,6 +617,7 @@ def main():
             "kernel_us_mean": round(dom_us, 3),
             "source_digest": kernel_digest(dom),
         },
+        "device_errors": device_errors,
         "insert": ins,
         "cp_emulation": cp,
         "read_ceilings": ceilings,

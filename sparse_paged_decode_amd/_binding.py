@@ -276,6 +276,14 @@ class Workspace:
     def nbytes(self):
         return self.buf.numel()
 
+    def error_word(self):
+        """The workspace's device error word as a one-element int32 device
+        tensor (a view, no copy): the MONO_DEVERR_* bits the calls on this
+        workspace raised.  It can be read after any later synchronisation
+        (or copied out asynchronously); check_device_errors() reads and
+        clears it."""
+        return self.buf[:4].view(torch.int32)
+
 
 _default_ws = {}
 
