@@ -94,12 +94,14 @@ template <class Fmt>
 struct AttnGroup {
   typename Fmt::Chunk k;     // K chunk g (elements 32g..32g+31) of token m
   typename Fmt::Slice v[4];  // V elements 8m..8m+7 of tokens 4g..4g+3
-  uint32_t valid;            // token m is a candidate
+  uint32_t vm;               // bit r: token r of the group is a candidate (the same in every lane)
 };
 
 // Returns true in the workgroup that wrote the output (the only split, or
 // the last split to arrive, which merged the others).
-template <class Fmt, bool kLocal = false>
+// kGroups: groups of 16 tokens each wave fetches together in one pass (the
+// attention-only kernel instance takes 2 to fit in fewer registers).
+template <class Fmt, bool kLocal = false, int kGroups = kPassGroups>
 __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
@@ -126,9 +128,9 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     const bool in = grp < n_groups && entry < e1;
     return in ? ((kLocal || a.sel_row) ? raw : entry) : -1;
   };
-  int jv[kPassGroups];
+  int jv[kGroups];
 #pragma unroll
-  for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
+  for (int x = 0; x < kGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
   const int bt_len = (pos >> 7) + 1;
   const bool bt_lds = bt_len <= kBtCache;
   typedef __attribute__((address_space(3))) const int32_t lds_i32;
@@ -146,8 +148,10 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
   __syncthreads();
 
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
-  float m_run = -INFINITY, l_run = 0.f;
-  f32x4_t acc[8];
+  // m_run: running maximum of head m (every lane (g, m)); acc[x][i] and
+  // acc_l[i]: output dim 8m + x and softmax sum of head 4g + i.
+  float m_run = -INFINITY;
+  f32x4_t acc[8], acc_l = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int x = 0; x < 8; ++x) acc[x] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
@@ -178,14 +182,20 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     }
     return ((uint32_t)pid << 7) | (uint32_t)(j & (kPageTokens - 1));
   };
-  // Loads are unconditional (a non-candidate reads page 0, row 0) and their
-  // values are not touched here: a non-candidate's logits become -inf in
-  // qk_group (each logit depends on its own token's K row only) and its V
-  // values become zero in pv_group, so a NaN in such a row cannot leak.
+  // Loads are unconditional and their values are not touched here.  A
+  // non-candidate's K row is page 0, row 0: its logits become -inf in
+  // qk_group (each logit depends on its own token's K row only).  Its V row
+  // is that of the group's first candidate, so its V values are values the
+  // group's candidates hold anyway, and its weight is exactly zero; a group
+  // with no candidate skips P V (its V rows are page 0, row 0).  A NaN in a
+  // row that is not a candidate's therefore cannot reach the output.
   auto load_group = [&](uint32_t ref) -> AttnGroup<Fmt> {
     AttnGroup<Fmt> t;
-    t.valid = ref != ~0u;
-    const uint32_t r0 = t.valid ? ref : 0u;
+    const bool valid = ref != ~0u;
+    const uint64_t bal = __ballot(valid);
+    t.vm = (uint32_t)bal;  // lanes 0..15 hold tokens 0..15
+    const uint32_t fb = bal ? (uint32_t)__builtin_amdgcn_readlane((int)ref, (int)__builtin_ctzll(bal)) : 0u;
+    const uint32_t r0 = valid ? ref : 0u;
     {
       const uint8_t* page = kbase + (size_t)(r0 >> 7) * kv_stride;
       t.k = Fmt::load_chunk(page, Fmt::chunk_addr((int)(r0 & 127u), g));
@@ -193,7 +203,7 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t ri = __shfl(ref, 4 * g + i);
-      const uint32_t r1 = ri != ~0u ? ri : 0u;
+      const uint32_t r1 = ri != ~0u ? ri : fb;
       const uint8_t* page = vbase + (size_t)(r1 >> 7) * kv_stride;
       t.v[i] = Fmt::load_slice(page, r1 & 127u, m);
     }
@@ -204,25 +214,18 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Fmt::chunk_bf16(t.k, s), qb[s], c, 0, 0, 0);
-    // Validity of token r sits in bit r of this ballot (lanes 0..15).
-    const uint32_t vm = (uint32_t)__ballot(t.valid);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) c[i] = ((vm >> (4 * g + i)) & 1u) ? c[i] * sl2 : -INFINITY;
+    for (int i = 0; i < 4; ++i) c[i] = ((t.vm >> (4 * g + i)) & 1u) ? c[i] * sl2 : -INFINITY;
     return c;
   };
-  // acc += P V of a group; pa is the A operand (row n = head n, k-slot (g, i)
-  // = token 4g + i).
+  // acc += P V and acc_l += P 1 of a group; pa is the A operand (row n =
+  // head n, k-slot (g, i) = token 4g + i).
   auto pv_group = [&](const AttnGroup<Fmt>& t, s16x4_t pa) {
-    // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1);
-    // exact zeros for tokens that are not candidates.
-    const uint32_t vm = (uint32_t)__ballot(t.valid);
+    if (t.vm == 0u) return;  // no candidate: every weight is zero
+    // V of tokens 4g..4g+3, dims 8m..8m+7, as bf16 pairs (dims 8m+2p, 8m+2p+1).
     u32x4_t vv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const u32x4_t c = Fmt::slice_bf16(t.v[i]);
-      const bool ok = (vm >> (4 * g + i)) & 1u;
-      vv[i] = u32x4_t{ok ? c[0] : 0u, ok ? c[1] : 0u, ok ? c[2] : 0u, ok ? c[3] : 0u};
-    }
+    for (int i = 0; i < 4; ++i) vv[i] = Fmt::slice_bf16(t.v[i]);
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int p = x >> 1;
@@ -233,23 +236,26 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
       const s16x4_t vb = __builtin_bit_cast(s16x4_t, (uint64_t)b01 | ((uint64_t)b23 << 32));
       acc[x] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, acc[x], 0, 0, 0);
     }
+    // The softmax sums: P times a column of bf16 ones.
+    const s16x4_t ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
+    acc_l = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, acc_l, 0, 0, 0);
   };
 
-  // A pass covers kPassGroups groups of this wave: page lookups, the K/V
+  // A pass covers kGroups groups of this wave: page lookups, the K/V
   // loads of all of them at once, QK^T of all, one online-softmax update,
   // then P V of all.  The first pass's entries were requested at the start.
   auto passes = [&](auto long_table) {
-  for (int gb = wave; gb < n_groups; gb += kWaves * kPassGroups) {
-    AttnGroup<Fmt> grp[kPassGroups];
+  for (int gb = wave; gb < n_groups; gb += kWaves * kGroups) {
+    AttnGroup<Fmt> grp[kGroups];
 #pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) grp[x] = load_group(token_ref(token_of(gb + kWaves * x, jv[x]), long_table));
+    for (int x = 0; x < kGroups; ++x) grp[x] = load_group(token_ref(token_of(gb + kWaves * x, jv[x]), long_table));
     // The next pass's entries load while this pass computes.
 #pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) jv[x] = entry_load(gb + kWaves * kPassGroups + kWaves * x);
-    f32x4_t z[kPassGroups];
+    for (int x = 0; x < kGroups; ++x) jv[x] = entry_load(gb + kWaves * kGroups + kWaves * x);
+    f32x4_t z[kGroups];
     float mx = -INFINITY;
 #pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) {
+    for (int x = 0; x < kGroups; ++x) {
       z[x] = qk_group(grp[x]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, z[x][i]);
@@ -259,23 +265,25 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     const float m_new = fmaxf(m_run, mx);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    // Rescale only when some head's maximum grew past a finite one (a head
+    // whose maximum was -inf has had only zero weights so far).
+    if (__ballot(alpha != 1.f && m_run != -INFINITY)) {
+      // The accumulator rows are heads 4g..4g+3: their rescale factors sit
+      // in lanes 4g..4g+3.
+      f32x4_t al;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+      for (int x = 0; x < 8; ++x) acc[x] *= al;
+      acc_l *= al;
+    }
     m_run = m_new;
-    // The accumulator rows are heads 4g..4g+3: their rescale factors sit in
-    // lanes 4g..4g+3.
-    f32x4_t al;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) acc[x] *= al;
-    float psum = 0.f;
-#pragma unroll
-    for (int x = 0; x < kPassGroups; ++x) {
+    for (int x = 0; x < kGroups; ++x) {
       const uint32_t p01 = bf16x2_bits(__builtin_amdgcn_exp2f(z[x][0] - m_use), __builtin_amdgcn_exp2f(z[x][1] - m_use));
       const uint32_t p23 = bf16x2_bits(__builtin_amdgcn_exp2f(z[x][2] - m_use), __builtin_amdgcn_exp2f(z[x][3] - m_use));
-      psum += (bf16_lo_to_f32(p01) + bf16_hi_to_f32(p01)) + (bf16_lo_to_f32(p23) + bf16_hi_to_f32(p23));
       pv_group(grp[x], __builtin_bit_cast(s16x4_t, (uint64_t)p01 | ((uint64_t)p23 << 32)));
     }
-    l_run = l_run * alpha + psum;
   }
   };
   if (kLocal || bt_lds) {
@@ -286,8 +294,6 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
 
   // ---- combine the four waves -------------------------------------------
   __syncthreads();  // the block-table copy is no longer read
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
   float* so = reinterpret_cast<float*>(lds.combine);  // [wave][head][dim]
   float(*s_m)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes);
   float(*s_l)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes + kWaves * kQHeads * 4);
@@ -299,9 +305,10 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     *reinterpret_cast<f32x4_t*>(dst) = f32x4_t{acc[0][i], acc[1][i], acc[2][i], acc[3][i]};
     *reinterpret_cast<f32x4_t*>(dst + 4) = f32x4_t{acc[4][i], acc[5][i], acc[6][i], acc[7][i]};
   }
-  if (g == 0) {
-    s_m[wave][m] = m_run;
-    s_l[wave][m] = l_run;
+  if (g == 0) s_m[wave][m] = m_run;
+  if (m == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_l[wave][4 * g + i] = acc_l[i];
   }
   __syncthreads();
   const int hd = tid >> 4;         // query head within the group

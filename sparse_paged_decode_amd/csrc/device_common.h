@@ -30,17 +30,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// e8m0 byte -> the fp32 scale operand of the gfx950 scaled fp4 conversions.
-// Bytes 1..254 give the normal float 2^(e-127) (exponent field e, zero
-// mantissa).  Byte 0 gives the subnormal 2^-127 and byte 255 a quiet NaN, so
-// the operand carries the exact e8m0 value whether the instruction reads the
-// operand's value or only its exponent field.
-__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) {
-  uint32_t bits = e << 23;
-  bits = (e == 0u) ? 0x00400000u : bits;
-  bits = (e == 255u) ? 0x7fc00000u : bits;
-  return __uint_as_float(bits);
-}
+// e8m0 byte -> the fp32 scale operand of the gfx950 scaled fp4 conversions:
+// the byte in the operand's exponent field, zero mantissa.  The conversions
+// read only that field as the e8m0 scale, so bytes 0 (2^-127) and 255 (NaN)
+// need no special case (checked bit for bit on all 16 codes x 256 bytes).
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) { return __uint_as_float(e << 23); }
 
 // Eight e2m1 codes (one dword of packed row data: elements 8w..8w+7 when the
 // dword is the w-th of the row) -> eight bf16 values times the block scale,

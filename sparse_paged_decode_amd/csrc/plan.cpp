@@ -135,6 +135,7 @@ long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_s
                const char* what) {
   const bool tq4 = lay.T > 1 && (lay.mode & kModeIndex);
   *variant = step_variant(tq4, fp8);
+  if (lay.mode == kModeAttn && dev.resident[attn_variant(fp8)] > 0) *variant = attn_variant(fp8);
   int cap = std::max(1, dev.resident[*variant]);
   if (lay.mode & kModeIndex) {
     // Scan chunks sized so the scan items make about one round of the

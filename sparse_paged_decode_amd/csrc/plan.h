@@ -93,10 +93,12 @@ struct StepLayout {
 StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
 
 // Kernel instances of the step kernel: [1, 4 query tokens] x [MXFP4, fp8],
-// then the chunk-local instances [MXFP4, fp8].
-constexpr int kStepVariants = 6;
+// then the chunk-local instances [MXFP4, fp8], then the attention-only
+// instances [MXFP4, fp8] (the attention call's items alone).
+constexpr int kStepVariants = 8;
 inline int step_variant(bool tq4, bool fp8) { return (tq4 ? 1 : 0) + (fp8 ? 2 : 0); }
 inline int local_variant(bool fp8) { return fp8 ? 5 : 4; }
+inline int attn_variant(bool fp8) { return fp8 ? 7 : 6; }
 
 // What the device offers: compute units and, per kernel instance, how many
 // workgroups fit at once (occupancy x compute units).

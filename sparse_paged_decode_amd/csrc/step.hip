@@ -670,8 +670,8 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
     publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
 }
 
-template <int TQ, class Fmt>
-__device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& lay, uint32_t v, StepLds<TQ>& lds,
+template <class Fmt, int kGroups = kPassGroups>
+__device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& lay, uint32_t v, AttnLds& lds,
                                           uint32_t* ctrl, uint32_t* err) {
   const int H = lay.H, S = lay.n_splits;
   const int i = (int)(v / (uint32_t)(H * S));
@@ -711,16 +711,20 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
   aa.split_cnt = ctrl + lay.attn_cnt + qh;
   aa.err = err;
-  attn_split<Fmt>(aa, lds.attn);
+  attn_split<Fmt, false, kGroups>(aa, lds);
 }
 
-// kLocal: the chunk-local step's own instance, holding only the clear and
-// chunk-local items (a far smaller program than the instance with every
-// item kind, whose code does not fit the instruction cache).
-template <int TQ, class Fmt, bool kLocal>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
-  static_assert(!kLocal || TQ == 1, "the chunk-local step has one query token per request");
-  __shared__ std::conditional_t<kLocal, LocalLds, StepLds<TQ>> lds;
+// Item sets of the kernel instances: every kind; the chunk-local step's
+// clear and chunk-local items (a far smaller program than the instance with
+// every item kind, whose code does not fit the instruction cache); the
+// attention call's clear and attention items.
+enum : int { kSetAll = 0, kSetLocal = 1, kSetAttn = 2 };
+
+template <int TQ, class Fmt, int kSet>
+__device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& lay) {
+  constexpr bool kLocal = kSet == kSetLocal;
+  static_assert(kSet == kSetAll || TQ == 1, "the chunk-local and attention instances have one query token per group");
+  __shared__ std::conditional_t<kLocal, LocalLds, std::conditional_t<kSet == kSetAttn, AttnLds, StepLds<TQ>>> lds;
   __shared__ uint32_t s_item, s_flag, s_clear, s_rec, s_desc, s_pub;
   const int tid = thread_index();
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
@@ -760,6 +764,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
       if constexpr (kLocal) {
         if (kind == kItemScan) local_item<Fmt>(a, lay, idx, lds, ctrl, err);
+      } else if constexpr (kSet == kSetAttn) {
+        if (kind == kItemAttn) attn_item<Fmt>(a, lay, idx, lds, ctrl, err);
       } else if (kind == kItemScan) {
         scan_item<TQ, Fmt>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
       } else if (kind == kItemSelect) {
@@ -767,7 +773,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
       } else if (kind == kItemFilter) {
         filter_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
       } else if (kind == kItemAttn) {
-        attn_item<TQ, Fmt>(a, lay, idx, lds, ctrl, err);
+        attn_item<Fmt>(a, lay, idx, lds.attn, ctrl, err);
       }
     }
     __syncthreads();  // the next item reuses the LDS
@@ -793,6 +799,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void s
   if (s_flag) {
     for (size_t x = tid; x < lay.ctrl_words; x += kBlock) ctrl[x] = x == kHdrZeroed ? (uint32_t)lay.zero_units : 0u;
   }
+}
+
+template <int TQ, class Fmt, bool kLocal>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void step_kernel(StepArgs a, StepLayout lay) {
+  step_body<TQ, Fmt, kLocal ? kSetLocal : kSetAll>(a, lay);
+}
+
+template <class Fmt>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(StepArgs a, StepLayout lay) {
+  step_body<1, Fmt, kSetAttn>(a, lay);
 }
 
 // Compute units of the current device (0 if unknown).
@@ -830,7 +846,9 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
                                               reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, false>),
                                               reinterpret_cast<const void*>(&step_kernel<4, Fp8Format, false>),
                                               reinterpret_cast<const void*>(&step_kernel<1, Mxfp4Format, true>),
-                                              reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, true>)};
+                                              reinterpret_cast<const void*>(&step_kernel<1, Fp8Format, true>),
+                                              reinterpret_cast<const void*>(&attn_kernel<Mxfp4Format>),
+                                              reinterpret_cast<const void*>(&attn_kernel<Fp8Format>)};
   DeviceShape dev{};
   dev.cus = device_compute_units();
   for (int v = 0; v < kStepVariants; ++v) dev.resident[v] = resident_workgroups(kernels[v], v);
@@ -848,7 +866,9 @@ int launch_step(const StepArgs& a, const StepLayout& lay_in, hipStream_t stream,
     case 2: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
     case 3: MONO_LAUNCH(kid, (step_kernel<4, Fp8Format, false>), g, dim3(kBlock), 0, stream, a, lay); break;
     case 4: MONO_LAUNCH(kid, (step_kernel<1, Mxfp4Format, true>), g, dim3(kBlock), 0, stream, a, lay); break;
-    default: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, true>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 5: MONO_LAUNCH(kid, (step_kernel<1, Fp8Format, true>), g, dim3(kBlock), 0, stream, a, lay); break;
+    case 6: MONO_LAUNCH(kid, (attn_kernel<Mxfp4Format>), g, dim3(kBlock), 0, stream, a, lay); break;
+    default: MONO_LAUNCH(kid, (attn_kernel<Fp8Format>), g, dim3(kBlock), 0, stream, a, lay); break;
   }
   return check_launch(what);
 }

@@ -231,6 +231,8 @@ static void check_plan(int mode, int B, int T, int H, int bts, int k, bool fp8, 
     // every chunk item is a first-round item of a grid that fits at once
     CHECK((long)B * l.chunks == (long)l.n_scan && (long)l.n_scan <= grid && grid <= dev.resident[variant]);
     CHECK(l.n_queue == 0u);
+  } else if (mode == kModeAttn && dev.resident[attn_variant(fp8)] > 0) {
+    CHECK(variant == attn_variant(fp8));  // the attention call's own instance
   } else {
     CHECK(variant == step_variant(T > 1 && (mode & kModeIndex), fp8));
   }
@@ -284,6 +286,14 @@ static void check_plans() {
     int variant = -1;
     plan_step(l, mi, false, false, &variant, "long");
     CHECK(l.local == 0);
+  }
+  // Dense attention, batch 32 x 8192 tokens: the attention-only instance,
+  // one split of 512 tokens per resident workgroup.
+  {
+    StepLayout l = step_layout(kModeAttn, 32, 1, 1, 64, 0, 0);
+    int variant = -1;
+    const long grid = plan_step(l, mi, false, false, &variant, "w2");
+    CHECK(variant == attn_variant(false) && grid == 512 && l.split_tokens == 512 && l.n_splits == 16);
   }
   // Workload shapes and random shapes: plan invariants.
   check_plan(kModeAttn, 1, 1, 1, 2, 0, false, false, -1, -1, mi);
