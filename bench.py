@@ -323,15 +323,17 @@ def time_cp(spd, torch, dev, w, iq, ip, bt, sl, reps, heads=4):
         toks = np.clip(lens, lo * 128, hi * 128) - lo * 128
         win_bytes.append(int(toks.sum()) * ROW_BYTES["mxfp4"])
     shard_us = kt.mean_us["index_topk_kernel"]
+    merge_us = kt.mean_us["topk_merge_kernel"]
     return {
         "heads": heads,
         "shards": heads,
         "shard_kernel_us_mean": round(shard_us, 2),
-        "merge_kernel_us_mean": round(kt.mean_us["topk_merge_kernel"], 2),
-        "shard_index_bytes_one_rank": max(win_bytes),
-        "shard_index_bytes_read_here": heads * max(win_bytes),
-        "note": "each shard launch re-reads its window once per head (heads stacked as requests); a rank of the "
-                "context-parallel indexer would read it once for all heads",
+        "merge_kernel_us_mean": round(merge_us, 2),
+        "call_kernel_us": round(heads * shard_us + merge_us, 2),
+        "shard_index_bytes": max(win_bytes),
+        "shard_gbps": round(max(win_bytes) / shard_us / 1e3, 1),
+        "note": "one launch per shard scores its page window for every head (up to four (head, token) rows per "
+                "MFMA tile, so each window page is read once); the merge keeps each head's top-k",
     }
 
 

@@ -287,6 +287,31 @@ int mono_topk_merge(const int32_t* cand_idx_dev, const float* cand_scores_dev, i
                     int k_in, int k_out, int32_t* out_idx_dev, float* out_scores_dev,
                     void* stream);
 
+/* mono_indexer_cp_topk: the whole emulation in one call, with every head
+ * of a shard scored from one read of its window.
+ *
+ * index_q_dev        bf16 [heads, B*T, 128]: every rank's index-q head (row
+ *                    (h, b*T + t)); heads in [1, 64].
+ * index_pages_dev .. seq_lens_dev, B, T, k: as mono_index_score_topk.
+ * shards             G >= 1: shard r owns block-table columns
+ *                    [r*c, min(bt_stride, (r+1)*c)), c = ceil(bt_stride/G);
+ *                    shards whose window starts past the table are empty
+ *                    and skipped.  (non-empty shards) * k <= 8192, else
+ *                    MONO_ENOTSUP.
+ * selected_idx_dev   int32 [heads, B*T, k] out: each head's top-k positions
+ *                    (any order within a row, -1 padding), equal to the
+ *                    index call's selection for that head.
+ * ws_dev, ws_bytes   workspace of at least mono_indexer_cp_topk_workspace()
+ *                    (256-byte aligned): the index workspace, then the
+ *                    shards' candidate lists.
+ * Enqueues one index launch per non-empty shard, then the merge; errors as
+ * mono_index_score_topk. */
+size_t mono_indexer_cp_topk_workspace(int B, int T, int heads, int bt_stride, int k, int shards);
+int mono_indexer_cp_topk(const uint16_t* index_q_dev, const uint8_t* index_pages_dev,
+                         int64_t num_pages, const int32_t* block_table_dev, int bt_stride,
+                         const int32_t* seq_lens_dev, int B, int T, int heads, int k, int shards,
+                         int32_t* selected_idx_dev, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * The same step over fp8 caches (the older build's format: page
  * "vllm.models.minimax_m3.amd.mono.weights", SparseMoeLayer, names an fp8

@@ -59,6 +59,8 @@ EXPORTED_SYMBOLS = (
     "mono_index_score_topk_fp8",
     "mono_index_score_topk_window",
     "mono_topk_merge",
+    "mono_indexer_cp_topk_workspace",
+    "mono_indexer_cp_topk",
     "mono_pa_decode_fp8",
     "mono_sparse_decode_fp8",
     "fp8_pages_dequant_bf16",
@@ -111,6 +113,8 @@ def load_library(path=LIB_PATH):
         "mono_index_score_topk_fp8": (I, [P, P, I64, P, I, P, I, I, I, P, P, P, SZ, P]),
         "mono_index_score_topk_window": (I, [P, P, I64, P, I, P, I, I, I, I, I, P, P, P, SZ, P]),
         "mono_topk_merge": (I, [P, P, I, I64, I, I, P, P, P]),
+        "mono_indexer_cp_topk_workspace": (SZ, [I, I, I, I, I, I]),
+        "mono_indexer_cp_topk": (I, [P, P, I64, P, I, P, I, I, I, I, I, P, P, SZ, P]),
         "mono_pa_decode_fp8": (I, [P, P, P, I64, I, P, I, P, I, I, P, I, F, F, F, P, P, SZ, P]),
         "mono_sparse_decode_fp8": (I, [P, P, P, P, P, I64, I, P, I, P, I, I, I, F, F, F, P, P, P, SZ, P]),
         "fp8_pages_dequant_bf16": (I, [P, P, I64, P]),
@@ -429,39 +433,34 @@ def cp_shard_windows(bt_width, shards):
 
 
 def indexer_cp_topk(index_q_heads, index_pages, block_table, seq_lens, k, *, T=1, shards=None, workspace=None):
-    """Indexer context parallelism on one GPU: G shard scans, then one merge per head.
+    """Indexer context parallelism on one GPU (``mono_indexer_cp_topk``).
 
     index_q_heads: bf16 ``[H, B*T, 128]`` (every rank's index-q head).  Shard
     r scores block-table columns ``cp_shard_windows(W, G)[r]`` of every
-    request for all H heads (one window launch, the heads stacked as
-    requests) and emits its top-k (position, score) pairs; the merge keeps
-    each head's top-k over the G lists.  ``shards`` defaults to H.
+    request for all H heads in one launch (one read of its window), emitting
+    per head its top-k (position, score) pairs; the merge keeps each head's
+    top-k over the G lists.  ``shards`` defaults to H.
     Returns int32 ``[H, B*T, k]`` (any order within a row, -1 padding).
     """
+    lib = load_library()
     _need(index_q_heads.dim() == 3 and index_q_heads.shape[2] == HEAD_DIM and index_q_heads.dtype == torch.bfloat16,
           "index_q_heads must be bf16 [H, B*T, 128]")
+    _need(index_q_heads.is_contiguous(), "index_q_heads must be contiguous")
     H, N = index_q_heads.shape[0], index_q_heads.shape[1]
     G = H if shards is None else int(shards)
-    _need(G >= 1, "shards must be >= 1")
     B = _check_tables(block_table, seq_lens, N, T)
     dev = _on_gpu(index_q_heads, index_pages, block_table, seq_lens)
+    _check_pages(index_pages, "index_pages", 2, PAGE_BYTES)
     W = block_table.shape[1]
-    # The heads become H copies of the batch, one after another.
-    iq = index_q_heads.reshape(H * N, HEAD_DIM).contiguous()
-    bt = block_table[:B].repeat(H, 1).contiguous()
-    sl = seq_lens[:B].repeat(H).contiguous()
     k = int(k)
-    cand = torch.empty((G, H * N, k), dtype=torch.int32, device=dev)
-    cand_s = torch.empty((G, H * N, k), dtype=torch.float32, device=dev)
-    for r, (lo, hi) in enumerate(cp_shard_windows(W, G)):
-        if lo >= hi:  # more shards than table columns: an empty shard
-            cand[r].fill_(-1)
-            cand_s[r].fill_(float("nan"))
-            continue
-        mono_index_score_topk(iq, index_pages, bt, sl, k, T=T, out=cand[r], out_scores=cand_s[r],
-                              workspace=workspace, page_window=(lo, hi))
-    out, _ = mono_topk_merge(cand, cand_s, k)
-    return out.view(H, N, k)
+    need = int(lib.mono_indexer_cp_topk_workspace(B, T, H, W, k, G))
+    _need(need > 0, f"no workspace for B={B} T={T} heads={H} bt_stride={W} k={k} shards={G}")
+    ws = _workspace(workspace, dev, need, "cp")
+    out = torch.empty((H, N, k), dtype=torch.int32, device=dev)
+    _check(lib.mono_indexer_cp_topk(_ptr(index_q_heads), _ptr(index_pages), index_pages.shape[0], _ptr(block_table),
+                                    W, _ptr(seq_lens), B, T, H, k, G, _ptr(out), _ptr(ws.buf), ws.nbytes,
+                                    _stream(dev)))
+    return out
 
 
 def mono_pa_decode_mxfp4(q, k_pages, v_pages, block_table, seq_lens, selected_idx=None,

@@ -10,6 +10,8 @@
 #include "mono_decode.h"
 #include "launch.h"
 
+#include <algorithm>
+
 namespace mono {
 
 namespace {
@@ -205,6 +207,50 @@ int mono_topk_merge(const int32_t* cand_idx_dev, const float* cand_scores_dev, i
   if (N == 0) return MONO_OK;
   return launch_topk_merge(cand_idx_dev, cand_scores_dev, G, (int)N, k_in, k_out, out_idx_dev, out_scores_dev,
                            (hipStream_t)stream);
+}
+
+size_t mono_indexer_cp_topk_workspace(int B, int T, int heads, int bt_stride, int k, int shards) {
+  if (check_step_shape(B, T, bt_stride, k, true) != MONO_OK || heads < 1 || heads > kMaxHeads || shards < 1 ||
+      shards > 65536)
+    return 0;
+  return cp_layout(B, T, heads, bt_stride, k, shards).total;
+}
+
+int mono_indexer_cp_topk(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                         const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B, int T,
+                         int heads, int k, int shards, int32_t* selected_idx_dev, void* ws_dev, size_t ws_bytes,
+                         void* stream) {
+  const char* what = "mono_indexer_cp_topk";
+  clear_error();
+  CpLayout cp;
+  if (int rc = check_cp_call(index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride, seq_lens_dev, B, T,
+                             heads, k, shards, selected_idx_dev, ws_dev, ws_bytes, &cp))
+    return rc;
+  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  int32_t* cand = reinterpret_cast<int32_t*>(ws + cp.cand_idx);
+  float* cand_s = reinterpret_cast<float*>(ws + cp.cand_scores);
+  const size_t rows = (size_t)heads * B * T;
+  StepArgs a{};
+  a.fmt = kFmtMxfp4;
+  a.index_q = index_q_dev;
+  a.index_pages = index_pages_dev;
+  a.num_pages = num_pages;
+  a.block_table = block_table_dev;
+  a.bt_stride = bt_stride;
+  a.seq_lens = seq_lens_dev;
+  a.ws = ws;
+  // Shard r scores its page window for every head in one launch (each
+  // window page is read once), into its own candidate lists.
+  for (int r = 0; r < cp.shards; ++r) {
+    StepLayout lay = cp.index;
+    lay.win_lo = r * cp.width;
+    lay.win_hi = std::min(bt_stride, (r + 1) * cp.width);
+    a.sel = cand + (size_t)r * rows * k;
+    a.sel_scores = cand_s + (size_t)r * rows * k;
+    if (int rc = launch_step(a, lay, (hipStream_t)stream, what)) return rc;
+  }
+  // Each head's owner keeps the top k of the shards' lists.
+  return launch_topk_merge(cand, cand_s, cp.shards, (int)rows, k, k, selected_idx_dev, nullptr, (hipStream_t)stream);
 }
 
 int mono_index_score_topk_fp8(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,

@@ -12,11 +12,15 @@
 // (order-preserving score key << 32 | ~position; 0 for an empty slot), held
 // in registers, 32 per thread.  Every key is distinct (a position sits in
 // one shard only), so the k_out-th largest key K* is unique and the
-// selection is exactly the keys >= K*.  K* is found by radix select: digit
-// passes of 11, 11, 11, 11, 10 and 10 bits from the top, each a histogram
-// of the keys still matching the prefix found so far; the search stops as
-// soon as the remaining rank equals its bin's count (then the whole bin is
-// taken).  The selected keys are compacted with one LDS counter.
+// selection is exactly the keys >= K*.  K* is found by a radix select over
+// the range the keys actually span: each pass cuts the current range
+// [lo, hi] into at most 2048 bins of 2^s keys, counts the keys in each, and
+// narrows the range to the bin holding the remaining rank; it stops as soon
+// as that rank equals its bin's count (the whole bin is taken), at the
+// latest when bins hold one key value.  Binning the span rather than fixed
+// digits of the key spreads scores of one magnitude over many bins, so the
+// LDS counters see little contention.  The selected keys are compacted with
+// one LDS counter.
 #include "block_ops.h"
 #include "launch.h"
 #include "mono_decode.h"
@@ -36,7 +40,7 @@ __device__ __forceinline__ float score_of_key(uint32_t key) {
 struct MergeLds {
   uint32_t hist[kDigitBins];
   uint32_t scratch[kWaves + 3];
-  uint32_t cnt;
+  uint64_t lo[kWaves], hi[kWaves];
 };
 
 __global__ __launch_bounds__(256) void topk_merge_kernel(const int32_t* __restrict__ cand_idx,
@@ -47,64 +51,99 @@ __global__ __launch_bounds__(256) void topk_merge_kernel(const int32_t* __restri
   const int tid = threadIdx.x;
   const int i = blockIdx.x;
   const int n = G * k_in;
+  // Every load is issued before any is used (slots past the candidates
+  // read the row's first one and are dropped below), so they all overlap.
+  int32_t jv[kMergePer];
+  float sv[kMergePer];
+#pragma unroll
+  for (int u = 0; u < kMergePer; ++u) {
+    const int x = min(tid + kBlock * u, n - 1);
+    const int g = x / k_in, c = x - g * k_in;
+    const size_t off = ((size_t)g * N + i) * k_in + c;
+    jv[u] = cand_idx[off];
+    sv[u] = cand_scores[off];
+  }
   uint64_t key[kMergePer];
   uint32_t n_mine = 0;
 #pragma unroll
   for (int u = 0; u < kMergePer; ++u) {
-    const int x = tid + kBlock * u;
-    uint64_t kk = 0;
-    if (x < n) {
-      const int g = x / k_in, c = x - g * k_in;
-      const size_t off = ((size_t)g * N + i) * k_in + c;
-      const int32_t j = cand_idx[off];
-      if (j >= 0) kk = ((uint64_t)score_key(cand_scores[off]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-    }
-    key[u] = kk;
-    n_mine += kk != 0;
+    const bool ok = tid + kBlock * u < n && jv[u] >= 0;
+    key[u] = ok ? ((uint64_t)score_key(sv[u]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)jv[u]) : 0ull;
+    n_mine += ok;
   }
   uint32_t n_valid;
   (void)block_exclusive_scan(n_mine, lds.scratch, n_valid);
 
-  // Radix select of the threshold: keys k with (k & mask) >= prefix are taken.
-  uint64_t prefix = 0, mask = 0;
+  // Threshold: keys >= thr are taken.
+  uint64_t thr = 1;  // every non-empty key
   if (n_valid > (uint32_t)k_out) {
+    // The span of the keys.
+    uint64_t lo = ~0ull, hi = 0;
+#pragma unroll
+    for (int u = 0; u < kMergePer; ++u) {
+      if (key[u] != 0) {
+        lo = key[u] < lo ? key[u] : lo;
+        hi = key[u] > hi ? key[u] : hi;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const uint64_t ol = __shfl_xor(lo, off), oh = __shfl_xor(hi, off);
+      lo = ol < lo ? ol : lo;
+      hi = oh > hi ? oh : hi;
+    }
+    if ((tid & 63) == 0) {
+      lds.lo[tid >> 6] = lo;
+      lds.hi[tid >> 6] = hi;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      lo = lds.lo[w] < lo ? lds.lo[w] : lo;
+      hi = lds.hi[w] > hi ? lds.hi[w] : hi;
+    }
     uint32_t R = (uint32_t)k_out;
-    int shift = 64;
 #pragma unroll 1
-    for (int p = 0; p < 6; ++p) {
-      const int wd = p < 4 ? 11 : 10;
-      shift -= wd;
-      const int nbins = 1 << wd;
-      for (int x = tid; x < nbins; x += kBlock) lds.hist[x] = 0u;
+    for (;;) {
+      const uint64_t width = hi - lo;
+      const int bits = width == 0 ? 0 : 64 - __clzll((long long)width);
+      const int shift = bits > 11 ? bits - 11 : 0;  // (width >> shift) < 2048
+      for (int x = tid; x < kDigitBins; x += kBlock) lds.hist[x] = 0u;
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < kMergePer; ++u) {
-        if (key[u] != 0 && (key[u] & mask) == prefix)
-          atomicAdd(&lds.hist[(uint32_t)(key[u] >> shift) & (uint32_t)(nbins - 1)], 1u);
+        if (key[u] >= lo && key[u] <= hi && key[u] != 0) atomicAdd(&lds.hist[(uint32_t)((key[u] - lo) >> shift)], 1u);
       }
       __syncthreads();
-      const BinSplit b = find_bin_of_rank(lds.hist, nbins, R, lds.scratch);
-      prefix |= (uint64_t)b.bin << shift;
-      mask |= (uint64_t)(nbins - 1) << shift;
+      const BinSplit b = find_bin_of_rank(lds.hist, kDigitBins, R, lds.scratch);
+      const uint64_t b_lo = lo + ((uint64_t)b.bin << shift);
+      const uint64_t b_hi = shift == 0 ? b_lo : b_lo + (((uint64_t)1 << shift) - 1);
       R -= b.above;
-      if (b.count == R) break;  // the whole bin is taken
+      lo = b_lo;
+      hi = b_hi < hi ? b_hi : hi;
+      if (b.count == R || shift == 0) break;  // the whole bin is taken (one key value when shift == 0)
     }
+    thr = lo;
   }
-
-  if (tid == 0) lds.cnt = 0u;
-  __syncthreads();
+  // Each thread's taken keys go to consecutive slots after those of the
+  // threads before it (one prefix sum).
+  uint32_t n_take = 0;
+#pragma unroll
+  for (int u = 0; u < kMergePer; ++u) n_take += key[u] >= thr;  // thr >= 1: empty slots never count
+  uint32_t n_taken;
+  uint32_t slot = block_exclusive_scan(n_take, lds.scratch, n_taken);
 #pragma unroll
   for (int u = 0; u < kMergePer; ++u) {
-    const bool take = key[u] != 0 && (key[u] & mask) >= prefix;
-    const uint32_t slot = wave_append(take, &lds.cnt);
-    if (take && slot < (uint32_t)k_out) {
-      const size_t o = (size_t)i * k_out + slot;
-      out_idx[o] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[u]);
-      if (out_scores) out_scores[o] = score_of_key((uint32_t)(key[u] >> 32));
+    if (key[u] >= thr) {
+      if (slot < (uint32_t)k_out) {
+        const size_t o = (size_t)i * k_out + slot;
+        out_idx[o] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[u]);
+        if (out_scores) out_scores[o] = score_of_key((uint32_t)(key[u] >> 32));
+      }
+      ++slot;
     }
   }
-  __syncthreads();
-  const uint32_t taken = min(lds.cnt, (uint32_t)k_out);
+  const uint32_t taken = min(n_taken, (uint32_t)k_out);
   for (int x = (int)taken + tid; x < k_out; x += kBlock) {
     const size_t o = (size_t)i * k_out + x;
     out_idx[o] = -1;

@@ -33,7 +33,7 @@ void clear_error() { g_error[0] = '\0'; }
 const char* last_error() { return g_error; }
 
 // ---- workspace layout ------------------------------------------------------------
-StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse) {
+StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse, int G) {
   StepLayout l{};
   l.mode = mode;
   l.B = B;
@@ -41,8 +41,9 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.H = H;
   l.k = k;
   l.sparse = sparse;
-  const size_t N = (size_t)B * T;
-  l.q_groups = (T + 3) / 4;
+  l.G = G;
+  const size_t N = (size_t)G * B * T;  // index rows (query tokens when G == 1)
+  l.q_groups = (G * T + 3) / 4;
   l.chunk_pages = kScanChunkPages;  // plan_step re-balances this to the resident workgroups
   l.chunks = (bt_stride + l.chunk_pages - 1) / l.chunk_pages;
   l.lcap = bt_stride * kPageTokens;
@@ -133,7 +134,7 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
 // ---- launch plan -------------------------------------------------------------------
 long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_scores, int* variant,
                const char* what) {
-  const bool tq4 = lay.T > 1 && (lay.mode & kModeIndex);
+  const bool tq4 = lay.G * lay.T > 1 && (lay.mode & kModeIndex);
   *variant = step_variant(tq4, fp8);
   if (lay.mode == kModeAttn && dev.resident[attn_variant(fp8)] > 0) *variant = attn_variant(fp8);
   int cap = std::max(1, dev.resident[*variant]);
@@ -152,11 +153,11 @@ long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_s
     // once the slices would take more than two rounds of the resident
     // workgroups; with fewer query tokens, slices spread each selection
     // over more compute units and finish sooner.
-    const size_t N = (size_t)lay.B * lay.T;
+    const size_t N = (size_t)lay.G * lay.B * lay.T;
     if ((size_t)span * kPageTokens <= kSelectMax && N * (size_t)lay.slices > 2 * (size_t)cap) {
       lay.select_mode = 1;
       lay.n_filter = 0u;
-      lay.n_select = lay.T > 1 ? (uint32_t)N : 0u;
+      lay.n_select = lay.G * lay.T > 1 ? (uint32_t)N : 0u;
       lay.n_queue = lay.n_select + lay.n_attn;
     }
   }
@@ -314,6 +315,41 @@ int check_merge_call(const void* cand_idx, const void* cand_scores, int G, int64
   if (!cand_idx || !cand_scores || !out_idx) return set_error(MONO_EINVAL, "mono_topk_merge: NULL buffer");
   if (!aligned(cand_idx, 4) || !aligned(cand_scores, 4) || !aligned(out_idx, 4) || !aligned(out_scores, 4))
     return set_error(MONO_EINVAL, "mono_topk_merge: buffers need 4-byte alignment");
+  return MONO_OK;
+}
+
+CpLayout cp_layout(int B, int T, int G, int bt_stride, int k, int shards) {
+  CpLayout c{};
+  c.index = step_layout(kModeIndex, B, T, 1, bt_stride, k, 1, G);
+  c.width = (bt_stride + shards - 1) / shards;
+  c.shards = (bt_stride + c.width - 1) / c.width;  // windows [r * width, ...) that start inside the table
+  const size_t rows = (size_t)G * B * T;
+  const size_t cand = (size_t)c.shards * rows * (size_t)k * 4;
+  c.cand_idx = (c.index.total + 255) & ~(size_t)255;
+  c.cand_scores = c.cand_idx + ((cand + 255) & ~(size_t)255);
+  c.total = c.cand_scores + cand;
+  return c;
+}
+
+int check_cp_call(const void* index_q, const void* index_pages, int64_t num_pages, const void* block_table,
+                  int bt_stride, const void* seq_lens, int B, int T, int G, int k, int shards, const void* out,
+                  const void* ws, size_t ws_bytes, CpLayout* lay) {
+  const char* what = "mono_indexer_cp_topk";
+  if (int rc = check_step_shape(B, T, bt_stride, k, true)) return rc;
+  if (G < 1 || G > kMaxHeads) return set_error(MONO_EINVAL, "%s: heads must be in [1, %d] (got %d)", what, kMaxHeads, G);
+  if ((long long)G * B * T > (1LL << 30)) return set_error(MONO_EINVAL, "%s: heads*B*T too large", what);
+  if (shards < 1 || shards > 65536) return set_error(MONO_EINVAL, "%s: shards must be in [1, 65536] (got %d)", what, shards);
+  if (!index_q || !index_pages || !block_table || !seq_lens || !out || !ws)
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
+  if (!aligned(index_q, 16) || !aligned(index_pages, 16) || !aligned(ws, 256) || !aligned(block_table, 4) ||
+      !aligned(seq_lens, 4) || !aligned(out, 4))
+    return set_error(MONO_EINVAL, "%s: index_q/pages need 16-byte, ws 256-byte, tables 4-byte alignment", what);
+  *lay = cp_layout(B, T, G, bt_stride, k, shards);
+  if ((long long)lay->shards * k > kMergeMaxCandidates)
+    return set_error(MONO_ENOTSUP, "%s: shards*k = %d*%d candidates per row exceed %d", what, lay->shards, k,
+                     kMergeMaxCandidates);
+  if (ws_bytes < lay->total) return set_error(MONO_ENOSPC, "%s: workspace %zu B < %zu B", what, ws_bytes, lay->total);
   return MONO_OK;
 }
 

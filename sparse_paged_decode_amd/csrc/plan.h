@@ -66,7 +66,10 @@ constexpr uint32_t kIndexMask = (1u << kKindShift) - 1u;
 
 struct StepLayout {
   int mode, B, T, H, k, sparse;
-  int q_groups;      // ceil(T / 4) query-token groups per request
+  int G;             // index-q heads scored per query token (index call only; else 1)
+  // Index rows: G * B * T, row (h, b, t) at h * B * T + b * T + t.  A
+  // request's rows are its G * T (head, token) pairs u = h * T + t.
+  int q_groups;      // ceil(G * T / 4) row groups per request
   int chunk_pages;   // index pages per scan chunk
   int chunks;        // scan chunks per query group (window pages / chunk_pages, rounded up)
   int win_lo, win_hi;  // page window [win_lo, win_hi) of every request the index items score
@@ -90,7 +93,8 @@ struct StepLayout {
 };
 
 // Workspace layout of one call (mode, shapes); sizes only, no device state.
-StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse);
+// G > 1 only for the index call (mode kModeIndex).
+StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int sparse, int G = 1);
 
 // Kernel instances of the step kernel: [1, 4 query tokens] x [MXFP4, fp8],
 // then the chunk-local instances [MXFP4, fp8], then the attention-only
@@ -143,6 +147,20 @@ int check_sparse_call(const char* what, const void* index_q, const void* index_p
                       const void* ws, size_t ws_bytes, StepLayout* lay);
 int check_merge_call(const void* cand_idx, const void* cand_scores, int G, int64_t N, int k_in, int k_out,
                      const void* out_idx, const void* out_scores);
+// Indexer context parallelism on one device: the index layout of G heads
+// (its workspace first) and the shard candidate buffers after it.
+struct CpLayout {
+  StepLayout index;    // the index call over G heads, one page window at a time
+  int shards;          // shards with a non-empty window (windows past the table are empty)
+  int width;           // block-table columns per shard window: ceil(bt_stride / shards)
+  size_t cand_idx;     // byte offset of int32 [shards, G*B*T, k] candidate positions
+  size_t cand_scores;  // byte offset of fp32 [shards, G*B*T, k] candidate scores
+  size_t total;
+};
+CpLayout cp_layout(int B, int T, int G, int bt_stride, int k, int shards);
+int check_cp_call(const void* index_q, const void* index_pages, int64_t num_pages, const void* block_table,
+                  int bt_stride, const void* seq_lens, int B, int T, int G, int k, int shards, const void* out,
+                  const void* ws, size_t ws_bytes, CpLayout* lay);
 int check_insert_call(const void* k_rows, const void* v_rows, const void* index_rows, const void* slots, int64_t n,
                       int kv_heads, const void* k_pages, const void* v_pages, const void* index_pages,
                       int64_t num_pages, const void* err);

@@ -103,13 +103,16 @@ __device__ __forceinline__ void publish(const StepLayout& lay, uint32_t* ctrl, u
     store_coherent(ctrl + lay.queue + base + x, (kind << kKindShift) | (first + x));
 }
 
-// Chunks of request b's query group qg (pages seen by the group's last query token).
-__device__ __forceinline__ int group_chunks(int L, int T, int qg, int chunk_pages, int& tq, int& n_pages) {
-  const int t0 = qg * 4;
-  tq = min(4, T - t0);
-  const int n_tok = L - T + t0 + tq;
-  n_pages = (n_tok + kPageTokens - 1) / kPageTokens;
-  return (n_pages + chunk_pages - 1) / chunk_pages;
+// Index row of request b's (head, token) pair u = h * T + t.
+__device__ __forceinline__ int index_row(const StepLayout& lay, int b, int u) {
+  return (u / lay.T) * (lay.B * lay.T) + b * lay.T + u % lay.T;
+}
+
+// Request and query token of index row i.
+__device__ __forceinline__ void row_request(const StepLayout& lay, int i, int& b, int& t) {
+  const int r = i % (lay.B * lay.T);
+  b = r / lay.T;
+  t = r % lay.T;
 }
 
 // Tokens query position pos sees inside the layout's page window (all of
@@ -179,7 +182,9 @@ __device__ __forceinline__ SelectArgs select_args(const StepArgs& a, const StepL
 template <int TQ>
 __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout& lay, uint32_t i, StepLds<TQ>& lds,
                                             uint32_t* ctrl, uint32_t* err, uint32_t& s_pub) {
-  const int T = lay.T, b = (int)i / T, t = (int)i % T;
+  const int T = lay.T;
+  int b, t;
+  row_request(lay, (int)i, b, t);
   const int L = a.seq_lens[b];
   if (L >= T && L <= lay.lcap) {  // an invalid length was reported by the scan items
     select_query(select_args(a, lay, (int)i, window_valid(lay, L - T + t), ctrl, err), lds.resolve);
@@ -280,12 +285,12 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     sa.pages = a.index_pages;
     sa.num_pages = a.num_pages;
     sa.bt_row = a.block_table + (size_t)b * a.bt_stride;
-    sa.q_scores = nullptr;
-    sa.ghist = g1;
+    sa.scores = nullptr;
+    sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist);  // row i: g1
     sa.err = err;
     sa.lcap = lay.lcap;
-    sa.q0 = i;
-    sa.pos0 = L - 1;
+    sa.row[0] = sa.row[1] = sa.row[2] = sa.row[3] = i;
+    sa.pos[0] = sa.pos[1] = sa.pos[2] = sa.pos[3] = L - 1;
     sa.tq = 1;
     sa.p_begin = p_begin;
     sa.p_end = p_end;
@@ -578,29 +583,34 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
   const int qg = rem / lay.chunks, c = rem % lay.chunks;
   const int T = lay.T;
   const int L = a.seq_lens[b];
-  const int t0 = qg * 4;
-  const int tq_all = min(4, T - t0);
+  // The group's rows: the request's (head, token) pairs u0..u0+tq-1.
+  const int u0 = qg * 4;
+  const int tq = min(4, lay.G * T - u0);
   if (L < T || L > lay.lcap) {
     if (c == 0 && qg == 0 && thread_index() == 0) raise_error(err, kErrSeqLen);
   } else {
-    int tq, n_pages;
-    group_chunks(L, T, qg, lay.chunk_pages, tq, n_pages);
+    ScanArgs sa;
+    int last = 0;  // position of the group's last-placed token
+    for (int m = 0; m < 4; ++m) {
+      const int u = u0 + min(m, tq - 1);
+      sa.row[m] = index_row(lay, b, u);
+      const int pos = L - T + u % T;
+      sa.pos[m] = pos - lay.win_lo * kPageTokens;  // scores are indexed from the window's first token
+      last = max(last, pos);
+    }
     // The group's pages inside the window, relative to its first page.
+    const int n_pages = (last + 1 + kPageTokens - 1) / kPageTokens;
     const int n_rel = max(0, min(n_pages, lay.win_hi) - lay.win_lo);
     const int nchunks = (n_rel + lay.chunk_pages - 1) / lay.chunk_pages;
     if (c < nchunks) {
-      const int q0 = b * T + t0;
-      ScanArgs sa;
       sa.index_q = a.index_q;
       sa.pages = a.index_pages;
       sa.num_pages = a.num_pages;
       sa.bt_row = a.block_table + (size_t)b * a.bt_stride + lay.win_lo;
-      sa.q_scores = reinterpret_cast<float*>(a.ws + lay.scores) + (size_t)q0 * lay.lcap;
-      sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist) + (size_t)q0 * kHistBins;
+      sa.scores = reinterpret_cast<float*>(a.ws + lay.scores);
+      sa.ghist = reinterpret_cast<uint32_t*>(a.ws + lay.hist);
       sa.err = err;
       sa.lcap = lay.lcap;
-      sa.q0 = q0;
-      sa.pos0 = L - T + t0 - lay.win_lo * kPageTokens;  // scores are indexed from the window's first token
       sa.tq = tq;
       sa.p_begin = c * lay.chunk_pages;
       sa.p_end = min(sa.p_begin + lay.chunk_pages, n_rel);
@@ -609,19 +619,31 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
     }
   }
   // Every chunk slot of the group arrives, with or without work; the last
-  // one publishes the group's filter slices.
+  // one publishes the selection work of the group's rows.
   __syncthreads();
   if (thread_index() == 0)
     s_flag = atomicAdd(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, 1u) == (uint32_t)(lay.chunks - 1);
   __syncthreads();
   if (!s_flag) return;
-  const uint32_t q0 = (uint32_t)(b * T + t0);
-  if (!lay.select_mode) {
-    publish(lay, ctrl, kItemFilter, q0 * (uint32_t)lay.slices, (uint32_t)(tq_all * lay.slices), err, s_pub);
-  } else if (T == 1) {
-    select_item<TQ>(a, lay, q0, slds, ctrl, err, s_pub);
+  if (lay.G == 1) {  // the group's rows are consecutive
+    const uint32_t q0 = (uint32_t)(b * T + u0);
+    if (!lay.select_mode) {
+      publish(lay, ctrl, kItemFilter, q0 * (uint32_t)lay.slices, (uint32_t)(tq * lay.slices), err, s_pub);
+    } else if (T == 1) {
+      select_item<TQ>(a, lay, q0, slds, ctrl, err, s_pub);
+    } else {
+      publish(lay, ctrl, kItemSelect, q0, (uint32_t)tq, err, s_pub);
+    }
   } else {
-    publish(lay, ctrl, kItemSelect, q0, (uint32_t)tq_all, err, s_pub);
+    for (int m = 0; m < tq; ++m) {
+      const uint32_t row = (uint32_t)index_row(lay, b, u0 + m);
+      if (!lay.select_mode) {
+        publish(lay, ctrl, kItemFilter, row * (uint32_t)lay.slices, (uint32_t)lay.slices, err, s_pub);
+      } else {
+        publish(lay, ctrl, kItemSelect, row, 1u, err, s_pub);
+      }
+      __syncthreads();  // the next publication reuses s_pub
+    }
   }
 }
 
@@ -629,7 +651,9 @@ template <int TQ>
 __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout& lay, uint32_t u, StepLds<TQ>& lds,
                                             uint32_t* ctrl, uint32_t* err, uint32_t& s_flag, uint32_t& s_pub) {
   const int i = (int)(u / lay.slices), s = (int)(u % lay.slices);
-  const int T = lay.T, b = i / T, t = i % T;
+  const int T = lay.T;
+  int b, t;
+  row_request(lay, i, b, t);
   const int L = a.seq_lens[b];
   const bool valid = L >= T && L <= lay.lcap;  // an invalid length was reported by the scan items
   const int n_valid = window_valid(lay, L - T + t);

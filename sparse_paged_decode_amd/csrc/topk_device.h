@@ -41,26 +41,28 @@ struct ScanLds {
 };
 
 // ---------------------------------------------------------------------------
-// scan_chunk: pages [p_begin, p_end) of request b for query tokens t0..t0+tq-1.
+// scan_chunk: pages [p_begin, p_end) of request b for up to four index rows
+// of the request (query tokens, or (head, token) pairs).
 // Wave w scores rows 32w..32w+31 of every page as two 16-row MFMA tiles; lane
 // (g = lane/16, m = lane%16) loads chunk g (elements 32g..32g+31: one e8m0
 // block of 16 bytes, or 32 fp8 bytes) of row m of a tile, which is that
-// row's B-operand slot for the four k-steps.  Scores: C = Q K^T with the query tokens as M and the 16
-// rows of a tile as N, so lane (0, n) ends with row n's scores for query
-// tokens 0..3 (acc[i]).
+// row's B-operand slot for the four k-steps.  Scores: C = Q K^T with the
+// group's index rows as M and the 16 token rows of a tile as N, so lane
+// (0, n) ends with token row n's scores for group rows 0..3 (acc[i]): one
+// read of the page serves all of them.
 // ---------------------------------------------------------------------------
 struct ScanArgs {
-  const uint16_t* index_q;  // bf16 [B*T, 128]
+  const uint16_t* index_q;  // bf16 [rows, 128]
   const uint8_t* pages;     // [num_pages, page bytes of the format]
   int64_t num_pages;
   const int32_t* bt_row;    // block-table row of request b
-  float* q_scores;          // scores of query token t0, rows lcap apart
-  uint32_t* ghist;          // histogram rows of query tokens t0.., kHistBins apart
+  float* scores;            // score rows, lcap apart
+  uint32_t* ghist;          // histogram rows, kHistBins apart
   uint32_t* err;
   int lcap;
-  int q0;                   // flat index b*T + t0 of the group's first query token
-  int pos0;                 // position of query token t0
-  int tq;                   // query tokens in the group (1..4)
+  int row[4];               // index rows of the group (q vector, score row, histogram row)
+  int pos[4];               // their positions (relative to the window's first token)
+  int tq;                   // rows in the group (1..4)
   int p_begin, p_end;       // pages of the chunk
 };
 
@@ -79,13 +81,13 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
 
-  // A operand: row m is query token t0 + m (zero when m >= tq); its k-slot
-  // (g, e) of k-step s holds index-q element 32g + 8s + e.
+  // A operand: row m is group row m (zero when m >= tq); its k-slot (g, e)
+  // of k-step s holds index-q element 32g + 8s + e.
   const bool has_q = m < a.tq;
   bf16x8_t aq[4];
   {
-    const u32x4_t* src =
-        reinterpret_cast<const u32x4_t*>(a.index_q + (size_t)(a.q0 + (has_q ? m : 0)) * kHeadDim + 32 * g);
+    const int qrow = m == 1 ? a.row[1] : m == 2 ? a.row[2] : m == 3 ? a.row[3] : a.row[0];
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.index_q + (size_t)(has_q ? qrow : a.row[0]) * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t v = src[s];
@@ -149,11 +151,11 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
         const int j = p * kPageTokens + 32 * wave + 16 * tile + m;
 #pragma unroll
         for (int i = 0; i < TQ; ++i) {
-          if (i < a.tq && j <= a.pos0 + i) {
+          if (i < a.tq && j <= a.pos[i]) {
             if constexpr (kLocal) {
               lds_scores[j - p_begin * kPageTokens] = c[i];
             } else {
-              store_coherent(a.q_scores + (size_t)i * a.lcap + j, c[i]);
+              store_coherent(a.scores + (size_t)a.row[i] * a.lcap + j, c[i]);
             }
             atomicAdd(&lds.hist[i * kHistBins + (score_key(c[i]) >> kHistShift)], 1u);
           }
@@ -176,9 +178,12 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
   }
   __syncthreads();
 
-  for (int x = tid; x < a.tq * kHistBins; x += kBlock) {
-    const uint32_t v = lds.hist[x];
-    if (v) atomicAdd(&a.ghist[x], v);
+  for (int i = 0; i < TQ && i < a.tq; ++i) {
+    uint32_t* gh = a.ghist + (size_t)a.row[i] * kHistBins;
+    for (int x = tid; x < kHistBins; x += kBlock) {
+      const uint32_t v = lds.hist[i * kHistBins + x];
+      if (v) atomicAdd(&gh[x], v);
+    }
   }
 }
 

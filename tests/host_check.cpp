@@ -154,6 +154,38 @@ static void check_merge_insert_bench() {
   EXPECT_CODE(check_merge_call(nullptr, ptr(1), 4, 64, 2048, 2048, ptr(2), ptr(3)), MONO_EINVAL);
   EXPECT_CODE(check_merge_call(misaligned(0), ptr(1), 4, 64, 2048, 2048, ptr(2), ptr(3)), MONO_EINVAL);
 
+  // Indexer context parallelism: shard windows, the candidate budget and
+  // the workspace.
+  {
+    const CpLayout c = cp_layout(64, 1, 4, 256, 2048, 4);
+    CHECK(c.shards == 4 && c.width == 64);
+    CHECK(c.index.G == 4 && c.index.q_groups == 1);  // the four heads of a token share one scan group
+    CHECK(c.cand_idx >= c.index.total && c.cand_scores >= c.cand_idx + (size_t)4 * 256 * 2048 * 4);
+    CHECK(c.total == c.cand_scores + (size_t)4 * 256 * 2048 * 4);
+    const CpLayout e = cp_layout(2, 1, 3, 5, 100, 8);  // more shards than columns: 5 non-empty windows
+    CHECK(e.width == 1 && e.shards == 5);
+    const CpLayout m = cp_layout(3, 2, 3, 33, 250, 2);  // (head, token) rows: 6 per request, 2 groups
+    CHECK(m.shards == 2 && m.width == 17 && m.index.q_groups == 2);
+    CpLayout out;
+    const size_t big = (size_t)1 << 40;
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 4, ptr(4), ptr(5), big, &out),
+                MONO_OK);
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 5, ptr(4), ptr(5), big, &out),
+                MONO_ENOTSUP);  // five shards of 2048 candidates
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 0, 2048, 4, ptr(4), ptr(5), big, &out),
+                MONO_EINVAL);  // no heads
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 0, ptr(4), ptr(5), big, &out),
+                MONO_EINVAL);  // no shards
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 4, nullptr, ptr(5), big, &out),
+                MONO_EINVAL);
+    EXPECT_CODE(check_cp_call(ptr(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 4, ptr(4), ptr(5),
+                              cp_layout(64, 1, 4, 256, 2048, 4).total - 1, &out),
+                MONO_ENOSPC);
+    EXPECT_CODE(check_cp_call(misaligned(0), ptr(1), 100, ptr(2), 256, ptr(3), 64, 1, 4, 2048, 4, ptr(4), ptr(5), big,
+                              &out),
+                MONO_EINVAL);
+  }
+
   auto ins = [&](const void* kr, const void* vr, const void* ir, int64_t n, int H, const void* kp, const void* vp,
                  const void* ip, int64_t np, const void* err, const void* slots = ptr(9)) {
     return check_insert_call(kr, vr, ir, slots, n, H, kp, vp, ip, np, err);
@@ -204,9 +236,9 @@ static void check_layout(const StepLayout& l) {
 
 // Plan invariants for a call of the given shape on a device.
 static void check_plan(int mode, int B, int T, int H, int bts, int k, bool fp8, bool sel_scores, int lo, int hi,
-                       const DeviceShape& dev) {
+                       const DeviceShape& dev, int G = 1) {
   const int sparse = (mode & kModeIndex) ? 1 : (k > 0);
-  const StepLayout l0 = step_layout(mode, B, T, H, bts, k, sparse);
+  const StepLayout l0 = step_layout(mode, B, T, H, bts, k, sparse, G);
   check_layout(l0);
   StepLayout l = l0;
   if (lo >= 0) {
@@ -234,7 +266,7 @@ static void check_plan(int mode, int B, int T, int H, int bts, int k, bool fp8, 
   } else if (mode == kModeAttn && dev.resident[attn_variant(fp8)] > 0) {
     CHECK(variant == attn_variant(fp8));  // the attention call's own instance
   } else {
-    CHECK(variant == step_variant(T > 1 && (mode & kModeIndex), fp8));
+    CHECK(variant == step_variant(G * T > 1 && (mode & kModeIndex), fp8));
   }
 }
 
@@ -318,7 +350,8 @@ static void check_plans() {
       lo = (int)(rng() % bts);
       hi = lo + 1 + (int)(rng() % (bts - lo));
     }
-    check_plan(mode, B, T, H, bts, k, fp8, scores, lo, hi, d);
+    const int G = mode == kModeIndex ? 1 + (int)(rng() % 5) : 1;  // index heads (context parallelism)
+    check_plan(mode, B, T, H, bts, k, fp8, scores, lo, hi, d, G);
   }
 }
 

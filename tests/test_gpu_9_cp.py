@@ -5,8 +5,10 @@
   positions inside the window.
 * The merge kernel reproduces the oracle's merge exactly (the same
   position and score pairs; the order within a row is free).
-* Shards-then-merge selects exactly the sets the global index call selects
-  (same fp32 scores, same tie rule), and matches the oracle's global top-k.
+* Shards-then-merge (one C-ABI call: each shard scores its window for all
+  heads in one launch, groups of up to four (head, token) rows sharing each
+  page read) selects exactly the sets the global index call selects (same
+  fp32 scores, same tie rule), and matches the oracle's global top-k.
 """
 
 import numpy as np
@@ -100,7 +102,9 @@ def _heads(w, H, seed):
 
 
 @pytest.mark.parametrize("H,G,T,lens,W,k", [(4, 4, 1, [1, 500, 3000, 9000], 71, 700), (2, 3, 4, [4, 1000, 2049], 17, 300),
-                                            (3, 8, 1, [300, 600], 5, 100)], ids=["h4_g4", "h2_g3_t4", "h3_g8_empty_shards"])
+                                            (3, 8, 1, [300, 600], 5, 100), (3, 2, 2, [2, 129, 4000], 33, 250),
+                                            (5, 4, 3, [3, 777, 2500], 20, 64)],
+                         ids=["h4_g4", "h2_g3_t4", "h3_g8_empty_shards", "h3_g2_t2_mixed_groups", "h5_g4_t3"])
 def test_cp_equals_global_selection(spd, H, G, T, lens, W, k):
     w = make_workload(f"cp{H}{G}", B=len(lens), T=T, seq_lens=lens, bt_width=W, k=k, seed=72 + H, exp_range=(124, 127))
     d = to_device(w)
