@@ -591,6 +591,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
   } else {
     ScanArgs sa;
     int last = 0;  // position of the group's last-placed token
+#pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int u = u0 + min(m, tq - 1);
       sa.row[m] = index_row(lay, b, u);

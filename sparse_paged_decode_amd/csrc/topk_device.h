@@ -86,8 +86,11 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
   const bool has_q = m < a.tq;
   bf16x8_t aq[4];
   {
-    const int qrow = m == 1 ? a.row[1] : m == 2 ? a.row[2] : m == 3 ? a.row[3] : a.row[0];
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.index_q + (size_t)(has_q ? qrow : a.row[0]) * kHeadDim + 32 * g);
+    // (Selected by value: the rows are uniform, each read at a fixed index.)
+    const int r0 = __builtin_amdgcn_readfirstlane(a.row[0]), r1 = __builtin_amdgcn_readfirstlane(a.row[1]);
+    const int r2 = __builtin_amdgcn_readfirstlane(a.row[2]), r3 = __builtin_amdgcn_readfirstlane(a.row[3]);
+    const int qrow = m == 1 ? r1 : m == 2 ? r2 : m == 3 ? r3 : r0;
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.index_q + (size_t)(has_q ? qrow : r0) * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       u32x4_t v = src[s];
@@ -178,11 +181,14 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
   }
   __syncthreads();
 
-  for (int i = 0; i < TQ && i < a.tq; ++i) {
-    uint32_t* gh = a.ghist + (size_t)a.row[i] * kHistBins;
-    for (int x = tid; x < kHistBins; x += kBlock) {
-      const uint32_t v = lds.hist[i * kHistBins + x];
-      if (v) atomicAdd(&gh[x], v);
+#pragma unroll
+  for (int i = 0; i < TQ; ++i) {
+    if (i < a.tq) {
+      uint32_t* gh = a.ghist + (size_t)a.row[i] * kHistBins;
+      for (int x = tid; x < kHistBins; x += kBlock) {
+        const uint32_t v = lds.hist[i * kHistBins + x];
+        if (v) atomicAdd(&gh[x], v);
+      }
     }
   }
 }
