@@ -99,6 +99,8 @@ def parse():
     p.add_argument("--skip-graph", action="store_true", help="do not time the HIP-graph replays")
     p.add_argument("--skip-insert", action="store_true", help="do not time the cache insert")
     p.add_argument("--skip-cp", action="store_true", help="do not time the indexer context-parallel emulation")
+    p.add_argument("--skip-scan-variants", action="store_true",
+                   help="do not time the index scan on the matrix cores against the same scan on the VALU")
     p.add_argument("--skip-clocks", action="store_true",
                    help="do not sample the clocks under load (about one second of extra steps)")
     p.add_argument("--skip-ceilings", action="store_true",
@@ -337,6 +339,32 @@ def time_cp(spd, torch, dev, w, iq, ip, bt, sl, reps, heads=4):
     }
 
 
+def time_scan_variants(spd, torch, dev, w, iq, ip, bt, sl, reps, chunk_pages=32):
+    """The scan phase on the matrix cores and on the VALU (same reads, same
+    LDS scores and histograms): kernel times and read rates."""
+    hist = torch.zeros((w.B, 2048), dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    q1 = iq.view(w.B, w.T, 128)[:, -1].contiguous()  # each request's last query token
+    out = {}
+    for variant, name in ((0, "mfma"), (1, "valu")):
+        for _ in range(3):
+            spd.bench_scan(q1, ip, bt, sl, chunk_pages, variant, hist=hist, err=err)
+        torch.cuda.synchronize(dev)
+        with spd.KernelTimer(capacity=reps + 8) as kt:
+            for _ in range(reps):
+                spd.bench_scan(q1, ip, bt, sl, chunk_pages, variant, hist=hist, err=err)
+            torch.cuda.synchronize(dev)
+        us = kt.mean_us[f"scan_{name}_kernel"]
+        out[f"{name}_kernel_us"] = round(us, 2)
+    toks = int(np.clip(w.seq_lens.astype(np.int64), 0, None).sum())
+    nbytes = toks * ROW_BYTES["mxfp4"]
+    out["index_bytes"] = nbytes
+    out["mfma_gbps"] = round(nbytes / out["mfma_kernel_us"] / 1e3, 1)
+    out["valu_gbps"] = round(nbytes / out["valu_kernel_us"] / 1e3, 1)
+    out["chunk_pages"] = chunk_pages
+    return out
+
+
 class StepRunner:
     """One workload's inputs in HBM and its step.
 
@@ -570,6 +598,9 @@ def main():
             cp = time_cp(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
         else:
             cp = {"skipped": f"4 shards x top-{w.k} = {4 * w.k} candidates per query token; the merge takes 8192"}
+    scan_variants = None
+    if w.sparse and not f8 and not args.skip_scan_variants:
+        scan_variants = time_scan_variants(spd, torch, dev, w, iq, ip[0], bt, sl, min(K, 50))
     ceilings = None
     if w.sparse and not f8 and not args.skip_ceilings:
         ceilings = read_ceilings(spd, torch, dev, run, min(K, 50))
@@ -622,6 +653,7 @@ def main():
         "device_errors": device_errors,
         "insert": ins,
         "cp_emulation": cp,
+        "scan_mfma_vs_valu": scan_variants,
         "read_ceilings": ceilings,
         "cpu_baseline": cpu,
         "wall_s": round(wall, 3),

@@ -413,7 +413,7 @@ int mono_insert_mxfp4(const uint16_t* k_rows_dev, const uint16_t* v_rows_dev,
  * Returns the number of kernel ids the library has (MONO_NUM_KERNELS) or a
  * negative code.  mono_kernel_name(id) is the kernel's name ("" if unknown).
  * ------------------------------------------------------------------------- */
-#define MONO_NUM_KERNELS 15
+#define MONO_NUM_KERNELS 17
 int mono_profile_start(int capacity);
 int mono_profile_stop(double* total_ms, int* launches, int n);
 const char* mono_kernel_name(int id);
@@ -434,6 +434,24 @@ const char* mono_kernel_name(int id);
  * ------------------------------------------------------------------------- */
 int mono_bench_read(const uint8_t* pages_dev, const int32_t* page_ids_dev, int64_t n_pages, int mode,
                     int grid, uint32_t* sink_dev, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * The index scan on the matrix cores against the same scan on the vector
+ * ALUs, for benchmarks only.  Workgroup (b, c) scores pages
+ * [c*chunk_pages, ...) of request b's block-table row for query row b of
+ * index_q_dev (bf16 [B, 128]; one query token per request, at position
+ * seq_lens[b] - 1), keeps the scores in LDS and adds their histogram over
+ * the top 11 score-key bits to hist_dev[b] (uint32 [B, 2048], accumulated:
+ * the caller zeroes it).  Scores are the mxfp4_pages page's dot products of
+ * the query with the exactly dequantised token rows.
+ *   variant 0: the step's scan (bf16 MFMA 16x16x32);
+ *   variant 1: v_dot2_f32_bf16 on the VALU, two lanes per token row.
+ * chunk_pages in [1, 32].  err_dev: MONO_DEVERR_PAGE_ID on a bad page id.
+ * MONO_EINVAL for bad sizes, variant or pointers.
+ * ------------------------------------------------------------------------- */
+int mono_bench_scan(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                    const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B,
+                    int chunk_pages, int variant, uint32_t* hist_dev, uint32_t* err_dev, void* stream);
 
 /* Debug/test only.  Waits for `stream`, then returns the device error bits
  * (MONO_DEVERR_*) accumulated in the workspace and clears them, or a

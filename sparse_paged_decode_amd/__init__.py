@@ -57,6 +57,7 @@ from ._binding import (  # noqa: F401
     MonoError,
     Workspace,
     bench_read,
+    bench_scan,
     check_device_errors,
     cp_shard_windows,
     fp8_pages_dequant_bf16,

@@ -66,6 +66,7 @@ EXPORTED_SYMBOLS = (
     "fp8_pages_dequant_bf16",
     "mono_check_device_errors",
     "mono_bench_read",
+    "mono_bench_scan",
     "mono_profile_start",
     "mono_profile_stop",
     "mono_kernel_name",
@@ -120,6 +121,7 @@ def load_library(path=LIB_PATH):
         "fp8_pages_dequant_bf16": (I, [P, P, I64, P]),
         "mono_check_device_errors": (I, [P, P]),
         "mono_bench_read": (I, [P, P, I64, I, I, P, P]),
+        "mono_bench_scan": (I, [P, P, I64, P, I, P, I, I, I, P, P, P]),
         "mono_profile_start": (I, [I]),
         "mono_profile_stop": (I, [P, P, I]),
         "mono_kernel_name": (ctypes.c_char_p, [I]),
@@ -701,6 +703,29 @@ def bench_read(pages, page_ids=None, grid=512, sink=None):
     return sink
 
 
+def bench_scan(index_q, index_pages, block_table, seq_lens, chunk_pages, variant, hist=None, err=None):
+    """The index scan phase on the matrix cores (variant 0) or the VALU
+    (variant 1): bf16 ``index_q [B, 128]``, one query token per request.
+    Adds each request's score histogram (2048 bins) to ``hist`` (int32
+    ``[B, 2048]``, zeroed when created here); returns (hist, err word)."""
+    lib = load_library()
+    _need(index_q.dtype == torch.bfloat16 and index_q.dim() == 2 and index_q.shape[1] == HEAD_DIM
+          and index_q.is_contiguous(), "index_q must be bf16 [B, 128], contiguous")
+    _check_pages(index_pages, "index_pages", 2, PAGE_BYTES)
+    B = index_q.shape[0]
+    B = _check_tables(block_table, seq_lens, B, 1)
+    dev = _on_gpu(index_q, index_pages, block_table, seq_lens)
+    if hist is None:
+        hist = torch.zeros((B, 2048), dtype=torch.int32, device=dev)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+    _need(hist.dtype == torch.int32 and hist.is_contiguous() and hist.numel() >= B * 2048, "hist must be int32 [B, 2048]")
+    _check(lib.mono_bench_scan(_ptr(index_q), _ptr(index_pages), index_pages.shape[0], _ptr(block_table),
+                               block_table.shape[1], _ptr(seq_lens), B, int(chunk_pages), int(variant), _ptr(hist),
+                               _ptr(err), _stream(dev)))
+    return hist, err
+
+
 # --- per-kernel timing ---------------------------------------------------------------
 
 
@@ -721,7 +746,7 @@ class KernelTimer:
         return self
 
     def __exit__(self, *exc):
-        n = 16
+        n = 64  # more than the library's kernel ids (mono_profile_stop returns how many it has)
         tot = (ctypes.c_double * n)()
         cnt = (ctypes.c_int * n)()
         rc = _lib.mono_profile_stop(tot, cnt, n)

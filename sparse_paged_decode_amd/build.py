@@ -13,7 +13,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmono_decode.so")
-SOURCES = ["plan.cpp", "pages.hip", "step.hip", "merge.hip", "bench_read.hip", "abi.hip"]
+SOURCES = ["plan.cpp", "pages.hip", "step.hip", "merge.hip", "bench_read.hip", "bench_scan.hip", "abi.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -29,7 +29,8 @@ const char* const kKernelNames[kNumKernels] = {
     "pack_kernel",          "unpack_kernel",         "dequant_f32_kernel",  "dequant_bf16_kernel",
     "index_topk_kernel",    "pa_decode_kernel",      "sparse_decode_kernel", "insert_kernel",
     "index_topk_fp8_kernel", "pa_decode_fp8_kernel", "sparse_decode_fp8_kernel", "dequant_fp8_bf16_kernel",
-    "topk_merge_kernel",    "read_stream_kernel",    "read_gather_kernel"};
+    "topk_merge_kernel",    "read_stream_kernel",    "read_gather_kernel", "scan_mfma_kernel",
+    "scan_valu_kernel"};
 }  // namespace
 
 bool prof_slot(int id, hipEvent_t* start, hipEvent_t* stop) {
@@ -410,6 +411,17 @@ int mono_profile_stop(double* total_ms, int* launches, int n_kernels) {
   g_prof.kid.clear();
   g_prof.used = 0;
   return rc == MONO_OK ? kNumKernels : rc;
+}
+
+int mono_bench_scan(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,
+                    const int32_t* block_table_dev, int bt_stride, const int32_t* seq_lens_dev, int B, int chunk_pages,
+                    int variant, uint32_t* hist_dev, uint32_t* err_dev, void* stream) {
+  clear_error();
+  if (int rc = check_bench_scan_call(index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride,
+                                     seq_lens_dev, B, chunk_pages, variant, hist_dev, err_dev))
+    return rc;
+  return launch_bench_scan(index_q_dev, index_pages_dev, num_pages, block_table_dev, bt_stride, seq_lens_dev, B,
+                           chunk_pages, variant, hist_dev, err_dev, (hipStream_t)stream);
 }
 
 const char* mono_kernel_name(int id) { return (id >= 0 && id < kNumKernels) ? kKernelNames[id] : ""; }

@@ -33,6 +33,8 @@ enum KernelId {
   kKTopkMerge,
   kKReadStream,
   kKReadGather,
+  kKScanMfma,
+  kKScanValu,
   kNumKernels
 };
 // When timing is on, takes the next pair of timing events for kernel `id`
@@ -66,6 +68,11 @@ int launch_topk_merge(const int32_t* cand_idx, const float* cand_scores, int G, 
 // index scan's lane pattern; grid workgroups, one word each to sink.
 int launch_read_reference(const uint8_t* pages, const int32_t* page_ids, int64_t n_pages, int mode, int grid,
                           uint32_t* sink, hipStream_t stream);
+// The index scan phase on the matrix cores (variant 0) or the VALU
+// (variant 1), for benchmarks (bench_scan.hip).
+int launch_bench_scan(const uint16_t* index_q, const uint8_t* pages, int64_t num_pages, const int32_t* block_table,
+                      int bt_stride, const int32_t* seq_lens, int B, int chunk_pages, int variant, uint32_t* hist,
+                      uint32_t* err, hipStream_t stream);
 // fp8 pages [n_pages, 16384] -> bf16 [n_pages, 128, 128] through the step kernel's conversion.
 int launch_dequant_fp8_bf16(const uint8_t* pages, uint16_t* out, int64_t n_pages, hipStream_t stream);
 // Cache insert: caches c = 0 (K), 1 (V), 2 (index key) with row_heads[c]

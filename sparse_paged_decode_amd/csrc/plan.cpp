@@ -390,4 +390,24 @@ int check_bench_read_call(const void* pages, const void* page_ids, int64_t n_pag
   return MONO_OK;
 }
 
+int check_bench_scan_call(const void* index_q, const void* pages, int64_t num_pages, const void* block_table,
+                          int bt_stride, const void* seq_lens, int B, int chunk_pages, int variant, const void* hist,
+                          const void* err) {
+  const char* what = "mono_bench_scan";
+  if (variant != 0 && variant != 1) return set_error(MONO_EINVAL, "%s: variant must be 0 or 1 (got %d)", what, variant);
+  if (B < 1 || B > (1 << 16)) return set_error(MONO_EINVAL, "%s: B must be in [1, 65536]", what);
+  if (bt_stride < 1 || bt_stride > kMaxBtStride) return set_error(MONO_EINVAL, "%s: bad bt_stride %d", what, bt_stride);
+  if (chunk_pages < 1 || chunk_pages * kPageTokens > kLocalTokens)
+    return set_error(MONO_EINVAL, "%s: chunk_pages must be in [1, %d]", what, kLocalTokens / kPageTokens);
+  if ((int64_t)B * ((bt_stride + chunk_pages - 1) / chunk_pages) > ((int64_t)1 << 30))
+    return set_error(MONO_EINVAL, "%s: too many workgroups", what);
+  if (num_pages < 1) return set_error(MONO_EINVAL, "%s: num_pages must be >= 1", what);
+  if (!index_q || !pages || !block_table || !seq_lens || !hist || !err)
+    return set_error(MONO_EINVAL, "%s: NULL buffer", what);
+  if (!aligned(index_q, 16) || !aligned(pages, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4) ||
+      !aligned(hist, 4) || !aligned(err, 4))
+    return set_error(MONO_EINVAL, "%s: index_q/pages need 16-byte, tables and outputs 4-byte alignment", what);
+  return MONO_OK;
+}
+
 }  // namespace mono

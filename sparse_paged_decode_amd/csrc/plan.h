@@ -166,5 +166,8 @@ int check_insert_call(const void* k_rows, const void* v_rows, const void* index_
                       int64_t num_pages, const void* err);
 int check_bench_read_call(const void* pages, const void* page_ids, int64_t n_pages, int mode, int grid,
                           const void* sink);
+int check_bench_scan_call(const void* index_q, const void* pages, int64_t num_pages, const void* block_table,
+                          int bt_stride, const void* seq_lens, int B, int chunk_pages, int variant, const void* hist,
+                          const void* err);
 
 }  // namespace mono

@@ -207,6 +207,16 @@ static void check_merge_insert_bench() {
   EXPECT_CODE(ins(ptr(0), ptr(1), ptr(2), 178956971, 1, ptr(3), ptr(4), ptr(5), 100, ptr(6)), MONO_EINVAL);
   EXPECT_CODE(ins(ptr(0), ptr(1), ptr(2), INT64_MAX / 2, 64, ptr(3), ptr(4), ptr(5), 100, ptr(6)), MONO_EINVAL);
 
+  auto scan = [&](int B, int bts, int cp, int variant, const void* hist = ptr(5)) {
+    return check_bench_scan_call(ptr(0), ptr(1), 100, ptr(2), bts, ptr(3), B, cp, variant, hist, ptr(6));
+  };
+  EXPECT_CODE(scan(64, 256, 32, 0), MONO_OK);
+  EXPECT_CODE(scan(64, 256, 32, 1), MONO_OK);
+  EXPECT_CODE(scan(64, 256, 33, 0), MONO_EINVAL);  // 33 pages exceed the LDS score area
+  EXPECT_CODE(scan(64, 256, 0, 0), MONO_EINVAL);
+  EXPECT_CODE(scan(64, 256, 32, 2), MONO_EINVAL);
+  EXPECT_CODE(scan(0, 256, 32, 0), MONO_EINVAL);
+  EXPECT_CODE(scan(64, 256, 32, 0, nullptr), MONO_EINVAL);
   EXPECT_CODE(check_bench_read_call(ptr(0), nullptr, 16, 0, 512, ptr(1)), MONO_OK);
   EXPECT_CODE(check_bench_read_call(ptr(0), ptr(2), 16, 1, 512, ptr(1)), MONO_OK);
   EXPECT_CODE(check_bench_read_call(ptr(0), nullptr, 16, 1, 512, ptr(1)), MONO_EINVAL);  // gather needs ids
