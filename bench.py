@@ -47,7 +47,7 @@ CSRC = os.path.join(ROOT, "sparse_paged_decode_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
 # Source files that define each kernel; their digest keys the stored counter data.
 _STEP_SOURCES = ["step.hip", "topk_device.h", "attn_device.h", "device_common.h", "block_ops.h", "launch.h",
-                 "page_format.h"]
+                 "page_format.h", "plan.h", "plan.cpp"]
 KERNEL_SOURCES = {
     "sparse_decode_kernel": _STEP_SOURCES,
     "index_topk_kernel": _STEP_SOURCES,
