@@ -446,7 +446,9 @@ int mono_bench_read(const uint8_t* pages_dev, const int32_t* page_ids_dev, int64
  * the query with the exactly dequantised token rows.
  *   variant 0: the step's scan (bf16 MFMA 16x16x32);
  *   variant 1: v_dot2_f32_bf16 on the VALU, two lanes per token row.
- * chunk_pages in [1, 32].  err_dev: MONO_DEVERR_PAGE_ID on a bad page id.
+ * chunk_pages in [1, 32].  err_dev: MONO_DEVERR_PAGE_ID on a bad page id,
+ * MONO_DEVERR_SEQ_LEN for a length outside [1, bt_stride*128] (that request
+ * is skipped).
  * MONO_EINVAL for bad sizes, variant or pointers.
  * ------------------------------------------------------------------------- */
 int mono_bench_scan(const uint16_t* index_q_dev, const uint8_t* index_pages_dev, int64_t num_pages,

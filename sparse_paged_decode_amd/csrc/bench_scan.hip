@@ -29,16 +29,23 @@ struct BenchScanLds {
 };
 
 // The pages of workgroup (b, c), or false when the request has none there.
-__device__ __forceinline__ bool bench_chunk(const int32_t* seq_lens, int B, int chunks, int chunk_pages, int& b,
-                                            int& L, int& p_begin, int& p_end) {
+// A length outside [1, bt_stride * 128] is flagged and the request skipped
+// (its pages would lie past its block-table row).
+__device__ __forceinline__ bool bench_chunk(const int32_t* seq_lens, int B, int bt_stride, int chunks,
+                                            int chunk_pages, uint32_t* err, int& b, int& L, int& p_begin,
+                                            int& p_end) {
   b = (int)blockIdx.x / chunks;
   const int c = (int)blockIdx.x % chunks;
   if (b >= B) return false;
   L = seq_lens[b];
+  if (L < 1 || L > bt_stride * kPageTokens) {
+    if (c == 0 && threadIdx.x == 0) raise_error(err, kErrSeqLen);
+    return false;
+  }
   const int n_pages = (L + kPageTokens - 1) / kPageTokens;
   p_begin = c * chunk_pages;
   p_end = min(p_begin + chunk_pages, n_pages);
-  return L >= 1 && p_begin < p_end;
+  return p_begin < p_end;
 }
 
 __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t* index_q, const uint8_t* pages,
@@ -47,7 +54,7 @@ __global__ __launch_bounds__(256) void scan_mfma_kernel(const uint16_t* index_q,
                                                         uint32_t* hist, uint32_t* err) {
   __shared__ BenchScanLds lds;
   int b, L, p_begin, p_end;
-  if (!bench_chunk(seq_lens, B, chunks, chunk_pages, b, L, p_begin, p_end)) return;
+  if (!bench_chunk(seq_lens, B, bt_stride, chunks, chunk_pages, err, b, L, p_begin, p_end)) return;
   ScanArgs sa;
   sa.index_q = index_q;
   sa.pages = pages;
@@ -73,7 +80,7 @@ __global__ __launch_bounds__(256) void scan_valu_kernel(const uint16_t* index_q,
                                                         uint32_t* hist, uint32_t* err) {
   __shared__ BenchScanLds lds;
   int b, L, p_begin, p_end;
-  if (!bench_chunk(seq_lens, B, chunks, chunk_pages, b, L, p_begin, p_end)) return;
+  if (!bench_chunk(seq_lens, B, bt_stride, chunks, chunk_pages, err, b, L, p_begin, p_end)) return;
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int half = lane & 1;            // elements 64 * half .. 64 * half + 63 of the row
   const int row = 32 * wave + (lane >> 1);

@@ -316,23 +316,32 @@ __device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, in
 // score row itself.
 enum : int { kSrcLds = 0, kSrcList = 1, kSrcScores = 2, kSrcLdsBits = 3 };
 
+// The float with key `key` (score_key's inverse on every key but NaN's 0).
+__device__ __forceinline__ float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 // The remaining k - above tokens, all in histogram bin B1 (which holds
-// in_bin tokens), by two more radix passes (key bits 20..10, then 9..0);
-// exact ties at the threshold go to the lowest token indices.  Slots
-// above..k-1 of the output are filled.  With kSrcLds or kSrcLdsBits the
-// candidates are in lds.cand[0..in_bin) already.
+// in_bin tokens), by radix passes over key bits 20..10, then 9..0; exact
+// ties at the threshold go to the lowest token indices.  Slots above..k-1
+// of the output are filled.  With kSrcLds or kSrcLdsBits the candidates are
+// in lds.cand[0..in_bin) already: each thread then holds its share of them
+// in registers for the first pass, the tokens above the pass's threshold
+// sub-bin get their slots from one prefix sum, and the sub-bin's own tokens
+// (rarely more than a few) are compacted to lds.cand and, when at most 256,
+// ranked against one another by (key descending, index ascending), which
+// picks the same tokens the last pass and the tie rule would.
 __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds, uint32_t B1, uint32_t above,
                                             uint32_t in_bin, int src) {
   const int tid = thread_index();
   const int n_valid = a.n_valid;
-  if (tid == 0) lds.cnt = above;
-  __syncthreads();
-
+  const bool lds_src = src == kSrcLds || src == kSrcLdsBits;
   const uint32_t R = (uint32_t)a.k - above;  // 1 <= R <= in_bin
-  const int n_src = src == kSrcScores ? n_valid : (int)in_bin;  // every source but the score row holds in_bin entries
+  // every source but the score row holds in_bin entries
+  int n_src = src == kSrcScores ? n_valid : (int)in_bin;
   // All three sources yield the same multiset of (key, j).
   auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
-    if (src == kSrcLds || src == kSrcLdsBits) {
+    if (lds_src) {
       const uint2 c = lds.cand[e];
       key = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
       j = (int)c.y;
@@ -348,24 +357,90 @@ __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds
     key = score_key(load_coherent(a.scores + e));
     return (key >> kHistShift) == B1;
   };
+  // The score written beside a token: its LDS bits, else the key's value
+  // (NaN's key 0 excepted, whose bits are read back).
+  auto score_of = [&](uint32_t key, uint32_t bits, int j) -> float {
+    if (!a.out_scores) return 0.f;
+    if (src == kSrcLdsBits) return __uint_as_float(bits);
+    return (lds_src && key != 0u) ? key_value(key) : load_coherent(a.scores + j);
+  };
   auto emit = [&](int j) {
     put_selection(a, atomicAdd(&lds.cnt, 1u), j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
   };
+  if (!lds_src && tid == 0) lds.cnt = above;
+  __syncthreads();  // the caller's LDS candidates are written
 
   // pass 2: key bits 20..10
-  for (int x = tid; x < kHistBins; x += kBlock) lds.hist[x] = 0u;
-  __syncthreads();
-  for (int e = tid; e < n_src; e += kBlock) {
-    uint32_t key;
-    int j;
-    if (fetch(e, key, j)) atomicAdd(&lds.hist[(key >> 10) & 0x7FFu], 1u);
-  }
-  __syncthreads();
-  const BinSplit s2 = find_bin_of_rank(lds.hist, kHistBins, R, lds.scratch);
-  for (int e = tid; e < n_src; e += kBlock) {
-    uint32_t key;
-    int j;
-    if (fetch(e, key, j) && ((key >> 10) & 0x7FFu) > (uint32_t)s2.bin) emit(j);
+  BinSplit s2;
+  if (lds_src) {
+    constexpr int kPer = kLdsCand / kBlock;
+    uint32_t kx[kPer], bx[kPer], jx[kPer];
+    uint32_t valid = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int e = u * kBlock + tid;
+      const uint2 c = lds.cand[min(e, kLdsCand - 1)];
+      bx[u] = c.x;
+      jx[u] = c.y;
+      kx[u] = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
+      valid |= e < (int)in_bin ? (1u << u) : 0u;
+    }
+    for (int x = tid; x < kHistBins; x += kBlock) lds.hist[x] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (valid & (1u << u)) atomicAdd(&lds.hist[(kx[u] >> 10) & 0x7FFu], 1u);
+    __syncthreads();
+    s2 = find_bin_of_rank(lds.hist, kHistBins, R, lds.scratch);
+    uint32_t hi = 0, eq = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t sub = (kx[u] >> 10) & 0x7FFu;
+      hi |= ((valid >> u) & 1u) && sub > (uint32_t)s2.bin ? (1u << u) : 0u;
+      eq |= ((valid >> u) & 1u) && sub == (uint32_t)s2.bin ? (1u << u) : 0u;
+    }
+    // both counts are at most kLdsCand: one packed 16+16-bit prefix sum
+    uint32_t tot;
+    const uint32_t before = block_exclusive_scan(__popc(hi) | (__popc(eq) << 16), lds.scratch, tot);
+    uint32_t slot = above + (before & 0xFFFFu), cs = before >> 16;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (hi & (1u << u)) put_selection(a, slot++, (int)jx[u], score_of(kx[u], bx[u], (int)jx[u]));
+      if (eq & (1u << u)) lds.cand[cs++] = make_uint2(bx[u], jx[u]);
+    }
+    if (tid == 0) lds.cnt = above + s2.above;
+    __syncthreads();
+    const uint32_t n_surv = s2.count, R2 = R - s2.above;
+    if (n_surv <= (uint32_t)kBlock) {
+      if (tid < (int)n_surv) {
+        const uint2 me = lds.cand[tid];
+        const uint32_t mk = src == kSrcLds ? me.x : score_key(__uint_as_float(me.x));
+        uint32_t rank = 0;
+        for (uint32_t o = 0; o < n_surv; ++o) {
+          const uint2 c = lds.cand[o];
+          const uint32_t ok = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
+          rank += (ok > mk || (ok == mk && c.y < me.y)) ? 1u : 0u;
+        }
+        if (rank < R2) put_selection(a, above + s2.above + rank, (int)me.y, score_of(mk, me.x, (int)me.y));
+      }
+      return;
+    }
+    n_src = (int)n_surv;  // the last pass reads the compacted sub-bin
+  } else {
+    for (int x = tid; x < kHistBins; x += kBlock) lds.hist[x] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n_src; e += kBlock) {
+      uint32_t key;
+      int j;
+      if (fetch(e, key, j)) atomicAdd(&lds.hist[(key >> 10) & 0x7FFu], 1u);
+    }
+    __syncthreads();
+    s2 = find_bin_of_rank(lds.hist, kHistBins, R, lds.scratch);
+    for (int e = tid; e < n_src; e += kBlock) {
+      uint32_t key;
+      int j;
+      if (fetch(e, key, j) && ((key >> 10) & 0x7FFu) > (uint32_t)s2.bin) emit(j);
+    }
   }
   const uint32_t R2 = R - s2.above;
   const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;  // key >> 10 of the survivors
@@ -507,7 +582,6 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
   // is +0 (B1 is 1023 or 1024), when B1 is below bin 4, or when B1 + 1
   // would be past +inf's bin.
   const bool fcmp = B1 >= 4u && B1 != 1023u && B1 != 1024u && B1 <= 2043u;
-  auto key_value = [](uint32_t key) { return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key); };
   const float f_lo = key_value(B1 << kHistShift), f_hi = key_value((B1 + 1u) << kHistShift);
   uint32_t mine = 0;
   for (int b0 = 0; b0 < nb; b0 += kSelAhead + 1) {

@@ -105,6 +105,25 @@ def test_topk_many_ties_in_candidate_list(spd):
     assert sorted(sel[0].tolist()) == sorted(ref.tolist())  # lowest-index tie-break, exactly
 
 
+@pytest.mark.parametrize("L,W,k", [(3000, 24, 776), (60000, 470, 2048)], ids=["select_row", "slice_rows"])
+def test_topk_exact_ties_few_per_value(spd, L, W, k):
+    """512 distinct score values (v0 + v1/16 + v2/256 over e2m1 magnitudes),
+    each held by a few to a hundred tokens: the last radix level ends in a
+    small bin of exact ties, which goes to the lowest indices."""
+    w = make_workload("ties512", B=1, T=1, seq_lens=[L], bt_width=W, k=k, seed=7)
+    rng = np.random.default_rng(1)
+    codes = np.zeros((w.num_pages, 128, 128), dtype=np.uint8)
+    codes[:, :, 0:3] = rng.integers(0, 8, size=(w.num_pages, 128, 3))
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+    w.index_q[:, :] = 0
+    w.index_q[:, 0:3] = mxfp4.round_to_bf16_bits(np.array([1.0, 1.0 / 16, 1.0 / 256]))
+    sel, scores = _run(spd, w, k)
+    s = decode.index_scores(w.index_q[0], w.index_pool, w.block_table[0], L - 1)
+    ref = decode.topk(s, k)
+    assert sorted(sel[0].tolist()) == sorted(ref.tolist())  # lowest-index tie-break, exactly
+    assert np.array_equal(scores[0], s[sel[0]])  # every sum is exact in fp32
+
+
 def test_topk_repeat_calls_deterministic(spd):
     w = make_workload("rep", B=3, T=2, seq_lens=[3000, 5000, 4100], bt_width=40, k=512, seed=8)
     a, _ = _run(spd, w, 512)
