@@ -542,7 +542,7 @@ def main():
 
     # The same steps replayed from HIP graphs (one captured step per pool
     # copy), timed like the plain launches.
-    graph_ms = None
+    graph_ms = graph_multi_ms = None
     if not args.skip_graph:
         graphs = []
         for c in range(copies):
@@ -560,6 +560,22 @@ def main():
         ge[1].record(stream)
         torch.cuda.synchronize(dev)
         graph_ms = ge[0].elapsed_time(ge[1]) / K
+        # One graph holding one step per pool copy, replayed K / copies
+        # times: the graph launch's own cost spread over several steps.
+        gall = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gall):
+            for c in range(copies):
+                step(c)
+        reps = max(1, K // copies)
+        for _ in range(max(1, args.warmup // copies)):
+            gall.replay()
+        torch.cuda.synchronize(dev)
+        ge[0].record(stream)
+        for _ in range(reps):
+            gall.replay()
+        ge[1].record(stream)
+        torch.cuda.synchronize(dev)
+        graph_multi_ms = ge[0].elapsed_time(ge[1]) / (reps * copies)
 
     # Device error bits raised by any of the steps above (a bounded wait
     # that ran out, a bad page id or length): zero in a valid run.
@@ -634,6 +650,8 @@ def main():
         "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
         "step_us_p90": round(float(np.percentile(step_ms, 90)) * 1e3, 2),
         "graph_step_us": round(graph_ms * 1e3, 2) if graph_ms is not None else None,
+        "graph_step_us_steps_per_graph": {"1": round(graph_ms * 1e3, 2), str(copies): round(graph_multi_ms * 1e3, 2)}
+        if graph_ms is not None else None,
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "bytes_per_step": {"index": idx_bytes, "kv": kv_bytes},
         "kernels_us_mean": {name: round(us, 2) for name, us in kt.mean_us.items()},
