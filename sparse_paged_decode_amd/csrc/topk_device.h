@@ -217,6 +217,9 @@ struct ResolveLds {
   uint32_t cnt;
   uint16_t marks[kSelBatchesMax][kBlock];  // select_query: tokens above the threshold bin
 };
+// pick_in_bin stages positions in hist and cand seen as one word array.
+static_assert(offsetof(ResolveLds, hist) == 0 && offsetof(ResolveLds, cand) == sizeof(uint32_t) * kHistBins,
+              "hist and cand are contiguous");
 
 struct SelectArgs {
   const float* scores;  // the query token's scores (coherent), lcap floats
@@ -327,10 +330,12 @@ __device__ __forceinline__ float key_value(uint32_t key) {
 // of the output are filled.  With kSrcLds or kSrcLdsBits the candidates are
 // in lds.cand[0..in_bin) already: each thread then holds its share of them
 // in registers for the first pass, the tokens above the pass's threshold
-// sub-bin get their slots from one prefix sum, and the sub-bin's own tokens
-// (rarely more than a few) are compacted to lds.cand and, when at most 256,
-// ranked against one another by (key descending, index ascending), which
-// picks the same tokens the last pass and the tie rule would.
+// sub-bin get their slots from one prefix sum (their positions are staged
+// in LDS and written to consecutive slots by consecutive lanes, unless
+// scores are written too), and the sub-bin's own tokens (rarely more than a
+// few) are compacted to the end of lds.cand and, when at most 256, ranked
+// against one another by (key descending, index ascending), which picks
+// the same tokens the last pass and the tie rule would.
 __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds, uint32_t B1, uint32_t above,
                                             uint32_t in_bin, int src) {
   const int tid = thread_index();
@@ -339,10 +344,11 @@ __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds
   const uint32_t R = (uint32_t)a.k - above;  // 1 <= R <= in_bin
   // every source but the score row holds in_bin entries
   int n_src = src == kSrcScores ? n_valid : (int)in_bin;
+  int cbase = 0;  // first LDS candidate of the current pass
   // All three sources yield the same multiset of (key, j).
   auto fetch = [&](int e, uint32_t& key, int& j) -> bool {
     if (lds_src) {
-      const uint2 c = lds.cand[e];
+      const uint2 c = lds.cand[cbase + e];
       key = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
       j = (int)c.y;
       return true;
@@ -402,22 +408,37 @@ __device__ __forceinline__ void pick_in_bin(const SelectArgs& a, ResolveLds& lds
     // both counts are at most kLdsCand: one packed 16+16-bit prefix sum
     uint32_t tot;
     const uint32_t before = block_exclusive_scan(__popc(hi) | (__popc(eq) << 16), lds.scratch, tot);
-    uint32_t slot = above + (before & 0xFFFFu), cs = before >> 16;
+    const uint32_t n_surv = s2.count, R2 = R - s2.above;
+    // Survivors go to the end of lds.cand; the staged positions fill words
+    // 0..s2.above-1 of hist + cand, below them (s2.above + n_surv <= in_bin).
+    cbase = kLdsCand - (int)n_surv;
+    uint32_t* stage = reinterpret_cast<uint32_t*>(&lds);
+    const bool staged = a.out_scores == nullptr;
+    uint32_t slot = before & 0xFFFFu, cs = (uint32_t)cbase + (before >> 16);
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
-      if (hi & (1u << u)) put_selection(a, slot++, (int)jx[u], score_of(kx[u], bx[u], (int)jx[u]));
+      if (hi & (1u << u)) {
+        if (staged) {
+          stage[slot] = jx[u];
+        } else {
+          put_selection(a, above + slot, (int)jx[u], score_of(kx[u], bx[u], (int)jx[u]));
+        }
+        ++slot;
+      }
       if (eq & (1u << u)) lds.cand[cs++] = make_uint2(bx[u], jx[u]);
     }
     if (tid == 0) lds.cnt = above + s2.above;
     __syncthreads();
-    const uint32_t n_surv = s2.count, R2 = R - s2.above;
+    if (staged) {
+      for (uint32_t q = tid; q < s2.above; q += kBlock) put_selection(a, above + q, (int)stage[q], 0.f);
+    }
     if (n_surv <= (uint32_t)kBlock) {
       if (tid < (int)n_surv) {
-        const uint2 me = lds.cand[tid];
+        const uint2 me = lds.cand[cbase + tid];
         const uint32_t mk = src == kSrcLds ? me.x : score_key(__uint_as_float(me.x));
         uint32_t rank = 0;
         for (uint32_t o = 0; o < n_surv; ++o) {
-          const uint2 c = lds.cand[o];
+          const uint2 c = lds.cand[cbase + o];
           const uint32_t ok = src == kSrcLds ? c.x : score_key(__uint_as_float(c.x));
           rank += (ok > mk || (ok == mk && c.y < me.y)) ? 1u : 0u;
         }
@@ -647,7 +668,20 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
       }
     }
   };
-  if (a.out_scores) {
+  if (!a.out_scores && n_hi <= (uint32_t)kHistBins) {
+    // Positions staged in the histogram's LDS (free until pick_in_bin),
+    // then written to consecutive slots by consecutive lanes.
+    for (int b = 0; b < nb; ++b) {
+      uint32_t bits = lds.marks[b][tid];
+      while (bits) {
+        const int u = __builtin_ctz(bits);
+        bits &= bits - 1u;
+        lds.hist[slot++] = (uint32_t)(b * kSelBatch + tid * kSelPer + u);
+      }
+    }
+    __syncthreads();
+    for (uint32_t q = tid; q < n_hi; q += kBlock) put_selection(a, q, (int)lds.hist[q], 0.f);
+  } else if (a.out_scores) {
     write_marked(std::true_type{});
   } else {
     write_marked(std::false_type{});
