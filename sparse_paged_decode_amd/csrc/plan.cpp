@@ -164,11 +164,14 @@ long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_s
   if (lay.mode & kModeAttn) {
     // Attention splits as large as it takes to make about one round of the
     // resident workgroups (never smaller than the layout's, whose partial
-    // buffers are sized for the most splits).
+    // buffers are sized for the most splits).  In the one-launch step the
+    // splits are published as selections finish, so two rounds' worth lets
+    // the workgroups that are free by then share the last tokens' attention.
     const size_t NH = (size_t)lay.B * lay.T * lay.H;
     const long list_max = lay.sparse ? (long)lay.k : (long)lay.lcap;
     int split = lay.split_tokens;
-    while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > (size_t)cap) split *= 2;
+    const size_t acap = (size_t)cap * (lay.mode == kModeFused ? kFusedAttnRounds : 1);
+    while (split < kMaxSplitTokens && NH * (size_t)((list_max + split - 1) / split) > acap) split *= 2;
     lay.split_tokens = split;
     lay.n_splits = (int)((list_max + split - 1) / split);
     lay.n_attn = (uint32_t)(NH * lay.n_splits);

@@ -43,6 +43,7 @@ constexpr int kSelectMax = 65536;    // longest score row a single workgroup sel
 constexpr size_t kClearBytes = 32768;  // bytes zeroed by one clear item
 constexpr int kMinSplitTokens = 256;   // attention candidates per split: one pass of 4 waves x 4 groups of 16
 constexpr int kMaxSplitTokens = 8192;
+constexpr int kFusedAttnRounds = 2;   // attention splits of the one-launch step: up to 2 rounds of workgroups
 // Chunk-local step: scores a scan item keeps in LDS (32 pages), and chunks
 // per request (its attention splits).
 constexpr int kLocalTokens = 4096;

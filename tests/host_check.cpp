@@ -321,13 +321,20 @@ static void check_plans() {
     l = step_layout(kModeFused, 128, 4, 1, 512, 2048, 1);
     plan_step(l, mi, false, false, &variant, "t4");
     CHECK(l.local == 0 && variant == step_variant(true, false));
+    // 512 query tokens: two splits of 1024 each (two rounds of workgroups),
+    // within the 8 splits the partial buffers hold.
+    CHECK(l.split_tokens == 1024 && l.n_splits == 2 && l.n_attn == 1024u && l.n_splits <= l.part_splits);
+    // The attention call alone keeps one round: one split per query token.
+    l = step_layout(kModeAttn, 128, 4, 1, 512, 2048, 1);
+    plan_step(l, mi, false, false, &variant, "t4-attn");
+    CHECK(l.n_splits == 1 && l.n_attn == 512u);
   }
   // Long rows (8 x 262144 tokens): a chunk would exceed the LDS score area.
   {
     StepLayout l = step_layout(kModeFused, 8, 1, 1, 2048, 4096, 1);
     int variant = -1;
     plan_step(l, mi, false, false, &variant, "long");
-    CHECK(l.local == 0);
+    CHECK(l.local == 0 && l.split_tokens == 256 && l.n_splits == 16);
   }
   // Dense attention, batch 32 x 8192 tokens: the attention-only instance,
   // one split of 512 tokens per resident workgroup.
