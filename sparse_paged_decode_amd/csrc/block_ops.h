@@ -10,14 +10,30 @@ namespace mono {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-// Inclusive prefix sum within a 64-lane wave.
+// DPP controls (GFX9 encoding): shift right by n lanes within each row of
+// 16, and broadcast lane 15 / lane 31 to the rows the row mask enables.
+constexpr int kDppRowShr = 0x110;
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+
+// x of the lane the DPP control selects, or 0 where the source lane lies
+// outside the row or the row mask leaves the lane's row out.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xf, false);
+}
+
+// Inclusive prefix sum within a 64-lane wave, on DPP moves (no LDS round
+// trips): a Hillis-Steele sum within each row of 16 lanes, then row 0's
+// total added to row 1 and row 2's to row 3, then the first half's total
+// to rows 2 and 3.  Every lane of the wave must be active.
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
-  const int lane = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(v, off);
-    if (lane >= off) v += o;
-  }
+  v += dpp_or_zero<kDppRowShr | 1, 0xf>(v);
+  v += dpp_or_zero<kDppRowShr | 2, 0xf>(v);
+  v += dpp_or_zero<kDppRowShr | 4, 0xf>(v);
+  v += dpp_or_zero<kDppRowShr | 8, 0xf>(v);
+  v += dpp_or_zero<kDppRowBcast15, 0xa>(v);
+  v += dpp_or_zero<kDppRowBcast31, 0xc>(v);
   return v;
 }
 
@@ -55,6 +71,8 @@ __device__ __forceinline__ uint32_t wave_append(bool pred, uint32_t* counter) {
   return base + (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
 }
 
+constexpr int kMaxBinsPerThread = 8;  // find_bin_of_rank: histograms of up to 2048 bins
+
 struct BinSplit {
   int bin;         // bin holding the R-th largest element
   uint32_t above;  // elements in bins above it (< R)
@@ -72,24 +90,38 @@ __device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int n
     scratch[kWaves + 1] = 0u;
     scratch[kWaves + 2] = 0u;
   }
-  const int per = nbins / kBlock;
-  // thread t owns the t-th group of `per` bins counted from the top
+  const int per = nbins / kBlock;  // at most kMaxBinsPerThread
+  // thread t owns the t-th group of `per` bins counted from the top; its
+  // counts stay in registers for the search
   const int hi = nbins - 1 - thread_index() * per;
+  uint32_t h[kMaxBinsPerThread];
   uint32_t sum = 0;
-  for (int q = 0; q < per; ++q) sum += hist[hi - q];
+#pragma unroll
+  for (int q = 0; q < kMaxBinsPerThread; ++q) {
+    h[q] = q < per ? hist[hi - q] : 0u;
+    sum += h[q];
+  }
   uint32_t total;
   uint32_t above = block_exclusive_scan(sum, scratch, total);
   if (above < R && R <= above + sum) {
-    for (int q = 0; q < per; ++q) {
-      const uint32_t c = hist[hi - q];
-      if (above + c >= R) {
-        scratch[kWaves] = (uint32_t)(hi - q);
-        scratch[kWaves + 1] = above;
-        scratch[kWaves + 2] = c;
-        break;
+    int found = 0;
+    uint32_t f_above = above, f_count = h[0];
+#pragma unroll
+    for (int q = kMaxBinsPerThread - 1; q >= 0; --q) {
+      // bin q of the group holds the R-th largest when the bins before it
+      // stay below R and it reaches R: exactly one q does
+      uint32_t before = above;
+#pragma unroll
+      for (int p = 0; p < q; ++p) before += h[p];
+      if (q < per && before < R && before + h[q] >= R) {
+        found = q;
+        f_above = before;
+        f_count = h[q];
       }
-      above += c;
     }
+    scratch[kWaves] = (uint32_t)(hi - found);
+    scratch[kWaves + 1] = f_above;
+    scratch[kWaves + 2] = f_count;
   }
   __syncthreads();
   BinSplit r;
