@@ -79,28 +79,19 @@ struct BinSplit {
   uint32_t count;  // elements in that bin (above + count >= R)
 };
 
-// hist: __shared__ counts of `nbins` bins (nbins a multiple of 256, bins
-// ordered by increasing key).  Finds the bin that holds the R-th largest
-// element (1 <= R <= total count).  Every thread gets the result.
-// `scratch` is __shared__ uint32_t[kWaves + 3].
-__device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int nbins, uint32_t R,
-                                                     uint32_t* scratch) {
+// The split for per-thread bin counts in registers: thread t holds the
+// counts of bins hi, hi - 1, ..., hi - per + 1 in h[0..per), where
+// hi = nbins - 1 - t * per (groups of `per` bins counted from the top).
+__device__ __forceinline__ BinSplit bin_of_rank_in_regs(const uint32_t (&h)[kMaxBinsPerThread], int per, int hi,
+                                                        uint32_t R, uint32_t* scratch) {
   if (thread_index() == 0) {  // defined result even if R exceeded the count
     scratch[kWaves] = 0u;
     scratch[kWaves + 1] = 0u;
     scratch[kWaves + 2] = 0u;
   }
-  const int per = nbins / kBlock;  // at most kMaxBinsPerThread
-  // thread t owns the t-th group of `per` bins counted from the top; its
-  // counts stay in registers for the search
-  const int hi = nbins - 1 - thread_index() * per;
-  uint32_t h[kMaxBinsPerThread];
   uint32_t sum = 0;
 #pragma unroll
-  for (int q = 0; q < kMaxBinsPerThread; ++q) {
-    h[q] = q < per ? hist[hi - q] : 0u;
-    sum += h[q];
-  }
+  for (int q = 0; q < kMaxBinsPerThread; ++q) sum += q < per ? h[q] : 0u;
   uint32_t total;
   uint32_t above = block_exclusive_scan(sum, scratch, total);
   if (above < R && R <= above + sum) {
@@ -130,6 +121,42 @@ __device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int n
   r.count = scratch[kWaves + 2];
   __syncthreads();
   return r;
+}
+
+// hist: __shared__ counts of `nbins` bins (nbins a multiple of 256, at most
+// 2048, bins ordered by increasing key).  Finds the bin that holds the R-th
+// largest element (1 <= R <= total count).  Every thread gets the result.
+// `scratch` is __shared__ uint32_t[kWaves + 3].
+__device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int nbins, uint32_t R,
+                                                     uint32_t* scratch) {
+  const int per = nbins / kBlock;
+  const int hi = nbins - 1 - thread_index() * per;
+  uint32_t h[kMaxBinsPerThread];
+#pragma unroll
+  for (int q = 0; q < kMaxBinsPerThread; ++q) h[q] = q < per ? hist[hi - q] : 0u;
+  return bin_of_rank_in_regs(h, per, hi, R, scratch);
+}
+
+// The same over a histogram row in global memory that other workgroups
+// completed (nbins 1024 or 2048): each thread reads its own group of bins
+// with 16-byte coherent loads, straight into registers.
+template <int kBins>
+__device__ __forceinline__ BinSplit find_bin_of_rank_global(const uint32_t* g, uint32_t R, uint32_t* scratch) {
+  static_assert(kBins == 1024 || kBins == 2048, "four or eight bins per thread");
+  constexpr int per = kBins / kBlock;
+  const int hi = kBins - 1 - thread_index() * per;
+  const int lo = hi - per + 1;
+  const __amdgpu_buffer_rsrc_t rsrc = buffer_rsrc(g, (uint32_t)kBins * 4u);
+  u32x4_t v[per / 4];
+#pragma unroll
+  for (int i = 0; i < per / 4; ++i) v[i] = load_coherent_x4(rsrc, (uint32_t)(lo + 4 * i) * 4u);
+  uint32_t h[kMaxBinsPerThread];
+#pragma unroll
+  for (int q = 0; q < kMaxBinsPerThread; ++q) {
+    const int x = per - 1 - q;  // bin hi - q is element x of the group
+    h[q] = q < per ? v[x >> 2][x & 3] : 0u;
+  }
+  return bin_of_rank_in_regs(h, per, hi, R, scratch);
 }
 
 }  // namespace mono

@@ -133,6 +133,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ void store_coherent_x4(__amdgpu_buffer_rsrc_t r, uint32_t offset, u32x4_t v) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)offset, 0, kPolicyAgentCoherent);
 }
+// 16 bytes per lane read with the same agent-scope coherence as
+// load_coherent (the sc1 policy); offsets past the resource read zero.
+__device__ __forceinline__ u32x4_t load_coherent_x4(__amdgpu_buffer_rsrc_t r, uint32_t offset) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)offset, 0, kPolicyAgentCoherent);
+}
 // Wait until this thread's outstanding vector memory operations (loads,
 // stores, atomics) have completed; also a compiler memory barrier.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

@@ -214,20 +214,6 @@ __device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint
   __syncthreads();
 }
 
-// The bin of the R-th largest key in a global histogram row of nbins (<= 2048) bins.
-__device__ __forceinline__ BinSplit global_rank_bin(const uint32_t* g, int nbins, uint32_t R, uint32_t* hist,
-                                                    uint32_t* scratch) {
-  const int tid = thread_index();
-  uint32_t h[kHistBins / kBlock];
-#pragma unroll
-  for (int u = 0; u < kHistBins / kBlock; ++u) h[u] = u * kBlock < nbins ? load_coherent(g + u * kBlock + tid) : 0u;
-#pragma unroll
-  for (int u = 0; u < kHistBins / kBlock; ++u)
-    if (u * kBlock < nbins) hist[u * kBlock + tid] = h[u];
-  __syncthreads();
-  return find_bin_of_rank(hist, nbins, R, scratch);
-}
-
 // Adds the digits (key >> shift) & (nbins - 1) of this thread's keys marked
 // in `mask` to global histogram row g, through an LDS histogram.
 __device__ __forceinline__ void level_counts(const uint32_t* key, uint32_t mask, int shift, int nbins, uint32_t* hist,
@@ -319,7 +305,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   bool ties = false;
   if (!all) {
     arrive_wait(lvl + 0, (uint32_t)nch, err);
-    const BinSplit s1 = global_rank_bin(g1, kHistBins, (uint32_t)k, hist, lds.scratch);
+    const BinSplit s1 = find_bin_of_rank_global<kHistBins>(g1, (uint32_t)k, lds.scratch);
     uint32_t R = (uint32_t)k - s1.above;
     const uint32_t B1 = (uint32_t)s1.bin;
     thr = B1 << kHistShift;
@@ -424,7 +410,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       for (int u = 0; u < 16; ++u) m2 |= ((key[u] >> kHistShift) == B1) ? (1u << u) : 0u;
       level_counts(key, m2 & valid, 10, kHistBins, hist, g2);
       arrive_wait(lvl + 1, (uint32_t)nch, err);
-      const BinSplit s2 = global_rank_bin(g2, kHistBins, R, hist, lds.scratch);
+      const BinSplit s2 = find_bin_of_rank_global<kHistBins>(g2, R, lds.scratch);
       R -= s2.above;
       const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;
       thr = pre2 << 10;
@@ -434,7 +420,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
         for (int u = 0; u < 16; ++u) m3 |= ((key[u] >> 10) == pre2) ? (1u << u) : 0u;
         level_counts(key, m3 & valid, 0, 1024, hist, g3);
         arrive_wait(lvl + 2, (uint32_t)nch, err);
-        const BinSplit s3 = global_rank_bin(g3, 1024, R, hist, lds.scratch);
+        const BinSplit s3 = find_bin_of_rank_global<1024>(g3, R, lds.scratch);
         R -= s3.above;
         thr = (pre2 << 10) | (uint32_t)s3.bin;
         if (s3.count != R) {

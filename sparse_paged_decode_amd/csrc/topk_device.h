@@ -246,16 +246,10 @@ __device__ __forceinline__ void put_selection(const SelectArgs& a, uint32_t slot
   if (a.out_scores) store_coherent(a.out_scores + slot, score);
 }
 
-// Loads a histogram row into LDS and finds the bin of the k-th largest score.
-__device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* hist, uint32_t* scratch) {
-  const int tid = thread_index();
-  uint32_t h[kHistBins / kBlock];
-#pragma unroll
-  for (int u = 0; u < kHistBins / kBlock; ++u) h[u] = load_coherent(a.ghist + u * kBlock + tid);
-#pragma unroll
-  for (int u = 0; u < kHistBins / kBlock; ++u) hist[u * kBlock + tid] = h[u];
-  __syncthreads();
-  return find_bin_of_rank(hist, kHistBins, (uint32_t)a.k, scratch);
+// Finds the bin of the k-th largest score in the query token's (complete)
+// histogram row.
+__device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* scratch) {
+  return find_bin_of_rank_global<kHistBins>(a.ghist, (uint32_t)a.k, scratch);
 }
 
 // Slice [j0, j1) of the scores.  Returns the histogram split it used (the
@@ -279,7 +273,7 @@ __device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, in
   float v[kPer];
 #pragma unroll
   for (int u = 0; u < kPer; ++u) v[u] = load_coherent(a.scores + min(j0 + u * kBlock + tid, a.lcap - 1));
-  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  const BinSplit sp = kth_bin(a, lds.scratch);
   const uint32_t B1 = (uint32_t)sp.bin;
   const bool use_cand = sp.count <= (uint32_t)kCandCap;
 
@@ -527,7 +521,7 @@ __device__ __forceinline__ void resolve_query(const SelectArgs& a, ResolveLds& l
 #pragma unroll
     for (int u = 0; u < kPer; ++u) c[u] = load_coherent(a.cand + u * kBlock + tid);
   }
-  const BinSplit sp = have_known ? known : kth_bin(a, lds.hist, lds.scratch);
+  const BinSplit sp = have_known ? known : kth_bin(a, lds.scratch);
   on_final(resolve ? sp.above : (uint32_t)a.k);
   for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
   if (!resolve) return;  // the filter items wrote everything
@@ -587,7 +581,7 @@ __device__ __forceinline__ void select_query(const SelectArgs& a, ResolveLds& ld
 #pragma unroll
   for (int b = 0; b < kSelAhead; ++b) load_batch(v[b], b);
   if (tid == 0) lds.cnt = 0u;  // candidate count while streaming
-  const BinSplit sp = kth_bin(a, lds.hist, lds.scratch);
+  const BinSplit sp = kth_bin(a, lds.scratch);
   for (int x = tid; x < kHistBins; x += kBlock) a.ghist[x] = 0u;
   const uint32_t B1 = (uint32_t)sp.bin, above = sp.above, in_bin = sp.count;
   const bool in_lds = in_bin <= (uint32_t)kLdsCand;
