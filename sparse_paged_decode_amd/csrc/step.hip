@@ -375,16 +375,61 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       }
       const int n_c = (int)min(lds.xpre[nch], (uint32_t)kExchCap);
       if (lds.xpre[nch] != s1.count && tid == 0) raise_error(err, kErrSelection);  // never expected
-      // Radix passes over key bits 20..10, then 9..0, among the candidates.
+      // A radix pass over key bits 20..10 among the candidates (each
+      // thread's share held in registers), then the rest within the
+      // threshold sub-bin.
       for (int x = tid; x < kHistBins; x += kBlock) hist[x] = 0u;
-      __syncthreads();
-      for (int e = tid; e < n_c; e += kBlock) atomicAdd(&hist[(cand[e].x >> 10) & 0x7FFu], 1u);
+      if (tid == 0) lds.scratch[kWaves + 3] = 0u;  // survivor count
+      __syncthreads();  // and every candidate is in LDS
+      uint32_t ck[kPer];
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) ck[q] = q * kBlock + tid < n_c ? cand[q * kBlock + tid].x : 0u;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q)
+        if (q * kBlock + tid < n_c) atomicAdd(&hist[(ck[q] >> 10) & 0x7FFu], 1u);
       __syncthreads();
       const BinSplit s2 = find_bin_of_rank(hist, kHistBins, R, lds.scratch);
       R -= s2.above;
       const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;
       thr = pre2 << 10;
-      if (s2.count != R) {
+      if (s2.count != R && s2.count <= (uint32_t)kBlock) {
+        // The sub-bin's keys (a few, as a rule) are compacted into the free
+        // histogram words; the one whose count of larger keys is below R
+        // and reaches R with its equals is the R-th largest.
+        uint32_t* skey = hist;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q)
+          if (q * kBlock + tid < n_c && (ck[q] >> 10) == pre2) skey[atomicAdd(&lds.scratch[kWaves + 3], 1u)] = ck[q];
+        __syncthreads();
+        const uint32_t n_surv = s2.count;
+        if (tid < (int)n_surv) {
+          const uint32_t mk = skey[tid];
+          uint32_t gt = 0, eq = 0;
+          for (uint32_t o = 0; o < n_surv; ++o) {
+            const uint32_t ok = skey[o];
+            gt += ok > mk ? 1u : 0u;
+            eq += ok == mk ? 1u : 0u;
+          }
+          if (gt < R && R <= gt + eq) {  // every such thread holds the same key: same values
+            lds.scratch[kWaves] = mk;
+            lds.scratch[kWaves + 1] = gt;
+            lds.scratch[kWaves + 2] = eq;
+          }
+        }
+        __syncthreads();
+        thr = lds.scratch[kWaves];
+        R -= lds.scratch[kWaves + 1];
+        if (lds.scratch[kWaves + 2] != R) {
+          // More tokens with key thr than places: the lowest positions
+          // first; `before` counts those of the chunks ahead of this one.
+          uint32_t mine = 0;
+          for (int e = tid; e < n_c; e += kBlock) mine += (cand[e].x == thr && (int)cand[e].y < tok0) ? 1u : 0u;
+          uint32_t before;
+          block_exclusive_scan(mine, lds.scratch, before);
+          take = R > before ? R - before : 0u;
+          ties = true;
+        }
+      } else if (s2.count != R) {
         for (int x = tid; x < 1024; x += kBlock) hist[x] = 0u;
         __syncthreads();
         for (int e = tid; e < n_c; e += kBlock)

@@ -254,6 +254,33 @@ def test_step_one_token_exact_ties_at_threshold(spd):
             _check_token(w, i, sel_np[i], out_bits)
 
 
+def test_step_one_token_small_tie_groups(spd):
+    """512 distinct score values (v0 + v1/16 + v2/256 over e2m1 magnitudes),
+    a few to a few dozen tokens each: the exchanged threshold bin ends in a
+    small sub-bin of exact ties, split between selected and not (3 -> 1,
+    18 -> 17, 19 -> 11 places), which goes to the lowest positions."""
+    w = make_workload("ties512step", B=4, T=1, seq_lens=[3000, 7000, 12000, 640], bt_width=96, k=777, seed=45,
+                      exp_range=(124, 127))
+    rng = np.random.default_rng(46)
+    codes = np.zeros((w.num_pages, 128, 128), dtype=np.uint8)
+    codes[:, :, 0:3] = rng.integers(0, 8, size=(w.num_pages, 128, 3))
+    _fixed_index_pool(w, codes)
+    w.index_q[:, :] = 0
+    w.index_q[:, 0:3] = mxfp4.round_to_bf16_bits(np.array([1.0, 1.0 / 16, 1.0 / 256]))
+    d = to_device(w)
+    ws = spd.Workspace("cuda")
+    for rep in range(2):
+        out, sel = _step(spd, w, d, ws)
+        assert spd.check_device_errors(ws) == 0
+        sel_np, out_bits = sel.cpu().numpy(), bf16_bits(out)
+        for i, L in enumerate(w.seq_lens):
+            pos = int(L) - 1
+            ref = decode.topk(decode.index_scores(w.index_q[i], w.index_pool, w.block_table[i], pos), w.k)
+            n = min(w.k, pos + 1)
+            assert sorted(sel_np[i][:n].tolist()) == sorted(ref.tolist()), (rep, i)
+            _check_token(w, i, sel_np[i], out_bits)
+
+
 def test_step_one_token_concentrated_threshold_bin(spd):
     """The tokens of the threshold bin sit in the first chunks only (more of
     them in one chunk than the exchange requests at once) and tie exactly:
