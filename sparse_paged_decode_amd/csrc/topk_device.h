@@ -203,8 +203,10 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
 // ---------------------------------------------------------------------------
 constexpr int kLdsCand = 3840;   // candidates the resolving workgroup stages in LDS
 
+constexpr int kFilterStage = 6144;  // words a filter slice stages its outputs in
+
 struct FilterLds {
-  uint32_t hist[kHistBins];
+  uint32_t stage[kFilterStage];  // positions above the threshold bin, then (key, position) candidates
   uint32_t scratch[8];
 };
 
@@ -289,13 +291,49 @@ __device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, in
   // counts <= kSlice per workgroup: both fit one packed 16+16-bit scan
   uint32_t tot;
   const uint32_t before = block_exclusive_scan(__popc(hi_mask) | (__popc(eq_mask) << 16), lds.scratch, tot);
+  const uint32_t n_hi = tot & 0xFFFFu, n_eq = tot >> 16;
+  // The slice's block of output slots and of candidate slots; while those
+  // atomics are in flight the outputs are staged in LDS at their offsets in
+  // the block (positions, then (key, position) pairs), to be written to
+  // consecutive slots by consecutive lanes.  Without room, or with scores
+  // to write as well, each lane writes its own.
+  const bool staged = !a.out_scores && n_hi + 2u * n_eq <= (uint32_t)kFilterStage;
+  uint32_t base_hi = 0, base_c = 0;
   if (tid == 0) {
-    lds.scratch[kWaves] = (tot & 0xFFFFu) ? atomicAdd(a.out_cnt, tot & 0xFFFFu) : 0u;
-    lds.scratch[kWaves + 1] = (tot >> 16) ? atomicAdd(a.cand_cnt, tot >> 16) : 0u;
+    base_hi = n_hi ? atomicAdd(a.out_cnt, n_hi) : 0u;
+    base_c = n_eq ? atomicAdd(a.cand_cnt, n_eq) : 0u;
+  }
+  if (staged) {
+    uint32_t o = before & 0xFFFFu, c = n_hi + 2u * (before >> 16);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const uint32_t j = (uint32_t)(j0 + u * kBlock + tid);
+      if (hi_mask & (1u << u)) lds.stage[o++] = j;
+      if (eq_mask & (1u << u)) {
+        lds.stage[c] = score_key(v[u]);
+        lds.stage[c + 1] = j;
+        c += 2;
+      }
+    }
+  }
+  if (tid == 0) {
+    lds.scratch[kWaves] = base_hi;
+    lds.scratch[kWaves + 1] = base_c;
   }
   __syncthreads();
-  uint32_t slot = lds.scratch[kWaves] + (before & 0xFFFFu);
-  uint32_t cs = lds.scratch[kWaves + 1] + (before >> 16);
+  base_hi = lds.scratch[kWaves];
+  base_c = lds.scratch[kWaves + 1];
+  if (staged) {
+    for (uint32_t q = tid; q < n_hi; q += kBlock) put_selection(a, base_hi + q, (int)lds.stage[q], 0.f);
+    for (uint32_t q = tid; q < n_eq; q += kBlock) {
+      const uint32_t cs = base_c + q;
+      const uint32_t key = lds.stage[n_hi + 2u * q], j = lds.stage[n_hi + 2u * q + 1u];
+      if (cs < (uint32_t)kCandCap) store_coherent(a.cand + cs, ((uint64_t)j << 32) | key);
+    }
+    return sp;
+  }
+  uint32_t slot = base_hi + (before & 0xFFFFu);
+  uint32_t cs = base_c + (before >> 16);
 #pragma unroll
   for (int u = 0; u < kPer; ++u) {
     const int j = j0 + u * kBlock + tid;
