@@ -145,6 +145,9 @@ def test_topk_bad_page_id_is_flagged_not_dereferenced(spd):
 MANY = [
     ("many_queries_t1", 300, 1, (100, 3000), 100, 300),
     ("many_queries_t2", 150, 2, (100, 5000), 100, 500),
+    # more tokens above the threshold bin than the LDS staging holds (2048):
+    # each lane writes its own
+    ("many_queries_k_over_2048", 300, 1, (2000, 6000), 100, 2500),
 ]
 
 
