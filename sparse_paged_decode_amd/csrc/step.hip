@@ -150,9 +150,19 @@ struct LocalLds {
 };
 static_assert(sizeof(float) * kLocalTokens >= sizeof(uint2) * kExchCap, "exchanged candidates reuse the score area");
 
+// A one-row scan item's scores, staged in LDS and written out whole at the
+// end of the chunk (a scan loop with no global stores keeps its page loads
+// in flight), with the chunk's page ids.
+struct ScanStageLds {
+  ScanLds<1> scan;
+  float scores[kMaxChunkPages * kPageTokens];
+  int32_t ptab[kMaxChunkPages];
+};
+
 template <int TQ>
 union StepLds {
   ScanLds<TQ> scan;
+  ScanStageLds stage;  // TQ 1
   FilterLds filter;
   ResolveLds resolve;
   AttnLds attn;
@@ -646,7 +656,20 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
       sa.tq = tq;
       sa.p_begin = c * lay.chunk_pages;
       sa.p_end = min(sa.p_begin + lay.chunk_pages, n_rel);
-      scan_chunk<TQ, Fmt>(sa, lds);
+      if constexpr (TQ == 1) {
+        ScanStageLds& st = slds.stage;
+        scan_chunk<1, Fmt, true>(sa, st.scan, (lds_f32*)st.scores, (lds_i32w*)st.ptab);
+        __syncthreads();
+        // The chunk's whole lines of the score row (entries past the
+        // row's last valid position hold values no reader uses).
+        const uint32_t n_bytes = (uint32_t)(sa.p_end - sa.p_begin) * kPageTokens * 4u;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            buffer_rsrc(sa.scores + (size_t)sa.row[0] * sa.lcap + (size_t)sa.p_begin * kPageTokens, n_bytes);
+        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st.scores);
+        for (uint32_t q = (uint32_t)thread_index(); q * 16u < n_bytes; q += kBlock) store_coherent_x4(rsrc, q * 16u, src[q]);
+      } else {
+        scan_chunk<TQ, Fmt>(sa, lds);
+      }
       wait_vmem();  // scores and histogram updates are complete before the arrival
     }
   }
