@@ -18,9 +18,9 @@ namespace mono {
 // then 128 rows x 4 B of e8m0 scales, one per 32 elements.
 struct Mxfp4Format {
   static constexpr int kPageBytes = 8704;
-  static constexpr int kScanBatch = 4;  // index pages a scan lane fetches ahead
-  // The same in the chunk-local step, whose 512 chunk scans all stream at
-  // once: two pages ahead measured faster there than one, three or four.
+  // Index pages a scan lane fetches ahead when the scores go to LDS (one
+  // query row: the chunk-local step and the one-row scan items): two pages
+  // ahead measured faster than one, three or four.
   static constexpr int kScanBatchLocal = 2;
   // The four-token instance (each page scored for up to four query tokens):
   // three pages ahead measured faster there than four.
@@ -69,7 +69,6 @@ struct Mxfp4Format {
 struct Fp8Format {
   static constexpr int kPageBytes = 16384;
   static constexpr int kRowBytes8 = 128;
-  static constexpr int kScanBatch = 2;  // the same bytes in flight as 4 MXFP4 pages
   static constexpr int kScanBatchLocal = 2;  // one page ahead measured slower
   static constexpr int kScanBatchMulti = 2;
 

@@ -69,15 +69,17 @@ struct ScanArgs {
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) int32_t lds_i32w;
 
-// With kLocal (one query token), the scores go to lds_scores (token j of the
+// With kLocal (one query row), the scores go to lds_scores (token j of the
 // chunk at j - 128 * p_begin) instead of global memory, and the chunk's page
-// ids to lds_ptab, for the chunk-local step.
+// ids to lds_ptab: the chunk-local step keeps them there, a one-row scan
+// item writes them out whole after the chunk.
 template <int TQ, class Fmt, bool kLocal = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, lds_f32* lds_scores = nullptr,
                                            lds_i32w* lds_ptab = nullptr) {
   static_assert(!kLocal || TQ == 1, "chunk-local scans hold one query token");
   // pages per prefetch batch
-  constexpr int kBatch = kLocal ? Fmt::kScanBatchLocal : (TQ > 1 ? Fmt::kScanBatchMulti : Fmt::kScanBatch);
+  static_assert(kLocal || TQ > 1, "one-row scans keep their scores in LDS");
+  constexpr int kBatch = kLocal ? Fmt::kScanBatchLocal : Fmt::kScanBatchMulti;
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
 
