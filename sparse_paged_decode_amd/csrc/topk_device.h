@@ -35,9 +35,16 @@
 namespace mono {
 
 
+// A scan's LDS.  One row: one count per histogram bin.  Several rows: two
+// 16-bit counts per word (a chunk holds at most 64 x 128 = 8192 tokens), and
+// the scores of kStagePages pages per row, written out as whole lines every
+// kStagePages pages so the scan loop itself issues no global store.
+constexpr int kStagePages = 12;
 template <int TQ>
 struct ScanLds {
-  uint32_t hist[TQ * kHistBins];
+  static constexpr bool kPacked = TQ > 1;
+  uint32_t hist[kPacked ? TQ * kHistBins / 2 : TQ * kHistBins];
+  float sc[kPacked ? TQ : 1][kPacked ? kStagePages * kPageTokens : 1];
 };
 
 // ---------------------------------------------------------------------------
@@ -101,7 +108,10 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
     }
   }
 
-  for (int x = tid; x < TQ * kHistBins; x += kBlock) lds.hist[x] = 0;
+  constexpr bool kPacked = ScanLds<TQ>::kPacked;
+  static_assert(!kPacked || kLocal || kStagePages % (2 * kBatch) == 0, "sub-blocks end with loop iterations");
+  constexpr int kRowWords = kPacked ? kHistBins / 2 : kHistBins;
+  for (int x = tid; x < TQ * kRowWords; x += kBlock) lds.hist[x] = 0;
   __syncthreads();
 
   const int row0 = 32 * wave + m;  // tile 0 row; tile 1 is row0 + 16
@@ -156,13 +166,18 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
         const int j = p * kPageTokens + 32 * wave + 16 * tile + m;
 #pragma unroll
         for (int i = 0; i < TQ; ++i) {
+          if constexpr (kPacked) {
+            // every row's slot is written (rows past tq are never written out)
+            lds.sc[i][(p - p_begin) % kStagePages * kPageTokens + 32 * wave + 16 * tile + m] = c[i];
+          }
           if (i < a.tq && j <= a.pos[i]) {
-            if constexpr (kLocal) {
-              lds_scores[j - p_begin * kPageTokens] = c[i];
+            if constexpr (kLocal) lds_scores[j - p_begin * kPageTokens] = c[i];
+            const uint32_t bin = score_key(c[i]) >> kHistShift;
+            if constexpr (kPacked) {
+              atomicAdd(&lds.hist[i * kRowWords + (bin >> 1)], 1u << ((bin & 1u) << 4));
             } else {
-              store_coherent(a.scores + (size_t)a.row[i] * a.lcap + j, c[i]);
+              atomicAdd(&lds.hist[i * kHistBins + bin], 1u);
             }
-            atomicAdd(&lds.hist[i * kHistBins + (score_key(c[i]) >> kHistShift)], 1u);
           }
         }
       }
@@ -180,6 +195,26 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
     load_batch(ra, p0 + 2 * kBatch);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) score_page(rb[u], p0 + kBatch + u);
+    if constexpr (kPacked) {
+      // A sub-block of pages is complete: its score lines go out (the
+      // next batch's loads are already in flight ahead of these stores).
+      const int done = min(p0 + 2 * kBatch, p_end);
+      if ((done - p_begin) % kStagePages == 0 || done == p_end) {
+        const int sp0 = p_begin + (done - p_begin - 1) / kStagePages * kStagePages;
+        const uint32_t n_bytes = (uint32_t)(done - sp0) * kPageTokens * 4u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < TQ; ++i) {
+          if (i < a.tq) {
+            const __amdgpu_buffer_rsrc_t rsrc =
+                buffer_rsrc(a.scores + (size_t)a.row[i] * a.lcap + (size_t)sp0 * kPageTokens, n_bytes);
+            const u32x4_t* src = reinterpret_cast<const u32x4_t*>(lds.sc[i]);
+            for (uint32_t q = (uint32_t)tid; q * 16u < n_bytes; q += kBlock) store_coherent_x4(rsrc, q * 16u, src[q]);
+          }
+        }
+        __syncthreads();
+      }
+    }
   }
   __syncthreads();
 
@@ -187,9 +222,14 @@ __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, 
   for (int i = 0; i < TQ; ++i) {
     if (i < a.tq) {
       uint32_t* gh = a.ghist + (size_t)a.row[i] * kHistBins;
-      for (int x = tid; x < kHistBins; x += kBlock) {
-        const uint32_t v = lds.hist[i * kHistBins + x];
-        if (v) atomicAdd(&gh[x], v);
+      for (int x = tid; x < kRowWords; x += kBlock) {
+        const uint32_t v = lds.hist[i * kRowWords + x];
+        if constexpr (kPacked) {
+          if (v & 0xFFFFu) atomicAdd(&gh[2 * x], v & 0xFFFFu);
+          if (v >> 16) atomicAdd(&gh[2 * x + 1], v >> 16);
+        } else {
+          if (v) atomicAdd(&gh[x], v);
+        }
       }
     }
   }
