@@ -22,9 +22,9 @@ struct Mxfp4Format {
   // query row: the chunk-local step and the one-row scan items): two pages
   // ahead measured faster than one, three or four.
   static constexpr int kScanBatchLocal = 2;
-  // The four-token instance (each page scored for up to four query tokens):
-  // three pages ahead measured faster there than four.
-  static constexpr int kScanBatchMulti = 3;
+  // The four-token instance (each page scored for up to four query tokens,
+  // the scores staged in LDS): two pages ahead measured faster than three.
+  static constexpr int kScanBatchMulti = 2;
 
   struct ChunkAddr {
     uint32_t d, e;  // byte offsets of the 16 data bytes and of the scale byte
