@@ -144,7 +144,7 @@ long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_s
     const int groups = lay.B * lay.q_groups;
     const int span = lay.win_hi - lay.win_lo;  // pages of the window (the whole table by default)
     const int per_group = std::max(1, cap / std::max(1, groups));
-    lay.chunk_pages = std::min(kMaxChunkPages, std::max(1, (span + per_group - 1) / per_group));
+    lay.chunk_pages = std::min(kPlanChunkPages, std::max(1, (span + per_group - 1) / per_group));
     lay.chunks = (span + lay.chunk_pages - 1) / lay.chunk_pages;
     lay.n_scan = (uint32_t)((size_t)groups * lay.chunks);
     lay.n_ready0 = lay.n_scan;

@@ -33,6 +33,12 @@ constexpr int kMergeMaxCandidates = 8192;  // topk merge: G * k_in per query tok
 // Scan and selection items (topk_device.h).
 constexpr int kScanChunkPages = 16;  // index pages per scan work item (default)
 constexpr int kMaxChunkPages = 64;   // one page id per lane of a wave
+// The largest scan chunk the plan makes.  With ragged lengths the chunks
+// that hold pages do not divide into whole rounds of the workgroups, and
+// the last round's chunks set the end of the scan: 32-page chunks measured
+// faster than 64 on a batch of 16K-64K contexts (16-page ones slower: each
+// chunk flushes its histograms and arrives once).
+constexpr int kPlanChunkPages = 32;
 constexpr int kHistBins = 2048;      // top 11 bits of the score key
 constexpr int kHistShift = 21;
 constexpr int kSlice = 4096;         // scores per filter work item

@@ -159,6 +159,19 @@ def test_topk_many_query_tokens(spd, name, B, T, lens, W, k):
         check_topk_row(sel[i], w, i, k)
 
 
+def test_topk_four_tokens_all_equal_full_chunks(spd):
+    """Four query tokens per request, every score of a row equal: 32-page
+    chunks put 4096 tokens of each row in one histogram bin (the four-row
+    scan packs two 16-bit counts per word), ties go to the lowest indices."""
+    w = make_workload("eq4", B=64, T=4, seq_lens=32768, bt_width=256, k=1000, seed=16)
+    codes = np.full((w.num_pages, 128, 128), 3, dtype=np.uint8)
+    w.index_pool = mxfp4.pack(codes, np.full((w.num_pages, 128, 4), 127, dtype=np.uint8))
+    sel, _ = _run(spd, w, 1000)
+    ref = np.arange(1000)
+    for i in range(w.N):
+        assert np.array_equal(np.sort(sel[i]), ref), f"query {i}"
+
+
 def test_topk_many_query_tokens_all_equal():
     """Every score equal in every row: the threshold bin overflows LDS, ties go to the lowest indices."""
     import sparse_paged_decode_amd as spd
