@@ -84,9 +84,8 @@ template <int TQ, class Fmt, bool kLocal = false>
 __device__ __forceinline__ void scan_chunk(const ScanArgs& a, ScanLds<TQ>& lds, lds_f32* lds_scores = nullptr,
                                            lds_i32w* lds_ptab = nullptr) {
   static_assert(!kLocal || TQ == 1, "chunk-local scans hold one query token");
-  // pages per prefetch batch
   static_assert(kLocal || TQ > 1, "one-row scans keep their scores in LDS");
-  constexpr int kBatch = kLocal ? Fmt::kScanBatchLocal : Fmt::kScanBatchMulti;
+  constexpr int kBatch = kLocal ? Fmt::kScanBatchLocal : Fmt::kScanBatchMulti;  // pages per prefetch batch
   const int tid = thread_index(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, m = lane & 15;
 
