@@ -790,7 +790,10 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
   aa.split_cnt = ctrl + lay.attn_cnt + qh;
   aa.err = err;
-  attn_split<Fmt, false, kGroups>(aa, lds);
+  // The workgroup that wrote the output is the last to use the split
+  // counter (every split arrived before it merged): it starts from zero
+  // for the next call.
+  if (attn_split<Fmt, false, kGroups>(aa, lds) && n_splits > 1 && thread_index() == 0) aa.split_cnt[0] = 0u;
 }
 
 // Item sets of the kernel instances: every kind; the chunk-local step's
@@ -862,14 +865,15 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
     t = s_item;
   }
 
-  // A chunk-local launch without clear items, whose every item was a first
-  // ticket, leaves the control block as it found it: each request's chunks
-  // reset their own counters and the ticket counter was never taken.  It
+  // A chunk-local or attention-only launch without clear items, whose every
+  // item was a first ticket, leaves the control block as it found it: each
+  // request's chunks (each token's merging split) reset their own counters
+  // and the ticket counter was never taken.  It
   // may leave the header's zero record as it is only when the record is
   // this layout's own: a record left by a larger layout also covers bytes
   // past this layout's zero region, which this call used as scratch, so
   // the exit below must lower it.
-  if (kLocal && n_clear == 0u && n_items <= gridDim.x && record_exact) return;
+  if ((kLocal || kSet == kSetAttn) && n_clear == 0u && n_items <= gridDim.x && record_exact) return;
   // Every workgroup has taken its last ticket before it counts itself out,
   // so the last one to leave can reset the control block for the next call
   // and record this layout's zero region as clean.
