@@ -52,14 +52,23 @@ __device__ __forceinline__ void clear_item(const StepLayout& lay, uint32_t c, ui
   if (thread_index() == 0) atomicAdd(ctrl + kHdrCleared, 1u);
 }
 
+// A bounded wait that ran out: the error bit, and the workspace's zero
+// record dropped so that the next call clears the control block before it
+// starts (a late producer may still fill a slot or count an arrival after
+// the counters' last users have reset them).
+__device__ __forceinline__ void wait_ran_out(uint32_t* err, uint32_t* ctrl) {
+  raise_error(err, kErrWait);
+  store_coherent(ctrl + kHdrZeroed, 0u);
+}
+
 // Thread 0 waits until *p >= target; everyone leaves together.
-__device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target, uint32_t* err) {
+__device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target, uint32_t* err, uint32_t* ctrl) {
   if (thread_index() == 0) {
     uint32_t spins = 0;
     while (load_coherent(p) < target) {
       __builtin_amdgcn_s_sleep(2);
       if (++spins > kMaxSpins) {
-        raise_error(err, kErrWait);
+        wait_ran_out(err, ctrl);
         break;
       }
     }
@@ -69,17 +78,18 @@ __device__ __forceinline__ void wait_counter(const uint32_t* p, uint32_t target,
 
 // Thread 0 waits until queue slot q is filled; returns its descriptor to
 // every thread (0 if the bounded wait ran out: the slot is then skipped).
-__device__ __forceinline__ uint32_t wait_slot(const uint32_t* q, uint32_t* err, uint32_t& s_desc) {
+__device__ __forceinline__ uint32_t wait_slot(const uint32_t* q, uint32_t* err, uint32_t* ctrl, uint32_t& s_desc) {
   if (thread_index() == 0) {
     uint32_t spins = 0, d;
     while ((d = load_coherent(q)) == 0u) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kMaxSpins) {
-        raise_error(err, kErrWait);
+        wait_ran_out(err, ctrl);
         break;
       }
     }
     s_desc = d;
+    if (d) *const_cast<uint32_t*>(q) = 0u;  // the slot's one consumer leaves it empty for the next call
   }
   __syncthreads();
   const uint32_t d = s_desc;
@@ -92,7 +102,12 @@ __device__ __forceinline__ uint32_t wait_slot(const uint32_t* q, uint32_t* err, 
 // complete (wait_vmem and a barrier), so consumers see them.
 __device__ __forceinline__ void publish(const StepLayout& lay, uint32_t* ctrl, uint32_t kind, uint32_t first,
                                         uint32_t count, uint32_t* err, uint32_t& s_base) {
-  if (thread_index() == 0) s_base = atomicAdd(ctrl + lay.pub, count);
+  if (thread_index() == 0) {
+    s_base = atomicAdd(ctrl + lay.pub, count);
+    // The publications add up to the queue's length: the last one leaves
+    // the counter at zero for the next call.
+    if (s_base + count == lay.n_queue) ctrl[lay.pub] = 0u;
+  }
   __syncthreads();
   const uint32_t base = s_base;
   if (base + count > lay.n_queue) {  // never expected: the counts are fixed by the shapes
@@ -208,7 +223,7 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
 // Every thread's memory updates are complete, then this workgroup arrives at
 // *cnt and waits until `target` workgroups have.  The arrival returns the
 // count, so the last workgroup to arrive does not poll.
-__device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint32_t* err) {
+__device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint32_t* err, uint32_t* ctrl) {
   wait_vmem();
   __syncthreads();
   if (thread_index() == 0 && atomicAdd(cnt, 1u) + 1u < target) {
@@ -216,7 +231,7 @@ __device__ __forceinline__ void arrive_wait(uint32_t* cnt, uint32_t target, uint
     while (load_coherent(cnt) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kMaxSpins) {
-        raise_error(err, kErrWait);
+        wait_ran_out(err, ctrl);
         break;
       }
     }
@@ -314,7 +329,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   uint32_t thr = 0u, take = 0xFFFFFFFFu;
   bool ties = false;
   if (!all) {
-    arrive_wait(lvl + 0, (uint32_t)nch, err);
+    arrive_wait(lvl + 0, (uint32_t)nch, err, ctrl);
     const BinSplit s1 = find_bin_of_rank_global<kHistBins>(g1, (uint32_t)k, lds.scratch);
     uint32_t R = (uint32_t)k - s1.above;
     const uint32_t B1 = (uint32_t)s1.bin;
@@ -341,7 +356,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
         }
       }
       if (tid == 0) store_coherent(xn_all + c, my_cnt);
-      arrive_wait(lvl + 1, (uint32_t)nch, err);
+      arrive_wait(lvl + 1, (uint32_t)nch, err, ctrl);
       // Counts and the first `win` entries of every chunk are requested at
       // once (win: a power of two, nch * win <= kExchCap); chunks with more
       // follow in a second round.
@@ -464,7 +479,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
 #pragma unroll
       for (int u = 0; u < 16; ++u) m2 |= ((key[u] >> kHistShift) == B1) ? (1u << u) : 0u;
       level_counts(key, m2 & valid, 10, kHistBins, hist, g2);
-      arrive_wait(lvl + 1, (uint32_t)nch, err);
+      arrive_wait(lvl + 1, (uint32_t)nch, err, ctrl);
       const BinSplit s2 = find_bin_of_rank_global<kHistBins>(g2, R, lds.scratch);
       R -= s2.above;
       const uint32_t pre2 = (B1 << 11) | (uint32_t)s2.bin;
@@ -474,7 +489,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
 #pragma unroll
         for (int u = 0; u < 16; ++u) m3 |= ((key[u] >> 10) == pre2) ? (1u << u) : 0u;
         level_counts(key, m3 & valid, 0, 1024, hist, g3);
-        arrive_wait(lvl + 2, (uint32_t)nch, err);
+        arrive_wait(lvl + 2, (uint32_t)nch, err, ctrl);
         const BinSplit s3 = find_bin_of_rank_global<1024>(g3, R, lds.scratch);
         R -= s3.above;
         thr = (pre2 << 10) | (uint32_t)s3.bin;
@@ -486,7 +501,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
           uint32_t tot;
           block_exclusive_scan(mine, lds.scratch, tot);
           if (tid == 0) store_coherent(gt + c, tot);
-          arrive_wait(lvl + 3, (uint32_t)nch, err);
+          arrive_wait(lvl + 3, (uint32_t)nch, err, ctrl);
           uint32_t before = 0;
           for (int x = 0; x < c; ++x) before += load_coherent(gt + x);
           take = R > before ? R - before : 0u;
@@ -676,8 +691,11 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
   // Every chunk slot of the group arrives, with or without work; the last
   // one publishes the selection work of the group's rows.
   __syncthreads();
-  if (thread_index() == 0)
-    s_flag = atomicAdd(ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg, 1u) == (uint32_t)(lay.chunks - 1);
+  if (thread_index() == 0) {
+    uint32_t* done = ctrl + lay.scan_done + (size_t)b * lay.q_groups + qg;
+    s_flag = atomicAdd(done, 1u) == (uint32_t)(lay.chunks - 1);
+    if (s_flag) *done = 0u;  // the last arrival: the counter's last use in this call
+  }
   __syncthreads();
   if (!s_flag) return;
   if (lay.G == 1) {  // the group's rows are consecutive
@@ -726,7 +744,14 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   // Every slice slot arrives; the last one resolves the selection and
   // publishes the token's attention splits.
   __syncthreads();
-  if (thread_index() == 0) s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(lay.slices - 1);
+  if (thread_index() == 0) {
+    s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(lay.slices - 1);
+    if (s_flag) {  // every slice of the row has used its counters
+      ctrl[lay.filter_cnt + i] = 0u;
+      ctrl[lay.out_cnt + i] = 0u;
+      ctrl[lay.cand_cnt + i] = 0u;
+    }
+  }
   __syncthreads();
   if (!s_flag) return;
   // Attention items of token i are numbered split-major (split * H + h), so
@@ -840,9 +865,9 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
       clear_item(lay, t, a.ws, ctrl);
     } else {
       const uint32_t u = t - n_clear;
-      if (n_clear) wait_counter(ctrl + kHdrCleared, n_clear, err);
+      if (n_clear) wait_counter(ctrl + kHdrCleared, n_clear, err, ctrl);
       const uint32_t d =
-          u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, s_desc);
+          u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, ctrl, s_desc);
       const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
       if constexpr (kLocal) {
         if (kind == kItemScan) local_item<Fmt>(a, lay, idx, lds, ctrl, err);
@@ -860,20 +885,28 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
     }
     __syncthreads();  // the next item reuses the LDS
     if (n_items <= gridDim.x) break;  // every item was a first ticket: no ticket is left
-    if (tid == 0) s_item = gridDim.x + atomicAdd(ctrl + kHdrTicket, 1u);
+    if (tid == 0) {
+      // Every workgroup ends on exactly one ticket past the last item, so
+      // the counter takes n_items increments in all: the last one leaves it
+      // at zero for the next call.
+      const uint32_t old = atomicAdd(ctrl + kHdrTicket, 1u);
+      if (old + 1u == n_items) ctrl[kHdrTicket] = 0u;
+      s_item = gridDim.x + old;
+    }
     __syncthreads();
     t = s_item;
   }
 
-  // A chunk-local or attention-only launch without clear items, whose every
-  // item was a first ticket, leaves the control block as it found it: each
-  // request's chunks (each token's merging split) reset their own counters
-  // and the ticket counter was never taken.  It
+  // A launch without clear items leaves the control block as it found it:
+  // every counter is reset by its last user (each request's chunks, a
+  // row's last scan chunk and resolving slice, each token's merging split,
+  // the last publisher, each queue slot's consumer, the last ticket).  It
   // may leave the header's zero record as it is only when the record is
   // this layout's own: a record left by a larger layout also covers bytes
   // past this layout's zero region, which this call used as scratch, so
-  // the exit below must lower it.
-  if ((kLocal || kSet == kSetAttn) && n_clear == 0u && n_items <= gridDim.x && record_exact) return;
+  // the exit below must lower it.  (A wait that ran out has dropped the
+  // record already, so the next call clears the region first.)
+  if (n_clear == 0u && record_exact) return;
   // Every workgroup has taken its last ticket before it counts itself out,
   // so the last one to leave can reset the control block for the next call
   // and record this layout's zero region as clean.
