@@ -109,6 +109,9 @@ def parse():
                    help="do not time the two-call form of the step (profiling runs count one kernel only)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 128 MiB device copy 10 times (counter calibration) and exit")
+    p.add_argument("--timeline", type=int, default=0, metavar="N",
+                   help="only print the phase timeline of N launches from the trace build of the library "
+                        "(libmono_decode_trace.so) and exit")
     return p.parse_args()
 
 
@@ -123,6 +126,120 @@ def copy_calibration():
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
+
+
+# Phase stamps of the trace build (include/mono_trace.h), by item kind.
+_ATTN_PHASES = {10: "attention: entry", 11: "attention: q and table loaded", 12: "attention: pass done",
+                13: "attention: partials stored", 14: "attention: partials complete", 15: "attention: arrived",
+                16: "attention: merged (last split)"}
+TIMELINE_PHASES = {
+    "chunk-local chunk": {2: "scan and histogram flush done", 3: "histogram complete (barrier)",
+                          4: "threshold bin found", 5: "threshold-bin pairs stored",
+                          6: "pairs complete (barrier)", 7: "pairs in LDS", 8: "k-th key found",
+                          9: "selection list built", **_ATTN_PHASES},
+    "scan": {2: "scores and histogram complete", 3: "arrived at the group counter", 17: "row selected (inline)"},
+    "filter slice": {2: "slice filtered", 3: "arrived at the row counter", 4: "resolve: final splits published",
+                     5: "resolve: done"},
+    "attention split": dict(_ATTN_PHASES),
+    "selection": {17: "row selected"},
+    "clear": {},
+}
+
+
+def timeline(args):
+    """Phase timeline of the step from the trace build: p10/p50/p90/max of
+    every stamp (us from the launch's first kernel entry) and the p50 step
+    from the previous stamp of the same item, per item kind."""
+    import ctypes
+
+    import torch
+
+    import sparse_paged_decode_amd as spd
+    from sparse_paged_decode_amd.build import TRACE_LIB_PATH
+    from workloads import workload
+
+    lib = spd.load_library(TRACE_LIB_PATH)
+    lib.mono_trace_clear.restype = ctypes.c_int
+    lib.mono_trace_read.restype = ctypes.c_int
+    lib.mono_trace_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t]
+    dev = torch.device("cuda:0")
+    w = workload(args.workload, cache=args.cache)
+    copies = max(1, args.copies)
+    run = StepRunner(spd, torch, dev, w, copies)
+    for s in range(max(args.warmup, copies)):
+        run.step(s % copies)
+    torch.cuda.synchronize(dev)
+    n_items, n_groups = 8192 * 32, 4096 * 32
+    print(f"# phase timeline of {w.name} ({args.cache} caches, {copies} pool copies rotated), trace build "
+          f"(libmono_decode_trace.so: thread 0 of each workgroup stamps the 100 MHz device clock)")
+    print(f"# command (repo root): python3 -u bench.py {' '.join(sys.argv[1:])}")
+    print("# us from the launch's first kernel entry; 'step' = p50 of the time since the previous stamp of the same item")
+    for launch in range(args.timeline):
+        if lib.mono_trace_clear() != 0:
+            raise RuntimeError("mono_trace_clear failed")
+        run.step(launch % copies)
+        torch.cuda.synchronize(dev)
+        items = np.zeros(n_items, dtype=np.uint64)
+        groups = np.zeros(n_groups, dtype=np.uint64)
+        if lib.mono_trace_read(items.ctypes.data, n_items, groups.ctypes.data, n_groups) != 0:
+            raise RuntimeError("mono_trace_read failed")
+        print_timeline(launch, items.reshape(8192, 32).astype(np.int64), groups.reshape(4096, 32).astype(np.int64))
+
+
+def print_timeline(launch, it, gr):
+    """Prints one launch's records (item records it[t, s], workgroup records
+    gr[w, s], as mono_trace_read returns them)."""
+    entry = gr[:, 0][gr[:, 0] > 0]
+    leave = gr[:, 1][gr[:, 1] > 0]
+    t0 = entry.min()
+    us = lambda v: (v - t0) / 100.0
+    print(f"\n== launch {launch}: {entry.size} workgroups enter over {us(entry.max()):.2f} us; "
+          f"the last leaves the item loop at {us(leave.max()):.2f} us")
+    used = it[:, 0] > 0
+    kinds = (it[:, 31] >> 24) & 0xFF
+    local = bool(((kinds == 1) & used & (it[:, 4] > 0)).any())
+    names = {1: "chunk-local chunk" if local else "scan", 2: "filter slice", 3: "attention split",
+             4: "selection", 0xFF: "clear"}
+    for kind, label in names.items():
+        rec = it[used & (kinds == kind)]
+        if rec.shape[0] == 0:
+            continue
+        phases = {0: "start", **TIMELINE_PHASES[label], 1: "end"}
+        print(f"  {label}: {rec.shape[0]} items")
+        print(f"    {'phase':38s} {'n':>5s} {'p10':>7s} {'p50':>7s} {'p90':>7s} {'max':>7s} {'step':>7s}")
+        # Stamps in program order: the start, the kind's phases by number, the end.
+        order = [0] + sorted(k for k in phases if k > 1) + [1]
+        last = np.zeros(rec.shape[0], dtype=np.int64)  # each item's latest stamp so far
+        for k in order:
+            v = rec[:, k]
+            ok = v > 0
+            if not ok.any():
+                continue
+            a = us(v[ok])
+            both = ok & (last > 0)
+            step = f"{np.median((v[both] - last[both]) / 100.0):7.2f}" if both.any() else ""
+            print(f"    {phases[k]:38s} {ok.sum():5d} {np.percentile(a, 10):7.2f} {np.percentile(a, 50):7.2f} "
+                  f"{np.percentile(a, 90):7.2f} {a.max():7.2f} {step:>7s}")
+            last = np.where(ok, v, last)
+        # First-round items by compute-unit slot: with two resident
+        # workgroups per CU, tickets below half the grid are the first
+        # workgroup dispatched to their CU.
+        tickets = np.nonzero(used & (kinds == kind))[0]
+        half = entry.size // 2
+        first = (tickets < half) & (rec[:, 2] > 0)
+        second = (tickets >= half) & (tickets < entry.size) & (rec[:, 2] > 0)
+        # The XCD of a first-round item is its ticket mod 8 (workgroups are
+        # dealt to the XCDs in turn).
+        fr = tickets < entry.size
+        if fr.sum() >= 8 and kind != 0xFF:
+            ends = [rec[fr & (tickets % 8 == x), 1] for x in range(8)]
+            ends = [us(e[e > 0]) for e in ends]
+            print("    item end by XCD (first-round items), p50 / max: "
+                  + ", ".join(f"{x}: {np.median(e):.1f} / {e.max():.1f}" for x, e in enumerate(ends) if e.size))
+        if first.any() and second.any() and 2 in phases:
+            d = (rec[:, 2] - rec[:, 0]) / 100.0
+            print(f"    {phases[2]} after the start, p50: {np.median(d[first]):.2f} us for tickets below {half} "
+                  f"(the first workgroup of each CU), {np.median(d[second]):.2f} us for tickets {half}..{entry.size - 1}")
 
 
 def _read_text(path):
@@ -468,6 +585,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.timeline > 0:
+        timeline(args)
         return
 
     import torch

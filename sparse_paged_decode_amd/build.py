@@ -13,6 +13,10 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_PATH = os.path.join(PKG_DIR, "libmono_decode.so")
+# The same library with the kernels' phase stamps compiled in (MONO_TRACE):
+# only step.hip differs; include/mono_trace.h declares its two extra calls.
+TRACE_LIB_PATH = os.path.join(PKG_DIR, "libmono_decode_trace.so")
+TRACE_SOURCE = "step.hip"
 SOURCES = ["plan.cpp", "pages.hip", "step.hip", "merge.hip", "bench_read.hip", "bench_scan.hip", "abi.hip"]
 ARCH = "gfx950"
 
@@ -58,16 +62,21 @@ def build(jobs=4):
     obj_dir = os.path.join(PKG_DIR, "_build")
     os.makedirs(obj_dir, exist_ok=True)
 
-    def compile_one(src):
-        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
-        _run([hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    def compile_one(job):
+        src, extra, suffix = job
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + suffix + ".o")
+        _run([hipcc, *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
         return obj
 
+    jobs_list = [(src, [], "") for src in SOURCES] + [(TRACE_SOURCE, ["-DMONO_TRACE"], "_trace")]
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB_PATH)
+        objs = list(ex.map(compile_one, jobs_list))
+    trace_obj = objs.pop()
+    for path, lib_objs in ((LIB_PATH, objs),
+                           (TRACE_LIB_PATH, [trace_obj if o.endswith(os.sep + "step.o") else o for o in objs])):
+        tmp = path + ".tmp"
+        _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *lib_objs])
+        os.replace(tmp, path)
     return LIB_PATH
 
 

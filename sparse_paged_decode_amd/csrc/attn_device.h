@@ -107,6 +107,7 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
   const int g = lane >> 4, m = lane & 15;
   const int e0 = a.e0, e1 = a.e1, pos = a.pos, H = a.H, h = a.h, split = a.split, n_splits = a.n_splits;
   const int n_groups = (e1 - e0 + kGroupTokens - 1) / kGroupTokens;
+  MONO_STAMP(10);
 
   // The first pass's selection entries are requested first; the block-table
   // row (into LDS) and the q operand (into registers) load meanwhile.
@@ -146,6 +147,7 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, src[s]);
   }
   __syncthreads();
+  MONO_STAMP(11);
 
   const float sl2 = a.scale * 1.4426950408889634f;  // logits in log2 units
   // m_run: running maximum of head m (every lane (g, m)); acc[x][i] and
@@ -293,7 +295,8 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
   }
 
   // ---- combine the four waves -------------------------------------------
-  __syncthreads();  // the block-table copy is no longer read
+  __syncthreads();
+  MONO_STAMP(12);  // the block-table copy is no longer read
   float* so = reinterpret_cast<float*>(lds.combine);  // [wave][head][dim]
   float(*s_m)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes);
   float(*s_l)[kQHeads] = reinterpret_cast<float(*)[kQHeads]>(lds.combine + kSoBytes + kWaves * kQHeads * 4);
@@ -353,13 +356,16 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     store_coherent_x4(r, (uint32_t)(kBlock + tid) * 16u, u32x4_t{__float_as_uint(o[4]), __float_as_uint(o[5]),
                                                                  __float_as_uint(o[6]), __float_as_uint(o[7])});
   }
+  MONO_STAMP(13);
   wait_vmem();
   __syncthreads();
+  MONO_STAMP(14);
   if (tid == 0) {
     const uint32_t prev = atomicAdd(a.split_cnt, 1u);
     *s_last = (prev == (uint32_t)(n_splits - 1)) ? 1u : 0u;
   }
   __syncthreads();
+  MONO_STAMP(15);
   if (!*s_last) return false;
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
@@ -407,6 +413,7 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     M = Mb;
   }
   store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
+  MONO_STAMP(16);
   return true;
 }
 

@@ -10,6 +10,7 @@
 #include <stdint.h>
 
 #include "plan.h"
+#include "trace.h"
 
 namespace mono {
 

@@ -214,6 +214,7 @@ __device__ __forceinline__ void select_item(const StepArgs& a, const StepLayout&
   if (L >= T && L <= lay.lcap) {  // an invalid length was reported by the scan items
     select_query(select_args(a, lay, (int)i, window_valid(lay, L - T + t), ctrl, err), lds.resolve);
     wait_vmem();
+    MONO_STAMP(17);
   }
   __syncthreads();
   if (lay.mode == kModeFused)
@@ -308,6 +309,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     scan_chunk<1, Fmt, true>(sa, lds.u.sel.scan, (lds_f32*)lds.u.sel.scores, (lds_i32w*)lds.ptab);
   }
   __syncthreads();
+  MONO_STAMP(2);
 
   // Thread t holds the keys of tokens 16t..16t+15 of the chunk.
   uint32_t key[16];
@@ -330,7 +332,9 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   bool ties = false;
   if (!all) {
     arrive_wait(lvl + 0, (uint32_t)nch, err, ctrl);
+    MONO_STAMP(3);
     const BinSplit s1 = find_bin_of_rank_global<kHistBins>(g1, (uint32_t)k, lds.scratch);
+    MONO_STAMP(4);
     uint32_t R = (uint32_t)k - s1.above;
     const uint32_t B1 = (uint32_t)s1.bin;
     thr = B1 << kHistShift;
@@ -356,7 +360,9 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
         }
       }
       if (tid == 0) store_coherent(xn_all + c, my_cnt);
+      MONO_STAMP(5);
       arrive_wait(lvl + 1, (uint32_t)nch, err, ctrl);
+      MONO_STAMP(6);
       // Counts and the first `win` entries of every chunk are requested at
       // once (win: a power of two, nch * win <= kExchCap); chunks with more
       // follow in a second round.
@@ -398,6 +404,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
           if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
         }
       }
+      MONO_STAMP(7);
       const int n_c = (int)min(lds.xpre[nch], (uint32_t)kExchCap);
       if (lds.xpre[nch] != s1.count && tid == 0) raise_error(err, kErrSelection);  // never expected
       // A radix pass over key bits 20..10 among the candidates (each
@@ -510,6 +517,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       }
     }
   }
+  MONO_STAMP(8);
   uint32_t selm = 0, tie_rank = 0;
   if (ties) {
     uint32_t mine = 0;
@@ -547,6 +555,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     done_prev = atomicAdd(lvl + 4, 1u);
   }
 
+  MONO_STAMP(9);
   const int H = lay.H;
   for (int h = 0; h < H; ++h) {
     const size_t qh = (size_t)i * H + h;
@@ -686,6 +695,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
         scan_chunk<TQ, Fmt>(sa, lds);
       }
       wait_vmem();  // scores and histogram updates are complete before the arrival
+      MONO_STAMP(2);
     }
   }
   // Every chunk slot of the group arrives, with or without work; the last
@@ -697,6 +707,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
     if (s_flag) *done = 0u;  // the last arrival: the counter's last use in this call
   }
   __syncthreads();
+  MONO_STAMP(3);
   if (!s_flag) return;
   if (lay.G == 1) {  // the group's rows are consecutive
     const uint32_t q0 = (uint32_t)(b * T + u0);
@@ -740,6 +751,7 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   if (sliced) {
     split = filter_slice(sa, s * kSlice, min((s + 1) * kSlice, n_valid), lds.filter);
     wait_vmem();
+    MONO_STAMP(2);
   }
   // Every slice slot arrives; the last one resolves the selection and
   // publishes the token's attention splits.
@@ -753,6 +765,7 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
     }
   }
   __syncthreads();
+  MONO_STAMP(3);
   if (!s_flag) return;
   // Attention items of token i are numbered split-major (split * H + h), so
   // the splits whose candidates are final can be published as one range:
@@ -763,12 +776,14 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
   uint32_t n_early = 0;
   if (valid) {
     resolve_query(sa, lds.resolve, sliced, split, [&](uint32_t n_final) {
+      MONO_STAMP(4);
       if (lay.mode != kModeFused) return;
       n_early = n_final >= (uint32_t)lay.k ? S : min(S, n_final / (uint32_t)lay.split_tokens);
       if (n_early) publish(lay, ctrl, kItemAttn, first, n_early * H, err, s_pub);
     });
     wait_vmem();
     __syncthreads();
+    MONO_STAMP(5);
   }
   if (lay.mode == kModeFused && n_early < S)
     publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
@@ -836,6 +851,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
   const int tid = thread_index();
   uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + lay.err);
   uint32_t* ctrl = reinterpret_cast<uint32_t*>(a.ws + lay.ctrl_base);
+  MONO_STAMP_GROUP(0);
 
   // The header records how much of the workspace the previous call left
   // zero.  If that does not cover this layout's zero region (first use, or
@@ -862,6 +878,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
   for (;;) {
     if (t >= n_items) break;
     if (t < n_clear) {
+      MONO_TRACE_ITEM(t, (kTraceClearKind << 24) | t);
       clear_item(lay, t, a.ws, ctrl);
     } else {
       const uint32_t u = t - n_clear;
@@ -869,6 +886,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
       const uint32_t d =
           u < lay.n_ready0 ? ((lay.ready_kind << kKindShift) | u) : wait_slot(ctrl + lay.queue + (u - lay.n_ready0), err, ctrl, s_desc);
       const uint32_t kind = d >> kKindShift, idx = d & kIndexMask;
+      MONO_TRACE_ITEM(t, (kind << 24) | idx);
       if constexpr (kLocal) {
         if (kind == kItemScan) local_item<Fmt>(a, lay, idx, lds, ctrl, err);
       } else if constexpr (kSet == kSetAttn) {
@@ -883,6 +901,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
         attn_item<Fmt>(a, lay, idx, lds.attn, ctrl, err);
       }
     }
+    MONO_STAMP(1);
     __syncthreads();  // the next item reuses the LDS
     if (n_items <= gridDim.x) break;  // every item was a first ticket: no ticket is left
     if (tid == 0) {
@@ -906,6 +925,7 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
   // past this layout's zero region, which this call used as scratch, so
   // the exit below must lower it.  (A wait that ran out has dropped the
   // record already, so the next call clears the region first.)
+  MONO_STAMP_GROUP(1);
   if (n_clear == 0u && record_exact) return;
   // Every workgroup has taken its last ticket before it counts itself out,
   // so the last one to leave can reset the control block for the next call
@@ -1051,3 +1071,40 @@ int launch_scratch_errors(uint8_t* scratch_ptr, size_t err_offset, uint32_t* dst
 }
 
 }  // namespace mono
+
+#ifdef MONO_TRACE
+// The trace library's record arrays and its two calls.
+#include "mono_trace.h"
+
+namespace mono {
+__device__ uint64_t g_trace_items[kTraceItems * kTraceStamps];
+__device__ uint64_t g_trace_groups[kTraceGroups * kTraceStamps];
+}  // namespace mono
+
+extern "C" int mono_trace_clear(void) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(mono::g_trace_items)) != hipSuccess ||
+      hipMemset(p, 0, sizeof(mono::g_trace_items)) != hipSuccess)
+    return MONO_EHIP;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(mono::g_trace_groups)) != hipSuccess ||
+      hipMemset(p, 0, sizeof(mono::g_trace_groups)) != hipSuccess)
+    return MONO_EHIP;
+  return hipDeviceSynchronize() == hipSuccess ? MONO_OK : MONO_EHIP;
+}
+
+extern "C" int mono_trace_read(uint64_t* items, size_t n_items, uint64_t* groups, size_t n_groups) {
+  using mono::kTraceGroups;
+  using mono::kTraceItems;
+  using mono::kTraceStamps;
+  if (n_items > (size_t)kTraceItems * kTraceStamps || n_groups > (size_t)kTraceGroups * kTraceStamps)
+    return MONO_EINVAL;
+  if (hipDeviceSynchronize() != hipSuccess) return MONO_EHIP;
+  if (n_items && hipMemcpyFromSymbol(items, HIP_SYMBOL(mono::g_trace_items), n_items * 8, 0,
+                                     hipMemcpyDeviceToHost) != hipSuccess)
+    return MONO_EHIP;
+  if (n_groups && hipMemcpyFromSymbol(groups, HIP_SYMBOL(mono::g_trace_groups), n_groups * 8, 0,
+                                      hipMemcpyDeviceToHost) != hipSuccess)
+    return MONO_EHIP;
+  return MONO_OK;
+}
+#endif

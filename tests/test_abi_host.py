@@ -1,6 +1,8 @@
 """CPU-side checks of the C ABI and the Python binding (no GPU, no kernel launches).
 
 * libmono_decode.so loads and exports every function include/mono_decode.h declares;
+  the trace build, libmono_decode_trace.so, exports those and the two of
+  include/mono_trace.h, which the product library does not;
 * host validation rejects bad arguments with the documented codes and a
   message, before touching the device;
 * workspace-size queries;
@@ -17,6 +19,7 @@ import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mono_decode.h")
+TRACE_HEADER = os.path.join(ROOT, "include", "mono_trace.h")
 
 
 @pytest.fixture(scope="module")
@@ -30,8 +33,8 @@ def lib():
     return spd.load_library()
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(names))
@@ -52,6 +55,20 @@ def test_exported_symbols_are_c_names(lib):
     out = os.popen(f"nm -D --defined-only {lib._name}").read()
     for n in _declared_functions():
         assert re.search(rf"\bT {n}$", out, flags=re.M), n
+
+
+def test_trace_build_exports(lib):
+    from sparse_paged_decode_amd.build import TRACE_LIB_PATH
+
+    assert os.path.exists(TRACE_LIB_PATH), "the build makes the trace library beside the product one"
+    trace = _declared_functions(TRACE_HEADER)
+    assert trace == ["mono_trace_clear", "mono_trace_read"]
+    tr = ctypes.CDLL(TRACE_LIB_PATH)
+    for n in _declared_functions() + trace:
+        assert hasattr(tr, n), f"{n} not exported by the trace library"
+    product = os.popen(f"nm -D --defined-only {lib._name}").read()
+    for n in trace:
+        assert not re.search(rf"\b{n}$", product, flags=re.M), f"{n} must not be in the product library"
 
 
 def test_version_and_error_string(lib):
