@@ -83,7 +83,7 @@ struct BinSplit {
 // counts of bins hi, hi - 1, ..., hi - per + 1 in h[0..per), where
 // hi = nbins - 1 - t * per (groups of `per` bins counted from the top).
 __device__ __forceinline__ BinSplit bin_of_rank_in_regs(const uint32_t (&h)[kMaxBinsPerThread], int per, int hi,
-                                                        uint32_t R, uint32_t* scratch) {
+                                                        uint32_t R, uint32_t* scratch, uint32_t* total_out = nullptr) {
   if (thread_index() == 0) {  // defined result even if R exceeded the count
     scratch[kWaves] = 0u;
     scratch[kWaves + 1] = 0u;
@@ -94,6 +94,7 @@ __device__ __forceinline__ BinSplit bin_of_rank_in_regs(const uint32_t (&h)[kMax
   for (int q = 0; q < kMaxBinsPerThread; ++q) sum += q < per ? h[q] : 0u;
   uint32_t total;
   uint32_t above = block_exclusive_scan(sum, scratch, total);
+  if (total_out) *total_out = total;
   if (above < R && R <= above + sum) {
     int found = 0;
     uint32_t f_above = above, f_count = h[0];
@@ -138,10 +139,12 @@ __device__ __forceinline__ BinSplit find_bin_of_rank(const uint32_t* hist, int n
 }
 
 // The same over a histogram row in global memory that other workgroups
-// completed (nbins 1024 or 2048): each thread reads its own group of bins
-// with 16-byte coherent loads, straight into registers.
+// update (nbins 1024 or 2048): each thread reads its own group of bins with
+// 16-byte coherent loads, straight into registers.  `total_out`, if given,
+// receives the sum of the counts read (every thread the same).
 template <int kBins>
-__device__ __forceinline__ BinSplit find_bin_of_rank_global(const uint32_t* g, uint32_t R, uint32_t* scratch) {
+__device__ __forceinline__ BinSplit find_bin_of_rank_global(const uint32_t* g, uint32_t R, uint32_t* scratch,
+                                                            uint32_t* total_out = nullptr) {
   static_assert(kBins == 1024 || kBins == 2048, "four or eight bins per thread");
   constexpr int per = kBins / kBlock;
   const int hi = kBins - 1 - thread_index() * per;
@@ -156,7 +159,7 @@ __device__ __forceinline__ BinSplit find_bin_of_rank_global(const uint32_t* g, u
     const int x = per - 1 - q;  // bin hi - q is element x of the group
     h[q] = q < per ? v[x >> 2][x & 3] : 0u;
   }
-  return bin_of_rank_in_regs(h, per, hi, R, scratch);
+  return bin_of_rank_in_regs(h, per, hi, R, scratch, total_out);
 }
 
 }  // namespace mono

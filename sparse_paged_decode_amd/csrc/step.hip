@@ -331,9 +331,22 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   uint32_t thr = 0u, take = 0xFFFFFFFFu;
   bool ties = false;
   if (!all) {
-    arrive_wait(lvl + 0, (uint32_t)nch, err, ctrl);
+    // The request's histogram row is complete once it counts all L tokens
+    // (counts only grow): every chunk reads the row until it does, so the
+    // row's last update is seen one round trip after it lands, with no
+    // arrival counter in between.
+    BinSplit s1;
+    for (uint32_t spins = 0;; ++spins) {
+      uint32_t total;
+      s1 = find_bin_of_rank_global<kHistBins>(g1, (uint32_t)k, lds.scratch, &total);
+      if (total == (uint32_t)L) break;  // the same in every thread
+      if (spins > kMaxSpins) {
+        if (tid == 0) wait_ran_out(err, ctrl);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
     MONO_STAMP(3);
-    const BinSplit s1 = find_bin_of_rank_global<kHistBins>(g1, (uint32_t)k, lds.scratch);
     MONO_STAMP(4);
     uint32_t R = (uint32_t)k - s1.above;
     const uint32_t B1 = (uint32_t)s1.bin;
