@@ -112,6 +112,8 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   l.hist2 = take(local_ok ? N * kHistBins * 4 : 0);
   l.hist3 = take(local_ok ? N * 1024 * 4 : 0);
   l.ties = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
+  l.xcand = take(local_ok ? N * kLocalMaxChunks * (size_t)kExchCap * 8 : 0);
+  l.xcnt = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
   // Everything from the end of the header to here must be zero when the
   // items start; the rest is scratch that each call overwrites.
   l.zero_end = off;
@@ -119,8 +121,6 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   const size_t zero_bytes = off - (l.ctrl_base + kHdrWords * 4);
   l.n_clear = (uint32_t)((zero_bytes + kClearBytes - 1) / kClearBytes);
   l.scores = take(index ? N * (size_t)l.lcap * 4 : 0);
-  l.xcand = take(local_ok ? N * kLocalMaxChunks * (size_t)kExchCap * 8 : 0);
-  l.xcnt = take(local_ok ? N * kLocalMaxChunks * 4 : 0);
   l.cand = take(index ? N * (size_t)kCandCap * 8 : 0);
   l.part_splits = local_ok ? std::max(l.n_splits, kLocalMaxChunks) : l.n_splits;
   const size_t S = (size_t)l.part_splits;

@@ -329,7 +329,7 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   // key == thr the first `take` in position order (all of them unless ties).
   const bool all = L <= k;
   uint32_t thr = 0u, take = 0xFFFFFFFFu;
-  bool ties = false;
+  bool ties = false, exchanged = false;
   if (!all) {
     // The request's histogram row is complete once it counts all L tokens
     // (counts only grow): every chunk reads the row until it does, so the
@@ -363,19 +363,24 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       const uint32_t my_off = block_exclusive_scan((uint32_t)__popc(m2), lds.scratch, my_cnt);
       uint64_t* xc_all = reinterpret_cast<uint64_t*>(a.ws + lay.xcand) + (size_t)i * kLocalMaxChunks * kExchCap;
       uint32_t* xn_all = reinterpret_cast<uint32_t*>(a.ws + lay.xcnt) + (size_t)i * kLocalMaxChunks;
+      // A written entry is never zero (the position is stored plus one) and
+      // a written count is the count plus one: every chunk reads the pairs
+      // until each chunk's count and entries are in, so the last chunk's
+      // pairs are seen one round trip after they land, with no arrival
+      // counter and no wait for the stores' completion.  The last chunk to
+      // finish its reads zeroes them again.
       {
         uint64_t* mine = xc_all + (size_t)c * kExchCap;
         uint32_t bits = m2, o = my_off;
         while (bits) {
           const int u = __builtin_ctz(bits);
           bits &= bits - 1u;
-          store_coherent(mine + o++, (uint64_t)key[u] | ((uint64_t)(uint32_t)(tok0 + 16 * tid + u) << 32));
+          store_coherent(mine + o++, (uint64_t)key[u] | ((uint64_t)(uint32_t)(tok0 + 16 * tid + u + 1) << 32));
         }
       }
-      if (tid == 0) store_coherent(xn_all + c, my_cnt);
+      if (tid == 0) store_coherent(xn_all + c, my_cnt + 1u);
       MONO_STAMP(5);
-      arrive_wait(lvl + 1, (uint32_t)nch, err, ctrl);
-      MONO_STAMP(6);
+      exchanged = true;
       // Counts and the first `win` entries of every chunk are requested at
       // once (win: a power of two, nch * win <= kExchCap); chunks with more
       // follow in a second round.
@@ -383,13 +388,32 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       const int win = 1 << win_log2;
       constexpr int kPer = kExchCap / kBlock;
       uint64_t v[kPer];
-      const uint32_t cnt_ld = tid < nch ? load_coherent(xn_all + tid) : 0u;
+      for (uint32_t spins = 0;; ++spins) {
+        const uint32_t cnt_ld = tid < nch ? load_coherent(xn_all + tid) : 0u;
 #pragma unroll
-      for (int q = 0; q < kPer; ++q) {
-        const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
-        v[q] = cc < nch ? load_coherent(xc_all + (size_t)cc * kExchCap + r) : 0ull;
+        for (int q = 0; q < kPer; ++q) {
+          const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
+          v[q] = cc < nch ? load_coherent(xc_all + (size_t)cc * kExchCap + r) : 0ull;
+        }
+        if (tid < nch) lds.xc[tid] = cnt_ld;
+        __syncthreads();
+        bool missing = false;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
+          if (cc < nch) {
+            const uint32_t c1 = lds.xc[cc];  // count + 1, or 0 while unwritten
+            missing |= c1 == 0u || ((uint32_t)r + 1u < c1 && v[q] == 0ull);
+          }
+        }
+        if (!__syncthreads_or(missing)) break;
+        if (spins > kMaxSpins) {
+          if (tid == 0) wait_ran_out(err, ctrl);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
       }
-      if (tid < nch) lds.xc[tid] = cnt_ld;
+      if (tid < nch) lds.xc[tid] = max(lds.xc[tid], 1u) - 1u;
       __syncthreads();
       if (tid == 0) {
         uint32_t acc = 0;
@@ -406,15 +430,23 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
         const int e = q * kBlock + tid, cc = e >> win_log2, r = e & (win - 1);
         if (cc < nch && (uint32_t)r < lds.xc[cc]) {
           const uint32_t at = lds.xpre[cc] + (uint32_t)r;
-          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)v[q], (uint32_t)(v[q] >> 32));
+          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)v[q], (uint32_t)(v[q] >> 32) - 1u);
         }
       }
       for (int cc = 0; cc < nch; ++cc) {
         const uint32_t n_cc = min(lds.xc[cc], (uint32_t)kExchCap);
         for (uint32_t r = (uint32_t)win + tid; r < n_cc; r += kBlock) {
           const uint32_t at = lds.xpre[cc] + r;
-          const uint64_t x = load_coherent(xc_all + (size_t)cc * kExchCap + r);
-          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+          uint64_t x;
+          uint32_t spins = 0;
+          while ((x = load_coherent(xc_all + (size_t)cc * kExchCap + r)) == 0ull) {
+            __builtin_amdgcn_s_sleep(1);
+            if (++spins > kMaxSpins) {
+              wait_ran_out(err, ctrl);
+              break;
+            }
+          }
+          if (at < (uint32_t)kExchCap) cand[at] = make_uint2((uint32_t)x, (uint32_t)(x >> 32) - 1u);
         }
       }
       MONO_STAMP(7);
@@ -648,6 +680,15 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     for (int x = tid; x < 1024; x += kBlock) g3[x] = 0u;
     if (tid < kLocalMaxChunks) gt[tid] = 0u;
     if (tid < kLvlWords) lvl[tid] = 0u;
+    if (exchanged) {  // the exchanged pairs and counts (lds.xc holds every chunk's count)
+      uint64_t* xc_all = reinterpret_cast<uint64_t*>(a.ws + lay.xcand) + (size_t)i * kLocalMaxChunks * kExchCap;
+      uint32_t* xn_all = reinterpret_cast<uint32_t*>(a.ws + lay.xcnt) + (size_t)i * kLocalMaxChunks;
+      for (int cc = 0; cc < nch; ++cc) {
+        const uint32_t n_cc = min(lds.xc[cc], (uint32_t)kExchCap);
+        for (uint32_t r = (uint32_t)tid; r < n_cc; r += kBlock) xc_all[(size_t)cc * kExchCap + r] = 0ull;
+      }
+      if (tid < nch) xn_all[tid] = 0u;
+    }
   }
 }
 

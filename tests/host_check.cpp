@@ -229,8 +229,8 @@ static void check_merge_insert_bench() {
 
 // Layout invariants: regions 256-byte aligned, in order, inside the total.
 static void check_layout(const StepLayout& l) {
-  const size_t regions[] = {l.err,  l.ctrl_base, l.hist, l.hist2, l.hist3, l.ties, l.scores,
-                            l.xcand, l.xcnt,     l.cand, l.pm,    l.pl,    l.pacc};
+  const size_t regions[] = {l.err,  l.ctrl_base, l.hist,   l.hist2, l.hist3, l.ties, l.xcand,
+                            l.xcnt, l.scores,    l.cand,   l.pm,    l.pl,    l.pacc};
   size_t prev = 0;
   for (size_t r : regions) {
     CHECK(r % 256 == 0);
@@ -239,6 +239,7 @@ static void check_layout(const StepLayout& l) {
   }
   CHECK(l.total >= prev);
   CHECK(l.ctrl_base == 256 && l.zero_end >= l.ctrl_base + l.ctrl_words * 4 && l.zero_end <= l.scores);
+  CHECK(l.xcnt <= l.zero_end);  // the exchanged pairs and counts start at zero (a written entry is never 0)
   CHECK(l.zero_units == (l.zero_end >> 8));
   CHECK((size_t)l.n_clear * kClearBytes + l.ctrl_base + kHdrWords * 4 >= l.zero_end);
   CHECK(l.queue + l.n_queue <= l.ctrl_words);
