@@ -205,6 +205,15 @@ long plan_step(StepLayout& lay, const DeviceShape& dev, bool fp8, bool has_sel_s
       lay.n_queue = 0u;
     }
   }
+  if (!lay.local && (lay.mode & kModeIndex) && lay.G == 1 && lay.T == 1 && !lay.select_mode && !has_sel_scores &&
+      lay.win_lo == 0 && lay.chunk_pages * kPageTokens <= kSlice && lay.n_scan <= (uint32_t)cap) {
+    // Local filtering: every scan chunk is a first-round ticket of the
+    // resident workgroups (the chunks of a row wait for the row's
+    // histogram), and a chunk's scores fit one slice.
+    lay.local_filter = 1;
+    lay.n_filter = 0u;
+    lay.n_queue = lay.n_select + lay.n_filter + lay.n_attn;
+  }
   const uint64_t n_items = (uint64_t)lay.n_clear + lay.n_ready0 + lay.n_queue;
   if (n_items == 0) return 0;
   if ((uint64_t)lay.n_scan + lay.n_select + lay.n_filter + lay.n_attn > kIndexMask)

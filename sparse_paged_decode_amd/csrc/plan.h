@@ -86,6 +86,7 @@ struct StepLayout {
   int n_splits;      // attention splits per (query token, KV head)
   int select_mode;   // 1: one workgroup selects each query token's top k
   int local;         // 1: chunk-local step (one query token per request; see step.hip)
+  int local_filter;  // 1: each scan chunk filters its own scores as a slice of its row (see scan_item)
   int part_splits;   // splits the partial buffers hold per (query token, KV head)
   uint32_t n_clear, n_scan, n_select, n_filter, n_attn;  // work items of each kind (clear: when needed)
   uint32_t n_ready0;    // items ready at the start (the first tickets after the clear items)

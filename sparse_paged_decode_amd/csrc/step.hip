@@ -692,6 +692,49 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
   }
 }
 
+// Every slice slot of query row i arrives (n_slots in all, whether it held
+// scores or not; its outputs complete before it arrives); the last one
+// resets the row's counters, resolves the selection and publishes the
+// row's attention splits.
+template <int TQ>
+__device__ __forceinline__ void slice_arrive(const StepArgs& a, const StepLayout& lay, int i, const SelectArgs& sa,
+                                             bool valid, bool sliced, BinSplit split, uint32_t n_slots,
+                                             StepLds<TQ>& lds, uint32_t* ctrl, uint32_t* err, uint32_t& s_flag,
+                                             uint32_t& s_pub) {
+  __syncthreads();
+  if (thread_index() == 0) {
+    s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == n_slots - 1u;
+    if (s_flag) {  // every slice of the row has used its counters
+      ctrl[lay.filter_cnt + i] = 0u;
+      ctrl[lay.out_cnt + i] = 0u;
+      ctrl[lay.cand_cnt + i] = 0u;
+    }
+  }
+  __syncthreads();
+  MONO_STAMP(3);
+  if (!s_flag) return;
+  // Attention items of token i are numbered split-major (split * H + h), so
+  // the splits whose candidates are final can be published as one range:
+  // the tokens above the threshold bin fill the first output slots before
+  // the rest are picked, and their splits run while this workgroup picks.
+  const uint32_t H = (uint32_t)lay.H, S = (uint32_t)lay.n_splits;
+  const uint32_t first = (uint32_t)i * H * S;
+  uint32_t n_early = 0;
+  if (valid) {
+    resolve_query(sa, lds.resolve, sliced, split, [&](uint32_t n_final) {
+      MONO_STAMP(4);
+      if (lay.mode != kModeFused) return;
+      n_early = n_final >= (uint32_t)lay.k ? S : min(S, n_final / (uint32_t)lay.split_tokens);
+      if (n_early) publish(lay, ctrl, kItemAttn, first, n_early * H, err, s_pub);
+    });
+    wait_vmem();
+    __syncthreads();
+    MONO_STAMP(5);
+  }
+  if (lay.mode == kModeFused && n_early < S)
+    publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
+}
+
 template <int TQ, class Fmt>
 __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& lay, uint32_t t, StepLds<TQ>& slds,
                                           uint32_t* ctrl, uint32_t* err, uint32_t& s_flag, uint32_t& s_pub) {
@@ -705,7 +748,18 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
   // The group's rows: the request's (head, token) pairs u0..u0+tq-1.
   const int u0 = qg * 4;
   const int tq = min(4, lay.G * T - u0);
-  if (L < T || L > lay.lcap) {
+  // Local filtering (one row per request, every scan item a first-round
+  // ticket): the chunk filters its own scores from LDS once the row's
+  // histogram is complete, as the row's slice, instead of writing them out
+  // and publishing filter items.
+  const bool local_filter = TQ == 1 && lay.local_filter;
+  const bool valid = L >= T && L <= lay.lcap;
+  const int row_i = index_row(lay, b, u0);
+  const int n_valid = valid ? window_valid(lay, L - T) : 0;
+  const SelectArgs fa = select_args(a, lay, row_i, n_valid, ctrl, err);
+  BinSplit split{0, 0u, 0u};
+  bool sliced = false;
+  if (!valid) {
     if (c == 0 && qg == 0 && thread_index() == 0) raise_error(err, kErrSeqLen);
   } else {
     ScanArgs sa;
@@ -741,16 +795,47 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
         // The chunk's whole lines of the score row (entries past the
         // row's last valid position hold values no reader uses).
         const uint32_t n_bytes = (uint32_t)(sa.p_end - sa.p_begin) * kPageTokens * 4u;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            buffer_rsrc(sa.scores + (size_t)sa.row[0] * sa.lcap + (size_t)sa.p_begin * kPageTokens, n_bytes);
-        const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st.scores);
-        for (uint32_t q = (uint32_t)thread_index(); q * 16u < n_bytes; q += kBlock) store_coherent_x4(rsrc, q * 16u, src[q]);
+        auto write_lines = [&]() {
+          const __amdgpu_buffer_rsrc_t rsrc =
+              buffer_rsrc(sa.scores + (size_t)sa.row[0] * sa.lcap + (size_t)sa.p_begin * kPageTokens, n_bytes);
+          const u32x4_t* src = reinterpret_cast<const u32x4_t*>(st.scores);
+          for (uint32_t q = (uint32_t)thread_index(); q * 16u < n_bytes; q += kBlock)
+            store_coherent_x4(rsrc, q * 16u, src[q]);
+        };
+        if (local_filter) {
+          if (n_valid > lay.k) {
+            // The row's histogram is complete once it counts all n_valid
+            // tokens (counts only grow); read until then.
+            for (uint32_t spins = 0;; ++spins) {
+              uint32_t total;
+              split = find_bin_of_rank_global<kHistBins>(fa.ghist, (uint32_t)lay.k, st.scan.hist, &total);
+              if (total == (uint32_t)n_valid) break;  // the same in every thread
+              if (spins > kMaxSpins) {
+                if (thread_index() == 0) wait_ran_out(err, ctrl);
+                break;
+              }
+              __builtin_amdgcn_s_sleep(2);
+            }
+            // An overflowing candidate list is resolved from the score row.
+            if (split.count > (uint32_t)kCandCap) write_lines();
+          }
+          const int j0 = sa.p_begin * kPageTokens;
+          split = filter_slice<true>(fa, j0, min(j0 + (sa.p_end - sa.p_begin) * kPageTokens, n_valid), slds.filter,
+                                     (lds_f32*)st.scores, n_valid > lay.k ? &split : nullptr);
+          sliced = true;
+        } else {
+          write_lines();
+        }
       } else {
         scan_chunk<TQ, Fmt>(sa, lds);
       }
       wait_vmem();  // scores and histogram updates are complete before the arrival
       MONO_STAMP(2);
     }
+  }
+  if (local_filter) {  // every chunk slot of the row arrives as one of its slices
+    slice_arrive<TQ>(a, lay, row_i, fa, valid, sliced, split, (uint32_t)lay.chunks, slds, ctrl, err, s_flag, s_pub);
+    return;
   }
   // Every chunk slot of the group arrives, with or without work; the last
   // one publishes the selection work of the group's rows.
@@ -807,40 +892,7 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
     wait_vmem();
     MONO_STAMP(2);
   }
-  // Every slice slot arrives; the last one resolves the selection and
-  // publishes the token's attention splits.
-  __syncthreads();
-  if (thread_index() == 0) {
-    s_flag = atomicAdd(ctrl + lay.filter_cnt + i, 1u) == (uint32_t)(lay.slices - 1);
-    if (s_flag) {  // every slice of the row has used its counters
-      ctrl[lay.filter_cnt + i] = 0u;
-      ctrl[lay.out_cnt + i] = 0u;
-      ctrl[lay.cand_cnt + i] = 0u;
-    }
-  }
-  __syncthreads();
-  MONO_STAMP(3);
-  if (!s_flag) return;
-  // Attention items of token i are numbered split-major (split * H + h), so
-  // the splits whose candidates are final can be published as one range:
-  // the tokens above the threshold bin fill the first output slots before
-  // the rest are picked, and their splits run while this workgroup picks.
-  const uint32_t H = (uint32_t)lay.H, S = (uint32_t)lay.n_splits;
-  const uint32_t first = (uint32_t)i * H * S;
-  uint32_t n_early = 0;
-  if (valid) {
-    resolve_query(sa, lds.resolve, sliced, split, [&](uint32_t n_final) {
-      MONO_STAMP(4);
-      if (lay.mode != kModeFused) return;
-      n_early = n_final >= (uint32_t)lay.k ? S : min(S, n_final / (uint32_t)lay.split_tokens);
-      if (n_early) publish(lay, ctrl, kItemAttn, first, n_early * H, err, s_pub);
-    });
-    wait_vmem();
-    __syncthreads();
-    MONO_STAMP(5);
-  }
-  if (lay.mode == kModeFused && n_early < S)
-    publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
+  slice_arrive<TQ>(a, lay, i, sa, valid, sliced, split, (uint32_t)lay.slices, lds, ctrl, err, s_flag, s_pub);
 }
 
 template <class Fmt, int kGroups = kPassGroups>

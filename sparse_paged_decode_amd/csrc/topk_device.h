@@ -297,11 +297,17 @@ __device__ __forceinline__ BinSplit kth_bin(const SelectArgs& a, uint32_t* scrat
 
 // Slice [j0, j1) of the scores.  Returns the histogram split it used (the
 // bin of the k-th largest score), which the resolve can reuse; count = 0 and
-// above = k when every valid token is selected.
-__device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds) {
+// above = k when every valid token is selected.  With kLds the slice's
+// scores are lscores[0, j1 - j0) in LDS (a scan chunk's own, j1 - j0 <=
+// kSlice), which the slice's LDS may overlap, and `known` is the split of
+// the complete histogram row, already read.
+template <bool kLds = false>
+__device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, int j1, FilterLds& lds,
+                                                 const lds_f32* lscores = nullptr, const BinSplit* known = nullptr) {
   const int tid = thread_index();
   if (a.n_valid <= a.k) {  // at most k valid tokens: all of them, then -1 padding
-    for (int j = j0 + tid; j < j1; j += kBlock) put_selection(a, (uint32_t)j, j, a.out_scores ? load_coherent(a.scores + j) : 0.f);
+    for (int j = j0 + tid; j < j1; j += kBlock)
+      put_selection(a, (uint32_t)j, j, !a.out_scores ? 0.f : kLds ? lscores[j - j0] : load_coherent(a.scores + j));
     if (j0 == 0) {
       for (int s = a.n_valid + tid; s < a.k; s += kBlock) {
         store_coherent(reinterpret_cast<uint32_t*>(a.out + s), 0xffffffffu);
@@ -315,8 +321,15 @@ __device__ __forceinline__ BinSplit filter_slice(const SelectArgs& a, int j0, in
   constexpr int kPer = kSlice / kBlock;
   float v[kPer];
 #pragma unroll
-  for (int u = 0; u < kPer; ++u) v[u] = load_coherent(a.scores + min(j0 + u * kBlock + tid, a.lcap - 1));
-  const BinSplit sp = kth_bin(a, lds.scratch);
+  for (int u = 0; u < kPer; ++u) {
+    if constexpr (kLds) {
+      v[u] = j0 + u * kBlock + tid < j1 ? lscores[u * kBlock + tid] : 0.f;
+    } else {
+      v[u] = load_coherent(a.scores + min(j0 + u * kBlock + tid, a.lcap - 1));
+    }
+  }
+  if constexpr (kLds) __syncthreads();  // every score is in registers before the slice's LDS is written
+  const BinSplit sp = known ? *known : kth_bin(a, lds.scratch);
   const uint32_t B1 = (uint32_t)sp.bin;
   const bool use_cand = sp.count <= (uint32_t)kCandCap;
 

@@ -279,6 +279,14 @@ static void check_plan(int mode, int B, int T, int H, int bts, int k, bool fp8, 
   } else {
     CHECK(variant == step_variant(G * T > 1 && (mode & kModeIndex), fp8));
   }
+  if (l.local_filter) {
+    // scan chunks filter their own scores: one row per request, chunks of
+    // one slice, every chunk a first-round item (they wait for the row's
+    // histogram), and no filter items in the queue
+    CHECK(!l.local && (mode & kModeIndex) && G == 1 && T == 1 && !l.select_mode && !sel_scores && l.win_lo == 0);
+    CHECK(l.chunk_pages * kPageTokens <= kSlice && (long)l.n_scan <= grid && l.n_filter == 0u);
+    CHECK(l.n_queue == l.n_select + l.n_attn);
+  }
 }
 
 static void check_plans() {
@@ -330,12 +338,21 @@ static void check_plans() {
     plan_step(l, mi, false, false, &variant, "t4-attn");
     CHECK(l.n_splits == 1 && l.n_attn == 512u);
   }
-  // Long rows (8 x 262144 tokens): a chunk would exceed the LDS score area.
+  // Long rows (8 x 262144 tokens): a chunk would exceed the LDS score area;
+  // the item-queue instance runs, its 512 scan chunks filtering their own
+  // scores.  With one resident workgroup short, the chunks publish filter
+  // items instead.
   {
     StepLayout l = step_layout(kModeFused, 8, 1, 1, 2048, 4096, 1);
     int variant = -1;
     plan_step(l, mi, false, false, &variant, "long");
     CHECK(l.local == 0 && l.split_tokens == 256 && l.n_splits == 16);
+    CHECK(l.local_filter == 1 && l.n_scan == 512u && l.n_filter == 0u);
+    DeviceShape d = mi;
+    d.resident[step_variant(false, false)] = 511;
+    l = step_layout(kModeFused, 8, 1, 1, 2048, 4096, 1);
+    plan_step(l, d, false, false, &variant, "long-short");
+    CHECK(l.local_filter == 0 && l.n_filter > 0u);
   }
   // Dense attention, batch 32 x 8192 tokens: the attention-only instance,
   // one split of 512 tokens per resident workgroup.
