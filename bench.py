@@ -128,7 +128,8 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}))
 
 
-# Phase stamps of the trace build (include/mono_trace.h), by item kind.
+# Phase stamps of the trace build (include/mono_trace.h), by item kind, in
+# program order.
 _ATTN_PHASES = {10: "attention: entry", 11: "attention: q and table loaded", 12: "attention: pass done",
                 13: "attention: partials stored", 14: "attention: partials complete", 15: "attention: arrived",
                 16: "attention: merged (last split)"}
@@ -137,7 +138,9 @@ TIMELINE_PHASES = {
                           4: "threshold bin found", 5: "threshold-bin pairs stored",
                           6: "pairs complete (barrier)", 7: "pairs in LDS", 8: "k-th key found",
                           9: "selection list built", **_ATTN_PHASES},
-    "scan": {2: "scores and histogram complete", 3: "arrived at the group counter", 17: "row selected (inline)"},
+    "scan": {7: "scan done (filtering locally)", 6: "row histogram complete (filtering locally)",
+             2: "scores (or the local slice) complete", 3: "arrived at the group (or slice) counter",
+             4: "resolve: final splits published", 5: "resolve: done", 17: "row selected (inline)"},
     "filter slice": {2: "slice filtered", 3: "arrived at the row counter", 4: "resolve: final splits published",
                      5: "resolve: done"},
     "attention split": dict(_ATTN_PHASES),
@@ -197,7 +200,7 @@ def print_timeline(launch, it, gr):
           f"the last leaves the item loop at {us(leave.max()):.2f} us")
     used = it[:, 0] > 0
     kinds = (it[:, 31] >> 24) & 0xFF
-    local = bool(((kinds == 1) & used & (it[:, 4] > 0)).any())
+    local = bool(((kinds == 1) & used & (it[:, 10] > 0)).any())  # chunk-local chunks run attention
     names = {1: "chunk-local chunk" if local else "scan", 2: "filter slice", 3: "attention split",
              4: "selection", 0xFF: "clear"}
     for kind, label in names.items():
@@ -207,8 +210,8 @@ def print_timeline(launch, it, gr):
         phases = {0: "start", **TIMELINE_PHASES[label], 1: "end"}
         print(f"  {label}: {rec.shape[0]} items")
         print(f"    {'phase':38s} {'n':>5s} {'p10':>7s} {'p50':>7s} {'p90':>7s} {'max':>7s} {'step':>7s}")
-        # Stamps in program order: the start, the kind's phases by number, the end.
-        order = [0] + sorted(k for k in phases if k > 1) + [1]
+        # Stamps in program order: the start, the kind's phases as listed, the end.
+        order = [0] + [k for k in phases if k > 1] + [1]
         last = np.zeros(rec.shape[0], dtype=np.int64)  # each item's latest stamp so far
         for k in order:
             v = rec[:, k]

@@ -803,6 +803,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
             store_coherent_x4(rsrc, q * 16u, src[q]);
         };
         if (local_filter) {
+          MONO_STAMP(7);
           if (n_valid > lay.k) {
             // The row's histogram is complete once it counts all n_valid
             // tokens (counts only grow); read until then.
@@ -816,6 +817,7 @@ __device__ __forceinline__ void scan_item(const StepArgs& a, const StepLayout& l
               }
               __builtin_amdgcn_s_sleep(2);
             }
+            MONO_STAMP(6);
             // An overflowing candidate list is resolved from the score row.
             if (split.count > (uint32_t)kCandCap) write_lines();
           }
