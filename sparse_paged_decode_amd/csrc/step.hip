@@ -35,6 +35,7 @@
 namespace mono {
 
 constexpr uint32_t kMaxSpins = 1u << 21;  // bound of one wait (seconds, far above any step)
+constexpr int kPairReadDelay = 32;  // s_sleep units (64 cycles each) before the first read of exchanged pairs: ~0.85 us
 
 namespace {
 
@@ -388,6 +389,11 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
       const int win = 1 << win_log2;
       constexpr int kPer = kExchCap / kBlock;
       uint64_t v[kPer];
+      // Every chunk of the request stores its pairs at about the same time
+      // (they all see the histogram complete together), so a read issued at
+      // once mostly finds some missing and costs a second round trip; the
+      // first read waits about as long as the stores take to land.
+      __builtin_amdgcn_s_sleep(kPairReadDelay);
       for (uint32_t spins = 0;; ++spins) {
         const uint32_t cnt_ld = tid < nch ? load_coherent(xn_all + tid) : 0u;
 #pragma unroll
