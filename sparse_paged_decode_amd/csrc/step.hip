@@ -569,20 +569,28 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     }
   }
   MONO_STAMP(8);
-  uint32_t selm = 0, tie_rank = 0;
-  if (ties) {
-    uint32_t mine = 0;
-#pragma unroll
-    for (int u = 0; u < 16; ++u) mine += (((valid >> u) & 1u) && key[u] == thr) ? 1u : 0u;
-    uint32_t tot;
-    tie_rank = block_exclusive_scan(mine, lds.scratch, tot);
-  }
+  // Selected: every valid token with key > thr, and of those equal to thr
+  // all of them, or with ties the first `take` of the request in position
+  // order (this thread's share: its lowest equal keys after the tie_rank
+  // equal keys of the threads before it).
+  uint32_t gt_mask = 0, eq_mask = 0;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
-    const bool eq = key[u] == thr;
-    const bool in = all || key[u] > thr || (eq && tie_rank < take);
-    if (((valid >> u) & 1u) && in) selm |= 1u << u;
-    if (ties && ((valid >> u) & 1u) && eq) ++tie_rank;
+    gt_mask |= key[u] > thr ? (1u << u) : 0u;
+    eq_mask |= key[u] == thr ? (1u << u) : 0u;
+  }
+  gt_mask &= valid;
+  eq_mask &= valid;
+  uint32_t selm = all ? valid : (gt_mask | eq_mask);
+  if (ties) {
+    uint32_t tot;
+    const uint32_t tie_rank = block_exclusive_scan((uint32_t)__popc(eq_mask), lds.scratch, tot);
+    uint32_t keep = take > tie_rank ? take - tie_rank : 0u, drop = eq_mask;
+    while (drop && keep) {  // the lowest `keep` equal keys stay selected
+      drop &= drop - 1u;
+      --keep;
+    }
+    if (!all) selm &= ~drop;
   }
   uint32_t n_sel;
   const uint32_t off = block_exclusive_scan((uint32_t)__popc(selm), lds.scratch, n_sel);
