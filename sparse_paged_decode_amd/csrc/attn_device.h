@@ -42,6 +42,7 @@ constexpr int kGroupTokens = 16;
 constexpr int kPassGroups = 4;  // groups of one wave whose entries are fetched together
 constexpr int kBtCache = 4096;  // block-table entries staged in LDS (longer rows read global memory)
 constexpr int kMergeBatch = 8;  // splits whose partials the merge requests at once
+constexpr uint32_t kGateSpins = 1u << 21;  // bound of a gated split's wait (seconds)
 // After the token loop the LDS holds the four waves' partial accumulators
 // (32 KiB, [wave][head][dim]) and their running maxima and sums.
 constexpr int kSoBytes = kWaves * kQHeads * kHeadDim * 4;
@@ -73,6 +74,11 @@ struct AttnArgs {
   float* pacc;              // [n_splits, 2, 256, 4] partial accumulators (see the split's store)
   uint32_t* split_cnt;      // arrivals of (query token, KV head)
   uint32_t* err;
+  // Gated splits only (else nullptr): the row's ready word, which the split
+  // waits for after its q and block-table loads and before its entries,
+  // and the control block (a wait that runs out drops its zero record).
+  const uint32_t* sel_ready;
+  uint32_t* ctrl;
   // Chunk-local attention only: the candidates are LDS entries (token
   // tok0 + llist[e]) whose pages are lptab[(j >> 7) - page0].
   const __attribute__((address_space(3))) uint16_t* llist;
@@ -130,8 +136,11 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     return in ? ((kLocal || a.sel_row) ? raw : entry) : -1;
   };
   int jv[kGroups];
+  const bool gated = !kLocal && a.sel_ready != nullptr;
+  if (!gated) {
 #pragma unroll
-  for (int x = 0; x < kGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
+    for (int x = 0; x < kGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
+  }
   const int bt_len = (pos >> 7) + 1;
   const bool bt_lds = bt_len <= kBtCache;
   typedef __attribute__((address_space(3))) const int32_t lds_i32;
@@ -145,6 +154,23 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.q + (size_t)m * kHeadDim + 32 * g);
 #pragma unroll
     for (int s = 0; s < 4; ++s) qb[s] = __builtin_bit_cast(bf16x8_t, src[s]);
+  }
+  if (gated) {
+    // The q operand and the block-table row load meanwhile.
+    if (tid == 0) {
+      uint32_t spins = 0;
+      while (load_coherent(a.sel_ready) == 0u) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > kGateSpins) {
+          raise_error(a.err, kErrWait);
+          store_coherent(a.ctrl + kHdrZeroed, 0u);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < kGroups; ++x) jv[x] = entry_load(wave + kWaves * x);
   }
   __syncthreads();
   MONO_STAMP(11);

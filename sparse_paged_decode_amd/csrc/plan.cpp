@@ -100,6 +100,9 @@ StepLayout step_layout(int mode, int B, int T, int H, int bt_stride, int k, int 
   w += index ? N : 0;
   l.attn_cnt = w;
   w += attn ? NH : 0;
+  l.sel_ready = w;
+  l.has_sel_ready = index && attn;
+  w += l.has_sel_ready ? NH : 0;
   l.lvl_cnt = w;
   w += local_ok ? N * kLvlWords : 0;
   l.pub = w;

@@ -67,7 +67,9 @@ constexpr uint32_t kHdrCleared = 2;  // clear items done
 constexpr uint32_t kHdrZeroed = 3;   // zero region the last call left clean, in 256-B units
 constexpr uint32_t kHdrWords = 4;
 // Work-item descriptors: kind in the top bits, index below.
-constexpr uint32_t kItemScan = 1, kItemFilter = 2, kItemAttn = 3, kItemSelect = 4;
+// kItemAttnGated: an attention split published before its row's selection
+// is complete, which waits for the row's ready word before reading it.
+constexpr uint32_t kItemScan = 1, kItemFilter = 2, kItemAttn = 3, kItemSelect = 4, kItemAttnGated = 5;
 constexpr uint32_t kKindShift = 28;
 constexpr uint32_t kIndexMask = (1u << kKindShift) - 1u;
 
@@ -95,7 +97,8 @@ struct StepLayout {
   size_t zero_end;      // [ctrl_base + header, zero_end) must be zero when items start
   uint64_t zero_units;  // zero_end / 256
   // control block (u32 words from ctrl_base): word offsets
-  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, lvl_cnt, pub, queue, ctrl_words;
+  size_t ctrl, scan_done, filter_cnt, out_cnt, cand_cnt, attn_cnt, sel_ready, lvl_cnt, pub, queue, ctrl_words;
+  int has_sel_ready;  // one-launch step: a ready word per (row, KV head): the row's selection is complete
   // byte offsets in the workspace (hist2, hist3, ties, xcand, xcnt: chunk-local step only)
   size_t err, ctrl_base, hist, hist2, hist3, ties, scores, xcand, xcnt, cand, pm, pl, pacc, total;
 };

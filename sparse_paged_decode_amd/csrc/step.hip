@@ -627,6 +627,8 @@ __device__ __forceinline__ void local_item(const StepArgs& a, const StepLayout& 
     aa.h = h;
     aa.bt_row = nullptr;
     aa.sel_row = nullptr;
+    aa.sel_ready = nullptr;
+    aa.ctrl = ctrl;
     aa.pos = L - 1;
     aa.e0 = 0;
     aa.e1 = (int)n_sel;
@@ -735,15 +737,26 @@ __device__ __forceinline__ void slice_arrive(const StepArgs& a, const StepLayout
   const uint32_t first = (uint32_t)i * H * S;
   uint32_t n_early = 0;
   if (valid) {
+    // Once the threshold is known, every split is published: those whose
+    // candidates are already final as such, the rest gated on the row's
+    // ready word, so that they load their q operands and block-table rows
+    // while the selection is finished.
+    bool published = false;
     resolve_query(sa, lds.resolve, sliced, split, [&](uint32_t n_final) {
       MONO_STAMP(4);
       if (lay.mode != kModeFused) return;
       n_early = n_final >= (uint32_t)lay.k ? S : min(S, n_final / (uint32_t)lay.split_tokens);
       if (n_early) publish(lay, ctrl, kItemAttn, first, n_early * H, err, s_pub);
+      __syncthreads();  // the next publication reuses s_pub
+      if (n_early < S) publish(lay, ctrl, kItemAttnGated, first + n_early * H, (S - n_early) * H, err, s_pub);
+      published = true;
     });
     wait_vmem();
     __syncthreads();
+    // The row's selection is complete (every output slot written).
+    if (lay.has_sel_ready && thread_index() < lay.H) store_coherent(ctrl + lay.sel_ready + (size_t)i * lay.H + thread_index(), 1u);
     MONO_STAMP(5);
+    if (published) return;
   }
   if (lay.mode == kModeFused && n_early < S)
     publish(lay, ctrl, kItemAttn, first + n_early * H, (S - n_early) * H, err, s_pub);
@@ -913,7 +926,7 @@ __device__ __forceinline__ void filter_item(const StepArgs& a, const StepLayout&
 
 template <class Fmt, int kGroups = kPassGroups>
 __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& lay, uint32_t v, AttnLds& lds,
-                                          uint32_t* ctrl, uint32_t* err) {
+                                          uint32_t* ctrl, uint32_t* err, bool gated = false) {
   const int H = lay.H, S = lay.n_splits;
   const int i = (int)(v / (uint32_t)(H * S));
   const int rem = (int)(v % (uint32_t)(H * S));
@@ -952,10 +965,16 @@ __device__ __forceinline__ void attn_item(const StepArgs& a, const StepLayout& l
   aa.pacc = reinterpret_cast<float*>(a.ws + lay.pacc) + qh * S * kQHeads * kHeadDim;
   aa.split_cnt = ctrl + lay.attn_cnt + qh;
   aa.err = err;
+  aa.sel_ready = gated ? ctrl + lay.sel_ready + qh : nullptr;
+  aa.ctrl = ctrl;
   // The workgroup that wrote the output is the last to use the split
-  // counter (every split arrived before it merged): it starts from zero
-  // for the next call.
-  if (attn_split<Fmt, false, kGroups>(aa, lds) && n_splits > 1 && thread_index() == 0) aa.split_cnt[0] = 0u;
+  // counter and the ready word of its (row, KV head) (every split arrived
+  // before it merged, every gated one after reading the word): both start
+  // from zero for the next call.
+  if (attn_split<Fmt, false, kGroups>(aa, lds) && thread_index() == 0) {
+    if (n_splits > 1) aa.split_cnt[0] = 0u;
+    if (lay.has_sel_ready) ctrl[lay.sel_ready + qh] = 0u;
+  }
 }
 
 // Item sets of the kernel instances: every kind; the chunk-local step's
@@ -1019,8 +1038,8 @@ __device__ __forceinline__ void step_body(const StepArgs& a, const StepLayout& l
         select_item<TQ>(a, lay, idx, lds, ctrl, err, s_pub);
       } else if (kind == kItemFilter) {
         filter_item<TQ>(a, lay, idx, lds, ctrl, err, s_flag, s_pub);
-      } else if (kind == kItemAttn) {
-        attn_item<Fmt>(a, lay, idx, lds.attn, ctrl, err);
+      } else if (kind == kItemAttn || kind == kItemAttnGated) {
+        attn_item<Fmt>(a, lay, idx, lds.attn, ctrl, err, kind == kItemAttnGated);
       }
     }
     MONO_STAMP(1);
