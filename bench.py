@@ -144,6 +144,9 @@ TIMELINE_PHASES = {
     "filter slice": {2: "slice filtered", 3: "arrived at the row counter", 4: "resolve: final splits published",
                      5: "resolve: done"},
     "attention split": dict(_ATTN_PHASES),
+    "attention split, gated": {10: "attention: entry", 11: "attention: q, table, ready word, entries", 12: "attention: pass done",
+                               13: "attention: partials stored", 14: "attention: partials complete",
+                               15: "attention: arrived", 16: "attention: merged (last split)"},
     "selection": {17: "row selected"},
     "clear": {},
 }
@@ -202,7 +205,7 @@ def print_timeline(launch, it, gr):
     kinds = (it[:, 31] >> 24) & 0xFF
     local = bool(((kinds == 1) & used & (it[:, 10] > 0)).any())  # chunk-local chunks run attention
     names = {1: "chunk-local chunk" if local else "scan", 2: "filter slice", 3: "attention split",
-             4: "selection", 0xFF: "clear"}
+             5: "attention split, gated", 4: "selection", 0xFF: "clear"}
     for kind, label in names.items():
         rec = it[used & (kinds == kind)]
         if rec.shape[0] == 0:
