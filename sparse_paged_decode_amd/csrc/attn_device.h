@@ -74,9 +74,11 @@ struct AttnArgs {
   float* pacc;              // [n_splits, 2, 256, 4] partial accumulators (see the split's store)
   uint32_t* split_cnt;      // arrivals of (query token, KV head)
   uint32_t* err;
-  // Gated splits only (else nullptr): the row's ready word, which the split
-  // waits for after its q and block-table loads and before its entries,
-  // and the control block (a wait that runs out drops its zero record).
+  // Gated splits only (else nullptr): the ready word of the split's (query
+  // token, KV head), set once the token's selection is complete, which the
+  // split waits for after its q and block-table loads and before reading
+  // its entries; and the control block (a wait that runs out drops its
+  // zero record).
   const uint32_t* sel_ready;
   uint32_t* ctrl;
   // Chunk-local attention only: the candidates are LDS entries (token
