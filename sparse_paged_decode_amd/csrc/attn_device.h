@@ -41,7 +41,7 @@ namespace mono {
 constexpr int kGroupTokens = 16;
 constexpr int kPassGroups = 4;  // groups of one wave whose entries are fetched together
 constexpr int kBtCache = 4096;  // block-table entries staged in LDS (longer rows read global memory)
-constexpr int kMergeBatch = 8;  // splits whose partials the merge requests at once
+constexpr int kMergeBatch = 16;  // splits whose partials the merge requests at once (8 when 8 or fewer, and in the chunk-local step)
 constexpr uint32_t kGateSpins = 1u << 21;  // bound of a gated split's wait (seconds)
 // After the token loop the LDS holds the four waves' partial accumulators
 // (32 KiB, [wave][head][dim]) and their running maxima and sums.
@@ -398,47 +398,58 @@ __device__ __forceinline__ bool attn_split(const AttnArgs& a, AttnLds& lds) {
 
   // ---- last workgroup: merge the splits of this (query token, KV head) ----
   // All partials are requested at once (up to kMergeBatch splits a round
-  // trip).  The maxima and sums of two splits share cache lines, so they
-  // are read coherently; each accumulator slot is written by one split only
-  // and read by this workgroup only, so plain 16-byte loads are current.
+  // trip, or half as many when there are no more splits than that).  The
+  // maxima and sums of two splits share cache lines, so they are read
+  // coherently; each accumulator slot is written by one split only and read
+  // by this workgroup only, so plain 16-byte loads are current.
   M = -INFINITY;
   lsum = 0.f;
 #pragma unroll
   for (int x = 0; x < 8; ++x) o[x] = 0.f;
-  for (int s0 = 0; s0 < n_splits; s0 += kMergeBatch) {
-    float mv[kMergeBatch], lv[kMergeBatch];
-    f32x4_t av[kMergeBatch][2];
-    // Loaded values are not rewritten before all loads of the batch are
-    // issued (a rewrite makes the compiler wait load by load); splits past
-    // the last are masked where the values are used.
+  auto merge = [&](auto batch) {
+    constexpr int kB = decltype(batch)::value;
+    for (int s0 = 0; s0 < n_splits; s0 += kB) {
+      float mv[kB], lv[kB];
+      f32x4_t av[kB][2];
+      // Loaded values are not rewritten before all loads of the batch are
+      // issued (a rewrite makes the compiler wait load by load); splits past
+      // the last are masked where the values are used.
 #pragma unroll
-    for (int y = 0; y < kMergeBatch; ++y) {
-      const size_t sl = (size_t)min(s0 + y, n_splits - 1);
-      mv[y] = load_coherent(pm + sl * kQHeads + hd);
-      lv[y] = load_coherent(pl + sl * kQHeads + hd);
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + sl * kQHeads * kHeadDim);
-      av[y][0] = src[tid];
-      av[y][1] = src[kBlock + tid];
-    }
-    float Mb = M;
-#pragma unroll
-    for (int y = 0; y < kMergeBatch; ++y) Mb = fmaxf(Mb, s0 + y < n_splits ? mv[y] : -INFINITY);
-    const float Mu_b = (Mb == -INFINITY) ? 0.f : Mb;
-    const float fo = __builtin_amdgcn_exp2f(M - Mu_b);  // rescale what was merged so far
-    lsum *= fo;
-#pragma unroll
-    for (int x = 0; x < 8; ++x) o[x] *= fo;
-#pragma unroll
-    for (int y = 0; y < kMergeBatch; ++y) {
-      const float f = s0 + y < n_splits ? __builtin_amdgcn_exp2f(mv[y] - Mu_b) : 0.f;
-      lsum += lv[y] * f;
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        o[x] += av[y][0][x] * f;
-        o[4 + x] += av[y][1][x] * f;
+      for (int y = 0; y < kB; ++y) {
+        const size_t sl = (size_t)min(s0 + y, n_splits - 1);
+        mv[y] = load_coherent(pm + sl * kQHeads + hd);
+        lv[y] = load_coherent(pl + sl * kQHeads + hd);
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(pacc + sl * kQHeads * kHeadDim);
+        av[y][0] = src[tid];
+        av[y][1] = src[kBlock + tid];
       }
+      float Mb = M;
+#pragma unroll
+      for (int y = 0; y < kB; ++y) Mb = fmaxf(Mb, s0 + y < n_splits ? mv[y] : -INFINITY);
+      const float Mu_b = (Mb == -INFINITY) ? 0.f : Mb;
+      const float fo = __builtin_amdgcn_exp2f(M - Mu_b);  // rescale what was merged so far
+      lsum *= fo;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) o[x] *= fo;
+#pragma unroll
+      for (int y = 0; y < kB; ++y) {
+        const float f = s0 + y < n_splits ? __builtin_amdgcn_exp2f(mv[y] - Mu_b) : 0.f;
+        lsum += lv[y] * f;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          o[x] += av[y][0][x] * f;
+          o[4 + x] += av[y][1][x] * f;
+        }
+      }
+      M = Mb;
     }
-    M = Mb;
+  };
+  if constexpr (kLocal) {
+    merge(std::integral_constant<int, kMergeBatch / 2>{});  // the chunk-local step keeps its register budget
+  } else if (n_splits > kMergeBatch / 2) {
+    merge(std::integral_constant<int, kMergeBatch>{});
+  } else {
+    merge(std::integral_constant<int, kMergeBatch / 2>{});
   }
   store_bf16x8(orow, o, lsum > 0.f ? a.v_scale / lsum : 0.f);
   MONO_STAMP(16);
